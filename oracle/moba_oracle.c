@@ -1,0 +1,358 @@
+/*
+ * MoBA causal prefill forward -- CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the CPU-baseline
+ * leg of the benchmark are the only callers. The GPU library never links,
+ * loads or calls this file, and this file uses nothing from the GPU library.
+ *
+ * What it computes is the plain definition of MoBA prefill: dense softmax
+ * attention under MoBA's block mask. That is the mask-based "moba_naive"
+ * formulation (MoBA: Mixture of Block Attention for Long-Context LLMs,
+ * README, "Implementation Details"); the efficient implementation described on
+ * the same page reaches the same result up to rounding, because merging the
+ * softmax of disjoint key sets through their log-sum-exp is exact (Kimi发布MoBA
+ * 突破性实现无限上下文, "PyTorch实现关键要点").
+ *
+ * Arithmetic is fp64 throughout. Inputs arrive as fp32 arrays; every bf16 and
+ * every fp32 value converts to fp64 exactly, so no input rounding happens here.
+ *
+ * Per sequence n of a packed batch (boundaries in cu_seqlens), with local
+ * positions t in [0, S_n):
+ *   1. Blocks. Block b covers [b*B, min((b+1)*B, S_n)); the remainder forms a
+ *      shorter final block. Blocks restart at every sequence start.
+ *      (Kimi article, "MoBA：基于块的混合注意力机制": the sequence is cut into
+ *      spans of equal length.)
+ *   2. Pool. Kbar[b,g] = mean of K[s,g,:] over the tokens s of block b, using the
+ *      block's true length. (Same section: each query looks at a pooled, e.g.
+ *      mean-pooled, representation of every block's keys.)
+ *   3. Gate. For row (t,h): i = t / B, g = h / (Hq/Hkv). The score of block j is
+ *      the unscaled dot product q[t,h] . Kbar[j,g]; only j < i are candidates.
+ *      The query's own block (j = i) is forced and not gated; future blocks are
+ *      masked. (README, "Parameter-less Gating Mechanism"; Kimi article,
+ *      "PyTorch实现关键要点": score = query times pooled keys, then the causal
+ *      mask, then top-k; README FAQ, issue #27: the current block is always
+ *      attended and is excluded from the top-k because pooling a whole block
+ *      would leak future tokens.)
+ *   4. Select. top-k counts the own block, so min(topk-1, i) past blocks are
+ *      kept (README FAQ, issue #27: moba_topk is reduced by one and capped by the
+ *      number of candidate chunks). Candidates are ranked by score, highest
+ *      first; equal scores rank the lower block index first (the pages are
+ *      silent on ties; this is the reading taken). The kept ids are reported in
+ *      ascending order, padded with -1 up to topk-1 entries.
+ *   5. Attend. The key set is A = {s : i*B <= s <= t} (own block, causal) united
+ *      with every token of every selected block. With scale c:
+ *        out = sum_{s in A} softmax_s(c * q . k_s) * v_s,
+ *        lse = m + log(sum_{s in A} exp(c * q . k_s - m)),  m = max logit.
+ *
+ * The oracle takes any subset of rows ("sampled mode"): it pools every block,
+ * then runs steps 3-5 for just the requested (token, head) rows. A row's result
+ * does not depend on which other rows are requested.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+static int64_t num_blocks_of(int64_t len, int64_t block) {
+  return (len + block - 1) / block;
+}
+
+/* Sequence n with cu[n] <= tok < cu[n+1] (empty sequences are skipped). */
+static int32_t seq_of_token(const int32_t* cu, int32_t nseq, int64_t tok) {
+  int32_t lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) / 2;
+    if ((int64_t)cu[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+static int check_layout(const int32_t* cu, int32_t nseq, int32_t hq, int32_t hkv,
+                        int32_t d, int32_t block) {
+  if (!cu || nseq < 1 || hq < 1 || hkv < 1 || d < 1 || block < 1) return 0;
+  if (hq % hkv != 0) return 0;
+  if (cu[0] != 0) return 0;
+  for (int32_t n = 0; n < nseq; ++n)
+    if (cu[n + 1] < cu[n]) return 0;
+  return 1;
+}
+
+/* Total number of blocks over all sequences, and the first global block id of
+ * each sequence (block_base must hold nseq entries). */
+static int64_t count_blocks(const int32_t* cu, int32_t nseq, int32_t block,
+                            int64_t* block_base) {
+  int64_t total = 0;
+  for (int32_t n = 0; n < nseq; ++n) {
+    if (block_base) block_base[n] = total;
+    total += num_blocks_of((int64_t)cu[n + 1] - cu[n], block);
+  }
+  return total;
+}
+
+int64_t moba_oracle_num_blocks(const int32_t* cu_seqlens, int32_t nseq, int32_t block) {
+  if (!cu_seqlens || nseq < 1 || block < 1) return -1;
+  return count_blocks(cu_seqlens, nseq, block, NULL);
+}
+
+/* Step 2: mean-pool every block of K.
+ * k:    [T, hkv, d] fp32, T = cu_seqlens[nseq].
+ * kbar: [NB, hkv, d] fp64 out, blocks numbered sequence by sequence. */
+int moba_oracle_pool(const float* k, const int32_t* cu_seqlens, int32_t nseq,
+                     int32_t hkv, int32_t d, int32_t block, double* kbar) {
+  if (!k || !kbar || !check_layout(cu_seqlens, nseq, hkv, hkv, d, block))
+    return ORACLE_BAD_ARG;
+  int64_t gb = 0;
+  for (int32_t n = 0; n < nseq; ++n) {
+    int64_t start = cu_seqlens[n], len = (int64_t)cu_seqlens[n + 1] - start;
+    int64_t nb = num_blocks_of(len, block);
+    for (int64_t b = 0; b < nb; ++b, ++gb) {
+      int64_t s0 = start + b * block;
+      int64_t s1 = start + ((b + 1) * block < len ? (b + 1) * block : len);
+      for (int32_t g = 0; g < hkv; ++g) {
+        double* dst = kbar + (gb * hkv + g) * d;
+        for (int32_t e = 0; e < d; ++e) dst[e] = 0.0;
+        for (int64_t s = s0; s < s1; ++s) {
+          const float* src = k + (s * hkv + g) * d;
+          for (int32_t e = 0; e < d; ++e) dst[e] += (double)src[e];
+        }
+        for (int32_t e = 0; e < d; ++e) dst[e] /= (double)(s1 - s0);
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+static double dot(const float* a, const double* b, int32_t d) {
+  double acc = 0.0;
+  for (int32_t e = 0; e < d; ++e) acc += (double)a[e] * b[e];
+  return acc;
+}
+
+static double dot_ff(const float* a, const float* b, int32_t d) {
+  double acc = 0.0;
+  for (int32_t e = 0; e < d; ++e) acc += (double)a[e] * (double)b[e];
+  return acc;
+}
+
+/* Steps 3-5 for a list of rows.
+ *
+ * q_rows:   [nrows, d] fp32, the query vector of each requested row.
+ * row_tok:  [nrows] packed token index of the row (0 <= tok < T).
+ * row_head: [nrows] query head of the row (0 <= h < hq).
+ * k, v:     [T, hkv, d] fp32.
+ * scale:    softmax scale; <= 0 selects 1/sqrt(d).
+ * out:      [nrows, d] fp64.         lse: [nrows] fp64.
+ * sel:      [nrows, topk-1] int32 (may be NULL when topk == 1).
+ * margin:   [nrows] fp64 or NULL: score of the last kept block minus the best
+ *           score left out; +inf when every candidate is kept.
+ * nthreads: OpenMP threads; <= 0 uses the runtime default.
+ */
+int moba_oracle_rows(const float* q_rows, const int32_t* row_tok, const int32_t* row_head,
+                     int64_t nrows, const float* k, const float* v,
+                     const int32_t* cu_seqlens, int32_t nseq, int32_t hq, int32_t hkv,
+                     int32_t d, int32_t block, int32_t topk, double scale,
+                     double* out, double* lse, int32_t* sel, double* margin,
+                     int32_t nthreads) {
+  if (!q_rows || !row_tok || !row_head || !k || !v || !out || !lse || nrows < 0 ||
+      topk < 1 || !check_layout(cu_seqlens, nseq, hq, hkv, d, block))
+    return ORACLE_BAD_ARG;
+  if (topk > 1 && !sel) return ORACLE_BAD_ARG;
+  const int64_t T = cu_seqlens[nseq];
+  for (int64_t r = 0; r < nrows; ++r)
+    if (row_tok[r] < 0 || row_tok[r] >= T || row_head[r] < 0 || row_head[r] >= hq)
+      return ORACLE_BAD_ARG;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+
+  int64_t* block_base = (int64_t*)malloc(sizeof(int64_t) * (size_t)nseq);
+  if (!block_base) return ORACLE_NO_MEMORY;
+  const int64_t nb_total = count_blocks(cu_seqlens, nseq, block, block_base);
+  double* kbar = (double*)malloc(sizeof(double) * (size_t)(nb_total * hkv * d));
+  if (!kbar) { free(block_base); return ORACLE_NO_MEMORY; }
+  moba_oracle_pool(k, cu_seqlens, nseq, hkv, d, block, kbar);
+
+  int64_t max_blocks = 0;
+  for (int32_t n = 0; n < nseq; ++n) {
+    int64_t nb = num_blocks_of((int64_t)cu_seqlens[n + 1] - cu_seqlens[n], block);
+    if (nb > max_blocks) max_blocks = nb;
+  }
+  const int32_t group = hq / hkv;
+  int failed = 0;
+
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* sigma = (double*)malloc(sizeof(double) * (size_t)(max_blocks + 1));
+    char* taken = (char*)malloc((size_t)(max_blocks + 1));
+    int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)block * (size_t)topk);
+    if (!sigma || !taken || !chosen || !logit) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+      for (int64_t r = 0; r < nrows; ++r) {
+        const float* q = q_rows + r * d;
+        const int64_t tok = row_tok[r];
+        const int32_t h = row_head[r];
+        const int32_t n = seq_of_token(cu_seqlens, nseq, tok);
+        const int64_t start = cu_seqlens[n];
+        const int64_t t = tok - start;
+        const int64_t i = t / block;
+        const int32_t g = h / group;
+        const int64_t nsel = (topk - 1 < i) ? topk - 1 : i;
+
+        /* Step 3: gate scores of the past blocks j < i. */
+        for (int64_t j = 0; j < i; ++j) {
+          sigma[j] = dot(q, kbar + ((block_base[n] + j) * hkv + g) * d, d);
+          taken[j] = 0;
+        }
+        /* Step 4: repeatedly take the best remaining candidate. A strict '>'
+         * keeps the lower index when scores tie. */
+        for (int64_t m = 0; m < nsel; ++m) {
+          int64_t best = -1;
+          for (int64_t j = 0; j < i; ++j)
+            if (!taken[j] && (best < 0 || sigma[j] > sigma[best])) best = j;
+          taken[best] = 1;
+          chosen[m] = (int32_t)best;
+        }
+        if (margin) {
+          double worst_kept = INFINITY, best_left = -INFINITY;
+          for (int64_t j = 0; j < i; ++j) {
+            if (taken[j] && sigma[j] < worst_kept) worst_kept = sigma[j];
+            if (!taken[j] && sigma[j] > best_left) best_left = sigma[j];
+          }
+          margin[r] = (nsel < i) ? worst_kept - best_left : INFINITY;
+        }
+        if (topk > 1) {
+          int32_t* srow = sel + r * (topk - 1);
+          int64_t w = 0;
+          for (int64_t j = 0; j < i; ++j)
+            if (taken[j]) srow[w++] = (int32_t)j;
+          for (; w < topk - 1; ++w) srow[w] = -1;
+        }
+
+        /* Step 5: the attended key set A, own block first (causal), then the
+         * selected blocks. Logits are stored, then softmax with the max taken
+         * out, then the weighted sum of V. */
+        int64_t na = 0;
+        for (int64_t s = start + i * block; s <= tok; ++s)
+          logit[na++] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
+        for (int64_t m = 0; m < nsel; ++m) {
+          int64_t s0 = start + (int64_t)chosen[m] * block;
+          for (int64_t s = s0; s < s0 + block; ++s)   /* past blocks are full */
+            logit[na++] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
+        }
+        double mx = -INFINITY;
+        for (int64_t a = 0; a < na; ++a) if (logit[a] > mx) mx = logit[a];
+        double denom = 0.0;
+        double* o = out + r * d;
+        for (int32_t e = 0; e < d; ++e) o[e] = 0.0;
+        int64_t a = 0;
+        for (int64_t s = start + i * block; s <= tok; ++s, ++a) {
+          double w = exp(logit[a] - mx);
+          denom += w;
+          const float* vs = v + (s * hkv + g) * d;
+          for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
+        }
+        for (int64_t m = 0; m < nsel; ++m) {
+          int64_t s0 = start + (int64_t)chosen[m] * block;
+          for (int64_t s = s0; s < s0 + block; ++s, ++a) {
+            double w = exp(logit[a] - mx);
+            denom += w;
+            const float* vs = v + (s * hkv + g) * d;
+            for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
+          }
+        }
+        for (int32_t e = 0; e < d; ++e) o[e] /= denom;
+        lse[r] = mx + log(denom);
+      }
+    }
+    free(sigma);
+    free(taken);
+    free(chosen);
+    free(logit);
+  }
+  free(kbar);
+  free(block_base);
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Plain causal softmax attention for a list of rows: key set {s : 0 <= s <= t}
+ * of the row's own sequence. This is the comparison point that MoBA replaces
+ * (full attention; README, "Seamlessly Transition between Full and Sparse
+ * Attention"). Same argument conventions as moba_oracle_rows. */
+int moba_oracle_causal_rows(const float* q_rows, const int32_t* row_tok,
+                            const int32_t* row_head, int64_t nrows, const float* k,
+                            const float* v, const int32_t* cu_seqlens, int32_t nseq,
+                            int32_t hq, int32_t hkv, int32_t d, double scale,
+                            double* out, double* lse, int32_t nthreads) {
+  if (!q_rows || !row_tok || !row_head || !k || !v || !out || !lse || nrows < 0 ||
+      !check_layout(cu_seqlens, nseq, hq, hkv, d, 1))
+    return ORACLE_BAD_ARG;
+  const int64_t T = cu_seqlens[nseq];
+  for (int64_t r = 0; r < nrows; ++r)
+    if (row_tok[r] < 0 || row_tok[r] >= T || row_head[r] < 0 || row_head[r] >= hq)
+      return ORACLE_BAD_ARG;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+  const int32_t group = hq / hkv;
+  int64_t max_len = 0;
+  for (int32_t n = 0; n < nseq; ++n)
+    if ((int64_t)cu_seqlens[n + 1] - cu_seqlens[n] > max_len)
+      max_len = (int64_t)cu_seqlens[n + 1] - cu_seqlens[n];
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(max_len + 1));
+    if (!logit) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+      for (int64_t r = 0; r < nrows; ++r) {
+        const float* q = q_rows + r * d;
+        const int64_t tok = row_tok[r];
+        const int32_t g = row_head[r] / group;
+        const int64_t start = cu_seqlens[seq_of_token(cu_seqlens, nseq, tok)];
+        double mx = -INFINITY;
+        for (int64_t s = start; s <= tok; ++s) {
+          logit[s - start] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
+          if (logit[s - start] > mx) mx = logit[s - start];
+        }
+        double denom = 0.0;
+        double* o = out + r * d;
+        for (int32_t e = 0; e < d; ++e) o[e] = 0.0;
+        for (int64_t s = start; s <= tok; ++s) {
+          double w = exp(logit[s - start] - mx);
+          denom += w;
+          const float* vs = v + (s * hkv + g) * d;
+          for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
+        }
+        for (int32_t e = 0; e < d; ++e) o[e] /= denom;
+        lse[r] = mx + log(denom);
+      }
+    }
+    free(logit);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
