@@ -1,0 +1,272 @@
+"""MoBA causal prefill forward on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libmoba.so, whose C ABI is include/moba.h. This
+module only marshals arguments: it allocates outputs and the workspace with
+torch, passes raw device pointers and torch's current stream, and turns status
+codes into exceptions. Every step of the computation runs in the library's HIP
+kernels. There is no fallback: if libmoba.so is missing or a call fails, an
+exception is raised.
+
+Build the library first:  python -m block_sparse_attention_causal_amd.build
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoba.so")
+
+MOBA_OK, MOBA_ERR_INVALID_ARG, MOBA_ERR_UNSUPPORTED, MOBA_ERR_WORKSPACE, MOBA_ERR_HIP = range(5)
+MOBA_DTYPE_F32, MOBA_DTYPE_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: MOBA_DTYPE_F32, torch.bfloat16: MOBA_DTYPE_BF16}
+STAGES = ("pool", "gate", "route", "attn_self", "attn_selected", "merge", "attn_dense")
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("MoBA call failed with status %d: %s" % (status, message))
+        self.status = status
+
+
+class moba_shape_t(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmoba.so is not built (%s); run "
+                          "`python -m block_sparse_attention_causal_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    shp = ctypes.POINTER(moba_shape_t)
+    sig = {
+        "moba_abi_version": ([], i32),
+        "moba_last_error": ([], ctypes.c_char_p),
+        "moba_workspace_bytes": ([p, i32, shp, i32, i32], sz),
+        "moba_forward": ([p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p], ctypes.c_int),
+        "moba_dense_causal_forward": ([p, p, p, p, p, i32, shp, p, p, p], ctypes.c_int),
+        "moba_block_pool": ([p, p, p, i32, shp, i32, p, p, sz, p], ctypes.c_int),
+        "moba_route_sizes": ([p, i32, shp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)],
+                             ctypes.c_int),
+        "moba_route": ([p, p, p, i32, shp, i32, i32, p, p, p, sz, p], ctypes.c_int),
+        "moba_timing_enable": ([i32], ctypes.c_int),
+        "moba_timing_read": ([p, p, i32], i32),
+        "moba_stage_name": ([i32], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    """Names the binding resolves in libmoba.so (loading fails if any is missing)."""
+    _load()
+    return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
+            "moba_dense_causal_forward", "moba_block_pool", "moba_route_sizes", "moba_route",
+            "moba_timing_enable", "moba_timing_read", "moba_stage_name"]
+
+
+def moba_last_error() -> str:
+    return _load().moba_last_error().decode()
+
+
+def _check(status: int):
+    if status != MOBA_OK:
+        raise MobaError(status, moba_last_error())
+
+
+def _shape(hq, hkv, d, dtype, scale=0.0):
+    if dtype not in _DTYPE_CODE:
+        raise TypeError("dtype must be float32 or bfloat16, got %s" % dtype)
+    return moba_shape_t(int(hq), int(hkv), int(d), _DTYPE_CODE[dtype], float(scale))
+
+
+def _cu(cu_seqlens, device):
+    """(host int32 tensor, device int32 tensor) for cu_seqlens given as list/tensor."""
+    host = torch.as_tensor(cu_seqlens, dtype=torch.int32).to("cpu").contiguous()
+    dev = host.to(device)
+    return host, dev
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous [T, H, D]" % name)
+        if t.dim() != 3:
+            raise ValueError("%s must be [T, H, D]" % name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("inconsistent q/k/v shapes %s %s %s" % (q.shape, k.shape, v.shape))
+
+
+def moba_workspace_bytes(cu_seqlens, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
+                         topk) -> int:
+    host = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous()
+    shape = _shape(num_q_heads, num_kv_heads, head_dim, dtype)
+    n = _load().moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                     int(block_size), int(topk))
+    if n == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    return int(n)
+
+
+def _workspace(nbytes, device):
+    # 256-byte aligned device buffer (the caching allocator returns 512-byte aligned blocks)
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moba_forward(q, k, v, cu_seqlens, block_size, topk, *, out=None, workspace=None,
+                 return_sel=False, return_lse=False, softmax_scale=0.0, cu_seqlens_dev=None):
+    """MoBA causal prefill forward: q [T,Hq,D], k/v [T,Hkv,D] (bf16 or fp32, on the GPU).
+
+    Returns out [T,Hq,D]; with return_sel / return_lse also the selected blocks
+    [T,Hq,topk-1] (int32) and the log-sum-exp [T,Hq] (fp32).
+    """
+    _check_qkv(q, k, v)
+    dev = q.device
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    host, cu_dev = _cu(cu_seqlens, dev)
+    if cu_seqlens_dev is not None:
+        cu_dev = cu_seqlens_dev
+    shape = _shape(hq, hkv, d, q.dtype, softmax_scale)
+    lib = _load()
+    nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                      int(block_size), int(topk))
+    if nbytes == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    if workspace is None:
+        workspace = _workspace(nbytes, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    sel = torch.empty(T, hq, max(topk - 1, 0), dtype=torch.int32, device=dev) \
+        if (return_sel and topk > 1) else None
+    lse = torch.empty(T, hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.moba_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_dev), _ptr(host),
+                            host.numel() - 1, ctypes.byref(shape), int(block_size), int(topk),
+                            _ptr(out), _ptr(workspace), workspace.numel(), _ptr(sel), _ptr(lse),
+                            _stream(dev)))
+    res = [out]
+    if return_sel:
+        res.append(sel if sel is not None else torch.empty(T, hq, 0, dtype=torch.int32, device=dev))
+    if return_lse:
+        res.append(lse)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def moba_dense_causal_forward(q, k, v, cu_seqlens, *, out=None, return_lse=False,
+                              softmax_scale=0.0, cu_seqlens_dev=None):
+    """Dense causal attention over packed sequences (the comparison kernel)."""
+    _check_qkv(q, k, v)
+    dev = q.device
+    T, hq, d = q.shape
+    host, cu_dev = _cu(cu_seqlens, dev)
+    if cu_seqlens_dev is not None:
+        cu_dev = cu_seqlens_dev
+    shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(T, hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(_load().moba_dense_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_dev), _ptr(host),
+                                             host.numel() - 1, ctypes.byref(shape), _ptr(out),
+                                             _ptr(lse), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def moba_block_pool(k, cu_seqlens, block_size):
+    """Mean-pooled keys [NB, Hkv, D] (fp32) of k [T, Hkv, D]."""
+    if not k.is_cuda or not k.is_contiguous() or k.dim() != 3:
+        raise ValueError("k must be a contiguous GPU tensor [T, Hkv, D]")
+    dev = k.device
+    T, hkv, d = k.shape
+    host, cu_dev = _cu(cu_seqlens, dev)
+    shape = _shape(hkv, hkv, d, k.dtype)
+    lib = _load()
+    nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                      int(block_size), 1)
+    if nbytes == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    ws = _workspace(nbytes, dev)
+    lens = (host[1:] - host[:-1]).tolist()
+    nb = sum((s + block_size - 1) // block_size for s in lens)
+    kbar = torch.empty(nb, hkv, d, dtype=torch.float32, device=dev)
+    _check(lib.moba_block_pool(_ptr(k), _ptr(cu_dev), _ptr(host), host.numel() - 1,
+                               ctypes.byref(shape), int(block_size), _ptr(kbar), _ptr(ws),
+                               ws.numel(), _stream(dev)))
+    return kbar
+
+
+def moba_route_sizes(cu_seqlens, num_q_heads, num_kv_heads, head_dim, dtype, block_size, topk):
+    host = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous()
+    shape = _shape(num_q_heads, num_kv_heads, head_dim, dtype)
+    nl, ne = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_load().moba_route_sizes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                    int(block_size), int(topk), ctypes.byref(nl),
+                                    ctypes.byref(ne)))
+    return int(nl.value), int(ne.value)
+
+
+def moba_route(sel, cu_seqlens, num_kv_heads, head_dim, dtype, block_size, topk):
+    """Routing lists of a selection map sel [T, Hq, topk-1] (int32, on the GPU).
+
+    Returns (list_offsets [num_lists+1], entries [num_entries]), both int32 on the GPU.
+    """
+    if not sel.is_cuda or sel.dtype != torch.int32 or not sel.is_contiguous():
+        raise ValueError("sel must be a contiguous int32 GPU tensor")
+    dev = sel.device
+    T, hq, _ = sel.shape
+    host, cu_dev = _cu(cu_seqlens, dev)
+    shape = _shape(hq, num_kv_heads, head_dim, dtype)
+    lib = _load()
+    nl, ne = moba_route_sizes(host, hq, num_kv_heads, head_dim, dtype, block_size, topk)
+    nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                      int(block_size), int(topk))
+    ws = _workspace(nbytes, dev)
+    offs = torch.empty(nl + 1, dtype=torch.int32, device=dev)
+    ent = torch.empty(max(ne, 1), dtype=torch.int32, device=dev)
+    _check(lib.moba_route(_ptr(sel), _ptr(cu_dev), _ptr(host), host.numel() - 1,
+                          ctypes.byref(shape), int(block_size), int(topk), _ptr(offs), _ptr(ent),
+                          _ptr(ws), ws.numel(), _stream(dev)))
+    return offs, ent[:ne]
+
+
+def moba_timing_enable(enable: bool = True):
+    _check(_load().moba_timing_enable(1 if enable else 0))
+
+
+def moba_timing_read() -> dict:
+    """{stage: (total_ms, launches)} of the timed launches since the last read."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    k = _load().moba_timing_read(ms, cnt, n)
+    return {STAGES[i]: (ms[i], cnt[i]) for i in range(k)}
+
+
+def moba_stage_name(stage: int) -> str:
+    return _load().moba_stage_name(int(stage)).decode()

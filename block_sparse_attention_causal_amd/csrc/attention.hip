@@ -1,0 +1,434 @@
+// a4a / a4b / a6: flash attention on the matrix cores.
+//
+// Kimi发布MoBA突破性实现无限上下文, "PyTorch实现关键要点": flash attention runs
+// separately over each query's own block (causal) and over the blocks the gate
+// selected, and the parts are then combined with an online-softmax merge.
+// MoBA README FAQ (issue #27): the own block is attended with a causal mask.
+//
+// One kernel template serves three tile kinds:
+//   SELF     tile = up to 256 rows of one block: 32 consecutive tokens per wave,
+//            the HG q-heads of one kv group side by side (GQA: the waves share
+//            the K/V tiles). Keys = block start .. last token of the tile, causal.
+//   SELECTED tile = up to 256 routed (row, slot) entries of one list (block j,
+//            kv-head g); keys = the B keys of block j, no mask. Rows of every
+//            q-head of the group mix freely in a tile (GQA sharing again).
+//   DENSE    SELF with the whole sequence as one block (the comparison kernel).
+//
+// Per wave (32 rows) and per 64-key chunk staged in LDS:
+//   S^T[key, row] = K . Q^T  (A = K from LDS, B = Q^T held in registers)
+//   online softmax per row in the log2 domain; lane l owns row l % 32 and half
+//   of its keys, lane l ^ 32 the other half, so only the running max is
+//   exchanged per chunk;
+//   O^T[d, row] += V^T . P^T (A = V^T from a transposed LDS copy, B = P^T
+//   straight from the score registers; the LDS key order is permuted so each
+//   lane's eight keys are contiguous).
+// K and V chunks are double-buffered in LDS; the next chunk is loaded into
+// registers while the current one is multiplied.
+#include "moba_plan.h"
+
+namespace moba {
+
+enum { MODE_SELF = 0, MODE_SELECTED = 1, MODE_DENSE = 2 };
+constexpr int KC = 64;  // keys per chunk
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu;
+  const int32_t* blk_seq;
+  const int32_t* blk_local;
+  const int32_t* list_offsets;
+  const int32_t* tile_offsets;
+  const int32_t* entries;
+  float* o_part;      // SELF with ks > 0: [T*hq, D]; SELECTED: [T*hq*ks, D]
+  float* lse_part;
+  void* out;          // DENSE, or SELF with ks == 0: final output [T*hq, D]
+  float* lse_out;     // optional with `out`
+  int64_t nb, nlists, ntiles, padded;
+  int nseq, hq, hkv, hg, block, ks, nu;
+  float scale_log2;
+};
+
+// Position of key k (0..63 inside a chunk) in the transposed V copy: inside
+// each group of 16 keys, bits 2 and 3 of the index are swapped.
+__device__ __forceinline__ int vt_pos_of_group4(int kg) {  // kg = key / 4
+  return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+}
+
+template <typename T, int D>
+struct KVStage {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int KPAD = 16 / (int)sizeof(T);
+  static constexpr int VPAD = 16 / (int)sizeof(T);
+  static constexpr int KLD = D + KPAD;
+  static constexpr int VLD = KC + VPAD;
+  static constexpr int KPIECES = KC * (D / VEC) / 512;   // 16-byte K pieces per thread
+  static constexpr int VTASKS = (KC / 4) * (D / 4);      // 4 keys x 4 dims tasks
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  typedef T vec4_t __attribute__((ext_vector_type(4)));
+  vec_t kr[KPIECES];
+  vec4_t vr[4];
+
+  __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
+                                       int64_t c0, int64_t kend, int hkv, int g) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < KPIECES; ++r) {
+      const int pc = tid + 512 * r;
+      const int key = pc / (D / VEC), col = pc % (D / VEC);
+      const int64_t s = c0 + key;
+      if (s < kend) {
+        kr[r] = *reinterpret_cast<const vec_t*>(k + (s * hkv + g) * D + col * VEC);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kr[r][e] = (T)0.0f;
+      }
+    }
+    if (tid < VTASKS) {
+      const int kg = tid % (KC / 4), dg = tid / (KC / 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t s = c0 + 4 * kg + b;
+        if (s < kend) {
+          vr[b] = *reinterpret_cast<const vec4_t*>(v + (s * hkv + g) * D + 4 * dg);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vr[b][e] = (T)0.0f;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* __restrict__ ks_lds, T* __restrict__ vt_lds) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < KPIECES; ++r) {
+      const int pc = tid + 512 * r;
+      const int key = pc / (D / VEC), col = pc % (D / VEC);
+      *reinterpret_cast<vec_t*>(ks_lds + key * KLD + col * VEC) = kr[r];
+    }
+    if (tid < VTASKS) {
+      const int kg = tid % (KC / 4), dg = tid / (KC / 4);
+      const int pos = vt_pos_of_group4(kg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vec4_t col;
+        col[0] = vr[0][e];
+        col[1] = vr[1][e];
+        col[2] = vr[2][e];
+        col[3] = vr[3][e];
+        *reinterpret_cast<vec4_t*>(vt_lds + (4 * dg + e) * VLD + pos) = col;
+      }
+    }
+  }
+};
+
+template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
+template <> __device__ __forceinline__ bf16x8 pack8<bf16>(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
+  return r;
+}
+template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+  return r;
+}
+
+template <typename T, int D, int MODE>
+__global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
+  typedef KVStage<T, D> Stage;
+  typedef typename Frag<T>::type frag_t;
+  __shared__ __attribute__((aligned(16))) T ks_lds[2][KC * Stage::KLD];
+  __shared__ __attribute__((aligned(16))) T vt_lds[2][D * Stage::VLD];
+
+  const int64_t logical = xcd_logical(blockIdx.x, a.padded);
+  if (logical >= a.ntiles) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int group = a.hq / a.hkv;
+  const T* __restrict__ q = (const T*)a.q;
+  const T* __restrict__ k = (const T*)a.k;
+  const T* __restrict__ v = (const T*)a.v;
+
+  int g;                      // kv-head of the tile
+  int64_t kbeg, kend;         // key range of the tile
+  int64_t row = -1;           // this lane's row (token * hq + head), -1 if none
+  int64_t dst_index = -1;     // where this lane's result goes (row or entry)
+  int64_t wtok0 = 0;          // first token of the wave (causal modes)
+  bool wave_live;             // the wave has at least one row
+
+  if (MODE == MODE_SELECTED) {
+    const int64_t tile = logical;
+    const int32_t* toffs = a.tile_offsets;
+    if (tile >= toffs[a.nlists]) return;
+    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int64_t b = L / a.hkv;
+    g = L % a.hkv;
+    const int n = a.blk_seq[b], j = a.blk_local[b];
+    kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
+    kend = kbeg + a.block;
+    const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kRowsPerTile +
+                       (int64_t)w * kRowsPerWave;
+    const int64_t e1 = a.list_offsets[L + 1];
+    wave_live = e0 < e1;
+    if (e0 + r32 < e1) {
+      const int32_t ev = a.entries[e0 + r32];
+      dst_index = ev;
+      row = ev / a.ks;
+    }
+  } else {
+    const int tt = 32 * (8 / a.hg);
+    const int nhs = a.hq / a.hg;
+    int64_t blk_start, blk_end;
+    int u, hs;
+    if (MODE == MODE_SELF) {
+      u = a.nu - 1 - (int)(logical % a.nu);
+      const int64_t rest = logical / a.nu;
+      hs = (int)(rest % nhs);
+      const int64_t b = a.nb - 1 - rest / nhs;
+      const int n = a.blk_seq[b], i = a.blk_local[b];
+      blk_start = (int64_t)a.cu[n] + (int64_t)i * a.block;
+      blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
+    } else {
+      const int n = (int)(logical % a.nseq);
+      const int64_t rest = logical / a.nseq;
+      u = a.nu - 1 - (int)(rest % a.nu);
+      hs = (int)(rest / a.nu);
+      blk_start = a.cu[n];
+      blk_end = a.cu[n + 1];
+    }
+    const int64_t tok0 = blk_start + (int64_t)u * tt;
+    if (tok0 >= blk_end) return;
+    const int h = hs * a.hg + (w % a.hg);
+    g = h / group;
+    wtok0 = tok0 + (int64_t)(w / a.hg) * 32;
+    wave_live = wtok0 < blk_end;
+    kbeg = blk_start;
+    kend = min(tok0 + tt, blk_end);
+    if (wtok0 + r32 < blk_end) {
+      row = (wtok0 + r32) * a.hq + h;
+      dst_index = row;
+    }
+  }
+
+  frag_t qf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = (row >= 0) ? load8(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  Stage st;
+  const int nch = (int)((kend - kbeg + KC - 1) / KC);
+  st.load(k, v, kbeg, kend, a.hkv, g);
+  st.store(ks_lds[0], vt_lds[0]);
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    const int64_t c0 = kbeg + (int64_t)c * KC;
+    if (c + 1 < nch) st.load(k, v, c0 + KC, kend, a.hkv, g);
+
+    // which 32-key tiles of this chunk the wave needs, and whether to mask
+    bool act[2];
+    bool need_mask = false;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (MODE == MODE_SELECTED) {
+        act[kt] = wave_live;
+      } else {
+        act[kt] = wave_live && (c0 + 32 * kt <= wtok0 + 31) && (c0 + 32 * kt < kend);
+        need_mask = need_mask || (act[kt] && (c0 + 32 * kt + 31 > wtok0));
+      }
+    }
+    if (act[0] || act[1]) {
+      const T* kl = ks_lds[buf];
+      const T* vl = vt_lds[buf];
+      f32x16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+        if (act[kt]) {
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            frag_t af = load8(kl + (32 * kt + r32) * Stage::KLD + 16 * kk + 8 * half);
+            s[kt] = mma_k16(af, qf[kk], s[kt]);
+          }
+        }
+      }
+      // scale to the log2 domain, mask, running max
+      float x[2][16];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float val = act[kt] ? s[kt][e] * a.scale_log2 : -INFINITY;
+          if (MODE != MODE_SELECTED && need_mask) {
+            const int64_t key = c0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (key > wtok0 + r32) val = -INFINITY;
+          }
+          x[kt][e] = val;
+          mloc = fmaxf(mloc, val);
+        }
+      }
+      mloc = fmaxf(mloc, swap_half(mloc));
+      const float m_new = fmaxf(m_run, mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          x[kt][e] = fast_exp2(x[kt][e] - m_use);
+          psum += x[kt][e];
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        if (!act[kt]) continue;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const frag_t pf = pack8<T>(&x[kt][8 * mm]);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            frag_t vf = load8(vl + (32 * dt + r32) * Stage::VLD + 32 * kt + 16 * mm + 8 * half);
+            o[dt] = mma_k16(vf, pf, o[dt]);
+          }
+        }
+      }
+    }
+    if (c + 1 < nch) st.store(ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
+    __syncthreads();
+  }
+
+  // epilogue: combine the two half-row sums, normalise, write
+  const float l_tot = l_run + swap_half(l_run);
+  if (row < 0) return;
+  const float inv = 1.f / l_tot;
+  const float lse = (m_run + fast_log2(l_tot)) * kLn2;
+  const bool final_out = (MODE == MODE_DENSE) || (MODE == MODE_SELF && a.ks == 0);
+  if (final_out) {
+    T* dst = (T*)a.out + dst_index * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        typedef T vec4_t __attribute__((ext_vector_type(4)));
+        vec4_t val;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) val[b] = from_f32<T>(o[dt][4 * aa + b] * inv);
+        *reinterpret_cast<vec4_t*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
+      }
+    if (a.lse_out && half == 0) a.lse_out[dst_index] = lse;
+  } else {
+    float* dst = a.o_part + dst_index * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        f32x4 val;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) val[b] = o[dt][4 * aa + b] * inv;
+        *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
+      }
+    if (half == 0) a.lse_part[dst_index] = lse;
+  }
+}
+
+template <int MODE>
+static hipError_t attn_dispatch(const Plan& p, const AttnArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)a.padded), blk(512);
+  if (p.dtype == MOBA_DTYPE_BF16) {
+    if (p.d == 128) hipLaunchKernelGGL((k_attn<bf16, 128, MODE>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_attn<bf16, 64, MODE>), grid, blk, 0, s, a);
+  } else {
+    if (p.d == 128) hipLaunchKernelGGL((k_attn<float, 128, MODE>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_attn<float, 64, MODE>), grid, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+static AttnArgs base_args(const Plan& p, const void* q, const void* k, const void* v,
+                          const int32_t* cu) {
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu = cu;
+  a.nb = p.nb;
+  a.nseq = p.nseq;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.hg = p.hg;
+  a.block = p.block;
+  a.ks = p.ks;
+  a.scale_log2 = p.scale * kLog2e;
+  return a;
+}
+
+hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, const void* v,
+                                const int32_t* cu_dev, const Work& w, hipStream_t s) {
+  if (p.ks == 0 || p.nentries == 0) return hipSuccess;
+  AttnArgs a = base_args(p, q, k, v, cu_dev);
+  a.blk_seq = w.blk_seq;
+  a.blk_local = w.blk_local;
+  a.list_offsets = w.list_offsets;
+  a.tile_offsets = w.tile_offsets;
+  a.entries = w.entries;
+  a.nlists = p.nlists;
+  a.o_part = w.o_sel;
+  a.lse_part = w.lse_sel;
+  a.ntiles = p.max_tiles;
+  a.padded = (p.max_tiles + 7) / 8 * 8;
+  return attn_dispatch<MODE_SELECTED>(p, a, s);
+}
+
+hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const void* v,
+                            const int32_t* cu_dev, const Work& w, void* out, float* lse_out,
+                            hipStream_t s) {
+  if (p.nb == 0) return hipSuccess;
+  AttnArgs a = base_args(p, q, k, v, cu_dev);
+  a.blk_seq = w.blk_seq;
+  a.blk_local = w.blk_local;
+  a.o_part = w.o_self;
+  a.lse_part = w.lse_self;
+  a.out = out;
+  a.lse_out = lse_out;
+  const int tt = 32 * (8 / p.hg);
+  a.nu = (p.block + tt - 1) / tt;
+  a.ntiles = p.nb * a.nu * (p.hq / p.hg);
+  a.padded = (a.ntiles + 7) / 8 * 8;
+  return attn_dispatch<MODE_SELF>(p, a, s);
+}
+
+hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const void* v,
+                             const int32_t* cu_dev, void* out, float* lse_out, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  AttnArgs a = base_args(p, q, k, v, cu_dev);
+  a.out = out;
+  a.lse_out = lse_out;
+  const int tt = 32 * (8 / p.hg);
+  a.nu = (int)((p.max_len + tt - 1) / tt);
+  a.ntiles = (int64_t)p.nseq * a.nu * (p.hq / p.hg);
+  a.padded = (a.ntiles + 7) / 8 * 8;
+  return attn_dispatch<MODE_DENSE>(p, a, s);
+}
+
+}  // namespace moba

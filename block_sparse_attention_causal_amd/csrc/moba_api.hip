@@ -1,0 +1,430 @@
+// C ABI of the MoBA prefill library: argument checks, the per-call plan,
+// workspace carving, stage ordering and optional per-stage HIP-event timing.
+// The library allocates no device memory; every launch goes on the caller's
+// stream and nothing here synchronises the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "moba_plan.h"
+
+namespace moba {
+
+static thread_local char g_err[512] = "";
+
+static moba_status_t fail(moba_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* shape,
+                        int32_t block, int32_t topk, bool need_block, Plan* p, char* err,
+                        size_t errlen) {
+  (void)err;
+  (void)errlen;
+  if (!shape) return fail(MOBA_ERR_INVALID_ARG, "shape is NULL");
+  if (!cu) return fail(MOBA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if (nseq < 0) return fail(MOBA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (cu[0] != 0) return fail(MOBA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int32_t n = 0; n < nseq; ++n)
+    if (cu[n + 1] < cu[n]) return fail(MOBA_ERR_INVALID_ARG, "cu_seqlens decreases at %d", n);
+  if (shape->num_q_heads < 1 || shape->num_kv_heads < 1)
+    return fail(MOBA_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (shape->num_q_heads % shape->num_kv_heads)
+    return fail(MOBA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (shape->head_dim != 64 && shape->head_dim != 128)
+    return fail(MOBA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", shape->head_dim);
+  if (shape->dtype != MOBA_DTYPE_F32 && shape->dtype != MOBA_DTYPE_BF16)
+    return fail(MOBA_ERR_UNSUPPORTED, "dtype %d not supported", shape->dtype);
+  if (need_block) {
+    if (block < 1) return fail(MOBA_ERR_INVALID_ARG, "block_size must be >= 1");
+    if (block % 64) return fail(MOBA_ERR_UNSUPPORTED, "block_size must be a multiple of 64");
+    if (topk < 1) return fail(MOBA_ERR_INVALID_ARG, "topk must be >= 1");
+    if (topk - 1 > kMaxSelected)
+      return fail(MOBA_ERR_UNSUPPORTED, "topk - 1 must be <= %d", kMaxSelected);
+  }
+  Plan& P = *p;
+  P = Plan();
+  P.nseq = nseq;
+  P.T = cu[nseq];
+  P.hq = shape->num_q_heads;
+  P.hkv = shape->num_kv_heads;
+  P.d = shape->head_dim;
+  P.dtype = shape->dtype;
+  P.group = P.hq / P.hkv;
+  P.hg = gcd_int(P.group, 8);
+  P.block = need_block ? block : 0;
+  P.topk = need_block ? topk : 1;
+  P.ks = P.topk - 1;
+  float sc = shape->softmax_scale;
+  P.scale = (sc > 0.f && isfinite(sc)) ? sc : 1.0f / sqrtf((float)P.d);
+  if (P.T * P.hq >= (int64_t(1) << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "T * num_q_heads must be < 2^31");
+  if (P.T * P.hq * (int64_t)P.ks >= (int64_t(1) << 31))
+    return fail(MOBA_ERR_UNSUPPORTED, "T * num_q_heads * (topk - 1) must be < 2^31");
+  for (int32_t n = 0; n < nseq; ++n) {
+    const int64_t len = (int64_t)cu[n + 1] - cu[n];
+    if (len > P.max_len) P.max_len = len;
+    if (!need_block) continue;
+    const int64_t nbn = (len + block - 1) / block;
+    P.nb += nbn;
+    if (nbn > P.max_nb) P.max_nb = (int32_t)nbn;
+    P.tri += (int64_t)P.hkv * nbn * (nbn - 1) / 2;
+    for (int64_t i = 0; i < nbn; ++i) {
+      const int64_t li = std::min((int64_t)block, len - i * block);
+      P.nentries += li * P.hq * std::min((int64_t)P.ks, i);
+    }
+  }
+  if (need_block && P.ks > 0) {
+    if (P.max_nb > kMaxBlocksPerSeq)
+      return fail(MOBA_ERR_UNSUPPORTED, "a sequence has more than %d blocks", kMaxBlocksPerSeq);
+    if (P.tri >= (int64_t(1) << 31))
+      return fail(MOBA_ERR_UNSUPPORTED, "routing histogram too large");
+  }
+  P.nlists = P.nb * P.hkv;
+  P.max_tiles = P.nentries / kRowsPerTile + P.nlists + 1;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t rows = P.T * P.hq;
+  P.off_blk_base = take(sizeof(int32_t) * (nseq + 1));
+  P.off_tri_base = take(sizeof(int32_t) * (nseq + 1));
+  P.off_blk_seq = take(sizeof(int32_t) * P.nb);
+  P.off_blk_local = take(sizeof(int32_t) * P.nb);
+  P.off_kbar = take(sizeof(float) * P.nb * P.hkv * P.d);
+  P.off_kbar_split =
+      take(P.dtype == MOBA_DTYPE_BF16 ? sizeof(bf16) * 3 * P.nb * P.hkv * P.d : 0);
+  if (P.ks > 0) {
+    P.off_sel = take(sizeof(int32_t) * rows * P.ks);
+    P.off_hist = take(sizeof(int32_t) * P.tri);
+    P.off_chunk_off = take(sizeof(int32_t) * P.tri);
+    P.off_list_count = take(sizeof(int32_t) * P.nlists);
+    P.off_list_offsets = take(sizeof(int32_t) * (P.nlists + 1));
+    P.off_tile_offsets = take(sizeof(int32_t) * (P.nlists + 1));
+    P.off_entries = take(sizeof(int32_t) * P.nentries);
+    P.off_o_self = take(sizeof(float) * rows * P.d);
+    P.off_lse_self = take(sizeof(float) * rows);
+    P.off_o_sel = take(sizeof(float) * rows * P.ks * P.d);
+    P.off_lse_sel = take(sizeof(float) * rows * P.ks);
+  }
+  P.total = off;
+  return MOBA_OK;
+}
+
+Work carve(const Plan& p, void* base) {
+  char* b = (char*)base;
+  Work w = {};
+  w.blk_base = (int32_t*)(b + p.off_blk_base);
+  w.tri_base = (int32_t*)(b + p.off_tri_base);
+  w.blk_seq = (int32_t*)(b + p.off_blk_seq);
+  w.blk_local = (int32_t*)(b + p.off_blk_local);
+  w.kbar = (float*)(b + p.off_kbar);
+  w.kbar_split = (bf16*)(b + p.off_kbar_split);
+  if (p.ks > 0) {
+    w.sel = (int32_t*)(b + p.off_sel);
+    w.hist = (int32_t*)(b + p.off_hist);
+    w.chunk_off = (int32_t*)(b + p.off_chunk_off);
+    w.list_count = (int32_t*)(b + p.off_list_count);
+    w.list_offsets = (int32_t*)(b + p.off_list_offsets);
+    w.tile_offsets = (int32_t*)(b + p.off_tile_offsets);
+    w.entries = (int32_t*)(b + p.off_entries);
+    w.o_self = (float*)(b + p.off_o_self);
+    w.lse_self = (float*)(b + p.off_lse_self);
+    w.o_sel = (float*)(b + p.off_o_sel);
+    w.lse_sel = (float*)(b + p.off_lse_sel);
+  }
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Optional per-stage timing.
+enum { ST_POOL = 0, ST_GATE, ST_ROUTE, ST_SELF, ST_SELECTED, ST_MERGE, ST_DENSE, ST_COUNT };
+static const char* kStageNames[ST_COUNT] = {"pool", "gate", "route", "attn_self",
+                                            "attn_selected", "merge", "attn_dense"};
+constexpr int kMaxTimed = 4096;
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  bool created = false;
+  hipEvent_t ev0[kMaxTimed], ev1[kMaxTimed];
+  int stage[kMaxTimed];
+  int used = 0;
+};
+static Timing g_timing;
+
+struct StageScope {
+  int slot = -1;
+  hipStream_t s;
+  StageScope(int st, hipStream_t stream) : s(stream) {
+    if (!g_timing.enabled) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.enabled || g_timing.used >= kMaxTimed) return;
+    slot = g_timing.used++;
+    g_timing.stage[slot] = st;
+    (void)hipEventRecord(g_timing.ev0[slot], s);
+  }
+  ~StageScope() {
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev1[slot], s);
+  }
+};
+
+static moba_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOBA_OK;
+  return fail(MOBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace moba
+
+using namespace moba;
+
+extern "C" {
+
+int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+const char* moba_last_error(void) { return g_err; }
+
+size_t moba_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                            const moba_shape_t* shape, int32_t block_size, int32_t topk) {
+  Plan p;
+  if (make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0) !=
+      MOBA_OK)
+    return 0;
+  g_err[0] = 0;
+  return p.total;
+}
+
+moba_status_t moba_forward(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                           int32_t num_seqs, const moba_shape_t* shape, int32_t block_size,
+                           int32_t topk, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t* sel_out, float* lse_out, void* stream) {
+  Plan p;
+  moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (p.T == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!q || !k || !v || !out || !cu_seqlens_dev)
+    return fail(MOBA_ERR_INVALID_ARG, "q, k, v, out and cu_seqlens_dev must be non-NULL");
+  if (!workspace) return fail(MOBA_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (workspace_bytes < p.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                p.total);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  Work w = carve(p, workspace);
+  int32_t* sel = sel_out ? sel_out : w.sel;
+  hipError_t e = launch_setup(p, cu_seqlens_dev, w, s);
+  if (e != hipSuccess) return hip_status(e, "setup");
+  {
+    StageScope t(ST_POOL, s);
+    e = launch_pool(p, k, cu_seqlens_dev, w, w.kbar, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "pool");
+  if (p.ks > 0) {
+    {
+      StageScope t(ST_GATE, s);
+      e = launch_gate(p, q, cu_seqlens_dev, w, sel, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "gate");
+    {
+      StageScope t(ST_ROUTE, s);
+      e = launch_route(p, sel, cu_seqlens_dev, w, w.list_offsets, w.entries, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "route");
+    {
+      StageScope t(ST_SELECTED, s);
+      e = launch_attn_selected(p, q, k, v, cu_seqlens_dev, w, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "selected-block attention");
+  }
+  {
+    StageScope t(ST_SELF, s);
+    e = launch_attn_self(p, q, k, v, cu_seqlens_dev, w, out, lse_out, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "self-block attention");
+  if (p.ks > 0) {
+    {
+      StageScope t(ST_MERGE, s);
+      e = launch_merge(p, cu_seqlens_dev, w, out, lse_out, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "merge");
+  }
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+moba_status_t moba_dense_causal_forward(const void* q, const void* k, const void* v,
+                                        const int32_t* cu_seqlens_dev,
+                                        const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        const moba_shape_t* shape, void* out, float* lse_out,
+                                        void* stream) {
+  Plan p;
+  moba_status_t st = make_plan(cu_seqlens_host, num_seqs, shape, 0, 1, false, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (p.T == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!q || !k || !v || !out || !cu_seqlens_dev)
+    return fail(MOBA_ERR_INVALID_ARG, "q, k, v, out and cu_seqlens_dev must be non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e;
+  {
+    StageScope t(ST_DENSE, s);
+    e = launch_attn_dense(p, q, k, v, cu_seqlens_dev, out, lse_out, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "dense causal attention");
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+moba_status_t moba_block_pool(const void* k, const int32_t* cu_seqlens_dev,
+                              const int32_t* cu_seqlens_host, int32_t num_seqs,
+                              const moba_shape_t* shape, int32_t block_size, float* kbar_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, 1, true, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (p.T == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!k || !kbar_out || !cu_seqlens_dev || !workspace)
+    return fail(MOBA_ERR_INVALID_ARG, "k, kbar_out, cu_seqlens_dev and workspace must be non-NULL");
+  if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (workspace_bytes < p.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                p.total);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  Work w = carve(p, workspace);
+  hipError_t e = launch_setup(p, cu_seqlens_dev, w, s);
+  if (e != hipSuccess) return hip_status(e, "setup");
+  {
+    StageScope t(ST_POOL, s);
+    e = launch_pool(p, k, cu_seqlens_dev, w, kbar_out, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "pool");
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+moba_status_t moba_route_sizes(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                               const moba_shape_t* shape, int32_t block_size, int32_t topk,
+                               int64_t* num_lists, int64_t* num_entries) {
+  Plan p;
+  moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (!num_lists || !num_entries) return fail(MOBA_ERR_INVALID_ARG, "output pointer is NULL");
+  *num_lists = p.nlists;
+  *num_entries = p.nentries;
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
+                         const int32_t* cu_seqlens_host, int32_t num_seqs,
+                         const moba_shape_t* shape, int32_t block_size, int32_t topk,
+                         int32_t* list_offsets, int32_t* entries, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Plan p;
+  moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (p.ks < 1) return fail(MOBA_ERR_INVALID_ARG, "moba_route needs topk >= 2");
+  if (p.T == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!sel_dev || !cu_seqlens_dev || !list_offsets || (!entries && p.nentries > 0) || !workspace)
+    return fail(MOBA_ERR_INVALID_ARG, "NULL device pointer");
+  if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (workspace_bytes < p.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                p.total);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  Work w = carve(p, workspace);
+  hipError_t e = launch_setup(p, cu_seqlens_dev, w, s);
+  if (e != hipSuccess) return hip_status(e, "setup");
+  {
+    StageScope t(ST_ROUTE, s);
+    e = launch_route(p, sel_dev, cu_seqlens_dev, w, list_offsets, entries, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "route");
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+moba_status_t moba_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (enable && !g_timing.created) {
+    for (int i = 0; i < kMaxTimed; ++i) {
+      hipError_t e0 = hipEventCreate(&g_timing.ev0[i]);
+      hipError_t e1 = hipEventCreate(&g_timing.ev1[i]);
+      if (e0 != hipSuccess || e1 != hipSuccess) return hip_status(e0 != hipSuccess ? e0 : e1, "hipEventCreate");
+    }
+    g_timing.created = true;
+  }
+  g_timing.enabled = enable != 0;
+  g_timing.used = 0;
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+int32_t moba_timing_read(double* stage_ms, int32_t* stage_launches, int32_t max_stages) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  const int n = max_stages < ST_COUNT ? max_stages : ST_COUNT;
+  for (int i = 0; i < n; ++i) {
+    if (stage_ms) stage_ms[i] = 0.0;
+    if (stage_launches) stage_launches[i] = 0;
+  }
+  for (int i = 0; i < g_timing.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timing.ev1[i]) != hipSuccess) continue;
+    if (hipEventElapsedTime(&ms, g_timing.ev0[i], g_timing.ev1[i]) != hipSuccess) continue;
+    const int st = g_timing.stage[i];
+    if (st < n) {
+      if (stage_ms) stage_ms[st] += ms;
+      if (stage_launches) stage_launches[st] += 1;
+    }
+  }
+  g_timing.used = 0;
+  return n;
+}
+
+const char* moba_stage_name(int32_t stage) {
+  if (stage < 0 || stage >= ST_COUNT) return "";
+  return kStageNames[stage];
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the MoBA kernels (gfx950, wave64).
+//
+// Matrix-core convention used everywhere: one "k16 step" is a 32x32 output tile
+// updated with a contraction of 16. For bf16 it is one v_mfma_f32_32x32x16_bf16;
+// for fp32 it is eight v_mfma_f32_32x32x2_f32 over the same register data. In
+// both cases lane l supplies, for operand A (32 x 16, row-major m x k),
+// A[l % 32][8 * (l / 32) + e] for e = 0..7, and for operand B (16 x 32),
+// B[8 * (l / 32) + e][l % 32]. The 16 accumulator floats of lane l hold
+// C[8 * (i / 4) + 4 * (l / 32) + (i % 4)][l % 32], i = 0..15.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// Eight consecutive elements of the contraction dimension for one lane.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ f32x16 mma_k16(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mma_k16(const f32x8& a, const f32x8& b, f32x16 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+// 16-byte vector loads/stores of "8 elements" (bf16: one 16 B access; fp32: two).
+__device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 load8(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ T zero8();
+template <> __device__ __forceinline__ bf16x8 zero8<bf16x8>() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+  return z;
+}
+template <> __device__ __forceinline__ f32x8 zero8<f32x8>() {
+  f32x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = 0.0f;
+  return z;
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, kWave); }
+__device__ __forceinline__ int swap_half(int x) { return __shfl_xor(x, 32, kWave); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Workgroups are dispatched to the 8 XCDs round-robin (id % 8). Remap the
+// dispatch id so that each XCD walks one contiguous range of logical tiles:
+// neighbouring tiles (which share K/V or pooled keys) then share that XCD's L2.
+// `padded` is the launched grid size, a multiple of 8.
+__device__ __forceinline__ int64_t xcd_logical(int64_t id, int64_t padded) {
+  return (id & 7) * (padded >> 3) + (id >> 3);
+}
+
+// Sequence index n with cu[n] <= tok < cu[n+1]; empty sequences are skipped.
+__device__ __forceinline__ int seq_of_token(const int32_t* cu, int nseq, int64_t tok) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Largest index L in [0, n) with offs[L] <= x (offs ascending, offs[0] = 0).
+__device__ __forceinline__ int upper_index(const int32_t* offs, int n, int64_t x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)offs[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace moba

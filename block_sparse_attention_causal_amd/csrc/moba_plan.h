@@ -1,0 +1,93 @@
+// Host-side plan of one MoBA forward call: sizes, workspace carving, launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moba.h"
+#include "moba_device.h"
+
+namespace moba {
+
+constexpr int kRowsPerWave = 32;           // one 32-row MFMA tile per wave
+constexpr int kWavesPerWG = 8;             // attention / gate workgroups: 512 threads
+constexpr int kRowsPerTile = kRowsPerWave * kWavesPerWG;   // routed rows per attention tile
+constexpr int kMaxSelected = 16;           // topk - 1 limit (per-lane register lists)
+constexpr int kMaxBlocksPerSeq = 16384;    // per-sequence block counters live in LDS
+
+struct Plan {
+  // problem
+  int32_t nseq = 0;
+  int64_t T = 0;
+  int32_t hq = 0, hkv = 0, d = 0, dtype = 0;
+  int32_t group = 1;        // Hq / Hkv
+  int32_t hg = 1;           // heads of one group that share a workgroup: gcd(group, 8)
+  int32_t block = 0, topk = 1, ks = 0;   // ks = topk - 1
+  float scale = 0.f;
+  // derived sizes
+  int64_t nb = 0;           // total blocks over all sequences
+  int32_t max_nb = 0;       // largest per-sequence block count
+  int64_t max_len = 0;      // longest sequence
+  int64_t tri = 0;          // sum_n Hkv * NB_n * (NB_n - 1) / 2 (route histograms)
+  int64_t nlists = 0;       // nb * hkv
+  int64_t nentries = 0;     // routed (row, slot) pairs
+  int64_t max_tiles = 0;    // launch bound for the selected-block attention grid
+  // workspace offsets (bytes); -1 when not used
+  size_t off_blk_base = 0, off_tri_base = 0, off_blk_seq = 0, off_blk_local = 0;
+  size_t off_kbar = 0, off_kbar_split = 0, off_sel = 0;
+  size_t off_hist = 0, off_chunk_off = 0, off_list_count = 0, off_list_offsets = 0;
+  size_t off_tile_offsets = 0, off_entries = 0;
+  size_t off_o_self = 0, off_lse_self = 0, off_o_sel = 0, off_lse_sel = 0;
+  size_t total = 0;
+};
+
+// Fills `plan` from validated arguments. Returns MOBA_OK or an error status and
+// writes a message into `err` (size errlen).
+moba_status_t make_plan(const int32_t* cu_host, int32_t nseq, const moba_shape_t* shape,
+                        int32_t block, int32_t topk, bool need_block, Plan* plan, char* err,
+                        size_t errlen);
+
+// Device pointers into a carved workspace.
+struct Work {
+  int32_t* blk_base;     // [nseq + 1] first global block id of each sequence
+  int32_t* tri_base;     // [nseq + 1] first route-histogram slot of each sequence
+  int32_t* blk_seq;      // [nb] sequence of each global block
+  int32_t* blk_local;    // [nb] index of each global block inside its sequence
+  float* kbar;           // [nb, hkv, d] pooled keys
+  bf16* kbar_split;      // [3, nb, hkv, d] pooled keys as hi + mid + lo bf16 (bf16 inputs)
+  int32_t* sel;          // [T, hq, ks] selected blocks
+  int32_t* hist;         // [tri] per (query block, kv-head) counts per past block
+  int32_t* chunk_off;    // [tri] start of each (query block, kv-head) inside each list
+  int32_t* list_count;   // [nlists]
+  int32_t* list_offsets; // [nlists + 1]
+  int32_t* tile_offsets; // [nlists + 1]
+  int32_t* entries;      // [nentries] row * ks + slot, grouped by list
+  float* o_self;         // [T * hq, d]
+  float* lse_self;       // [T * hq]
+  float* o_sel;          // [T * hq * ks, d]
+  float* lse_sel;        // [T * hq * ks]
+};
+
+Work carve(const Plan& p, void* base);
+
+// Kernel launchers (all asynchronous on `stream`).
+hipError_t launch_setup(const Plan& p, const int32_t* cu_dev, const Work& w, hipStream_t s);
+hipError_t launch_pool(const Plan& p, const void* k, const int32_t* cu_dev, const Work& w,
+                       float* kbar, hipStream_t s);
+hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, const Work& w,
+                       int32_t* sel, hipStream_t s);
+hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev, const Work& w,
+                        int32_t* list_offsets, int32_t* entries, hipStream_t s);
+hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, const void* v,
+                                const int32_t* cu_dev, const Work& w, hipStream_t s);
+// Self-block causal attention. With ks == 0 it writes the final output.
+hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const void* v,
+                            const int32_t* cu_dev, const Work& w, void* out, float* lse_out,
+                            hipStream_t s);
+hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const void* v,
+                             const int32_t* cu_dev, void* out, float* lse_out, hipStream_t s);
+hipError_t launch_merge(const Plan& p, const int32_t* cu_dev, const Work& w, void* out,
+                        float* lse_out, hipStream_t s);
+
+}  // namespace moba

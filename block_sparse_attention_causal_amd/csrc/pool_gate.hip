@@ -1,0 +1,388 @@
+// Block table set-up, block mean-pool (a1) and gate + causal block mask + top-k (a2).
+//
+// Pool: one mean-pooled key per (block, kv-head) (Kimi发布MoBA突破性实现无限上下文,
+// "PyTorch实现关键要点"; MoBA终极指南, "MoBA核心技术原理深度解析": pooling
+// comes after the rotary embedding, which the caller has already applied).
+// Gate: for every (token, q-head) row, score = q . Kbar[j] for each past block j
+// of the row's sequence, keep the best topk-1 (MoBA README, "Parameter-less
+// Gating Mechanism"; FAQ from issue #27: the own block is forced and not gated,
+// so topk-1 past blocks are chosen and the final block is never a candidate).
+#include "moba_plan.h"
+
+namespace moba {
+
+// ---------------------------------------------------------------------------
+// Set-up: per-sequence first global block id and first histogram slot.
+// One workgroup; each thread scans a contiguous slice of sequences.
+__global__ void __launch_bounds__(256) k_setup(const int32_t* __restrict__ cu, int nseq,
+                                               int block, int hkv, int32_t* blk_base,
+                                               int32_t* tri_base) {
+  __shared__ int64_t part_b[256], part_t[256];
+  const int t = threadIdx.x;
+  const int per = (nseq + 255) / 256;
+  const int n0 = min(nseq, t * per), n1 = min(nseq, n0 + per);
+  int64_t sb = 0, st = 0;
+  for (int n = n0; n < n1; ++n) {
+    int64_t nb = ((int64_t)cu[n + 1] - cu[n] + block - 1) / block;
+    sb += nb;
+    st += (int64_t)hkv * nb * (nb - 1) / 2;
+  }
+  part_b[t] = sb;
+  part_t[t] = st;
+  __syncthreads();
+  if (t == 0) {
+    int64_t ab = 0, at = 0;
+    for (int i = 0; i < 256; ++i) {
+      int64_t xb = part_b[i], xt = part_t[i];
+      part_b[i] = ab;
+      part_t[i] = at;
+      ab += xb;
+      at += xt;
+    }
+  }
+  __syncthreads();
+  int64_t ab = part_b[t], at = part_t[t];
+  for (int n = n0; n < n1; ++n) {
+    blk_base[n] = (int32_t)ab;
+    tri_base[n] = (int32_t)at;
+    int64_t nb = ((int64_t)cu[n + 1] - cu[n] + block - 1) / block;
+    ab += nb;
+    at += (int64_t)hkv * nb * (nb - 1) / 2;
+  }
+  if (n1 == nseq && n0 < n1) {
+    blk_base[nseq] = (int32_t)ab;
+    tri_base[nseq] = (int32_t)at;
+  }
+  if (nseq == 0 && t == 0) {
+    blk_base[0] = 0;
+    tri_base[0] = 0;
+  }
+}
+
+// Sequence and in-sequence index of every global block.
+__global__ void __launch_bounds__(256) k_block_info(const int32_t* __restrict__ blk_base, int nseq,
+                                                    int64_t nb, int32_t* blk_seq,
+                                                    int32_t* blk_local) {
+  int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nb) return;
+  int n = upper_index(blk_base, nseq, b);
+  // skip empty sequences that share the same base
+  while (n + 1 < nseq && blk_base[n + 1] <= b) ++n;
+  blk_seq[b] = n;
+  blk_local[b] = (int32_t)(b - blk_base[n]);
+}
+
+hipError_t launch_setup(const Plan& p, const int32_t* cu_dev, const Work& w, hipStream_t s) {
+  hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, s, cu_dev, p.nseq, p.block, p.hkv,
+                     w.blk_base, w.tri_base);
+  if (p.nb > 0)
+    hipLaunchKernelGGL(k_block_info, dim3((unsigned)((p.nb + 255) / 256)), dim3(256), 0, s,
+                       w.blk_base, p.nseq, p.nb, w.blk_seq, w.blk_local);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a1: block mean-pool. One workgroup per (block, kv-head); each thread owns 16
+// bytes of columns and sums a strided subset of the block's rows in fp32; the
+// row-lanes are then added in a fixed order, so the result is deterministic.
+// Also writes the pooled key split into three bf16 terms (hi + mid + lo equals
+// the fp32 value exactly for normal numbers), used by the bf16 gate.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
+                                              const int32_t* __restrict__ cu,
+                                              const int32_t* __restrict__ blk_seq,
+                                              const int32_t* __restrict__ blk_local, int hkv,
+                                              int block, int64_t nb, float* __restrict__ kbar,
+                                              bf16* __restrict__ kbar_split) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CPR = D / VEC;          // threads per row
+  constexpr int RL = 256 / CPR;         // row lanes
+  __shared__ float red[RL][D + 1];
+  const int64_t b = blockIdx.x / hkv;
+  const int g = blockIdx.x % hkv;
+  const int n = blk_seq[b];
+  const int i = blk_local[b];
+  const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
+  const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
+  const int cg = threadIdx.x % CPR, rl = threadIdx.x / CPR;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  const T* src = k + (s0 * hkv + g) * D + cg * VEC;
+  const int64_t stride = (int64_t)hkv * D;
+  int64_t r = rl;
+  for (; r + 3 * RL < len; r += 4 * RL) {
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t x0 = *reinterpret_cast<const vec_t*>(src + r * stride);
+    vec_t x1 = *reinterpret_cast<const vec_t*>(src + (r + RL) * stride);
+    vec_t x2 = *reinterpret_cast<const vec_t*>(src + (r + 2 * RL) * stride);
+    vec_t x3 = *reinterpret_cast<const vec_t*>(src + (r + 3 * RL) * stride);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x0[e]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x1[e]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x2[e]);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x3[e]);
+  }
+  for (; r < len; r += RL) {
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t x0 = *reinterpret_cast<const vec_t*>(src + r * stride);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x0[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) red[rl][cg * VEC + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    float sum = 0.f;
+    for (int l = 0; l < RL; ++l) sum += red[l][c];
+    const float mean = sum / (float)len;
+    const int64_t o = (b * hkv + g) * D + c;
+    kbar[o] = mean;
+    if (kbar_split) {
+      bf16 hi = (bf16)mean;
+      float r1 = mean - (float)hi;
+      bf16 mid = (bf16)r1;
+      float r2 = r1 - (float)mid;
+      const int64_t part = nb * hkv * D;
+      kbar_split[o] = hi;
+      kbar_split[part + o] = mid;
+      kbar_split[2 * part + o] = (bf16)r2;
+    }
+  }
+}
+
+hipError_t launch_pool(const Plan& p, const void* k, const int32_t* cu_dev, const Work& w,
+                       float* kbar, hipStream_t s) {
+  if (p.nb == 0) return hipSuccess;
+  dim3 grid((unsigned)(p.nb * p.hkv));
+  bf16* split = (p.dtype == MOBA_DTYPE_BF16) ? w.kbar_split : nullptr;
+  if (p.dtype == MOBA_DTYPE_BF16) {
+    if (p.d == 128)
+      hipLaunchKernelGGL((k_pool<bf16, 128>), grid, dim3(256), 0, s, (const bf16*)k, cu_dev,
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+    else
+      hipLaunchKernelGGL((k_pool<bf16, 64>), grid, dim3(256), 0, s, (const bf16*)k, cu_dev,
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+  } else {
+    if (p.d == 128)
+      hipLaunchKernelGGL((k_pool<float, 128>), grid, dim3(256), 0, s, (const float*)k, cu_dev,
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+    else
+      hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, s, (const float*)k, cu_dev,
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a2: gate + causal block mask + top-(topk-1).
+//
+// Workgroup = 8 waves = (8/HG token sub-tiles of 32) x (HG q-heads of one kv
+// group), all inside one block of one sequence, so they share one candidate
+// range [0, i) and one kv-head's pooled keys. Pooled keys are staged through
+// LDS 32 blocks at a time. Scores S^T = Kbar . Q^T come from the matrix cores
+// (bf16: three passes over the hi/mid/lo split of Kbar, products exact, fp32
+// accumulation; fp32: fp32 matrix ops). Lane l owns row l % 32 and sees 16 of
+// every 32 candidate blocks; its running best list is kept sorted by (score
+// descending, block ascending) in registers, then merged with the lane that
+// holds the other 16 (lane l ^ 32). Ties therefore go to the lower block.
+__device__ __forceinline__ bool better(float s1, int j1, float s2, int j2) {
+  return s1 > s2 || (s1 == s2 && j1 < j2);
+}
+
+template <int KB>
+__device__ __forceinline__ void list_insert(float (&bs)[KB], int (&bj)[KB], int ks, float s,
+                                            int j) {
+#pragma unroll
+  for (int p = 0; p < KB; ++p) {
+    if (p < ks) {
+      const bool b = better(s, j, bs[p], bj[p]);
+      const float ts = bs[p];
+      const int tj = bj[p];
+      bs[p] = b ? s : ts;
+      bj[p] = b ? j : tj;
+      s = b ? ts : s;
+      j = b ? tj : j;
+    }
+  }
+}
+
+constexpr int kNoBlock = 0x7fffffff;
+
+template <typename T, int D, int NP, int KB>
+__global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
+                                              const int32_t* __restrict__ cu,
+                                              const int32_t* __restrict__ blk_base,
+                                              const int32_t* __restrict__ blk_seq,
+                                              const int32_t* __restrict__ blk_local,
+                                              const T* __restrict__ kparts, int64_t nb, int hq,
+                                              int hkv, int hg, int block, int ks, int64_t ntiles,
+                                              int64_t padded, int32_t* __restrict__ sel) {
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int LD = D + PAD;
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ __attribute__((aligned(16))) T kb[NP][32][LD];
+
+  const int64_t logical = xcd_logical(blockIdx.x, padded);
+  if (logical >= ntiles) return;
+  const int tt = 32 * (8 / hg);                       // tokens per workgroup tile
+  const int nu = (block + tt - 1) / tt;
+  const int nhs = hq / hg;
+  const int u = (int)(logical % nu);
+  const int64_t rest = logical / nu;
+  const int64_t b = nb - 1 - (rest % nb);
+  const int hs = (int)(rest / nb);
+  const int n = blk_seq[b];
+  const int i = blk_local[b];
+  const int64_t seq0 = cu[n];
+  const int64_t blk_end = min(seq0 + (int64_t)(i + 1) * block, (int64_t)cu[n + 1]);
+  const int64_t tok0 = seq0 + (int64_t)i * block + (int64_t)u * tt;
+  if (tok0 >= blk_end || hs >= nhs) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int h = hs * hg + (w % hg);
+  const int g = h / (hq / hkv);
+  const int64_t tok = tok0 + (int64_t)(w / hg) * 32 + r32;
+  const bool row_ok = tok < blk_end;
+  const int64_t row = tok * hq + h;
+
+  float bs[KB];
+  int bj[KB];
+#pragma unroll
+  for (int p = 0; p < KB; ++p) { bs[p] = -INFINITY; bj[p] = kNoBlock; }
+
+  if (i > 0) {
+    typedef typename Frag<T>::type frag_t;
+    frag_t qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = row_ok ? load8(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+    const int64_t gbase = blk_base[n];
+    const int64_t part_stride = nb * hkv * D;
+    float ws = -INFINITY;
+    int wj = kNoBlock;
+    for (int j0 = 0; j0 < i; j0 += 32) {
+      __syncthreads();
+      // stage 32 candidate blocks x NP parts of pooled keys
+      constexpr int PIECES = NP * 32 * (D / VEC);
+      for (int pc = threadIdx.x; pc < PIECES; pc += 512) {
+        const int part = pc / (32 * (D / VEC));
+        const int rr = (pc / (D / VEC)) % 32;
+        const int col = pc % (D / VEC);
+        typedef T vec_t __attribute__((ext_vector_type(VEC)));
+        vec_t x;
+        if (j0 + rr < i) {
+          x = *reinterpret_cast<const vec_t*>(kparts + part * part_stride +
+                                              ((gbase + j0 + rr) * hkv + g) * D + col * VEC);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[e] = (T)0.0f;
+        }
+        *reinterpret_cast<vec_t*>(&kb[part][rr][col * VEC]) = x;
+      }
+      __syncthreads();
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int part = 0; part < NP; ++part) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          frag_t a = load8(&kb[part][r32][16 * kk + 8 * half]);
+          acc = mma_k16(a, qf[kk], acc);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const float s = acc[e];
+        if (j < i && better(s, j, ws, wj)) {
+          list_insert<KB>(bs, bj, ks, s, j);
+#pragma unroll
+          for (int p = 0; p < KB; ++p)
+            if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
+        }
+      }
+    }
+    // merge with the partner lane's list (same row, the other 16 of each 32)
+    float os[KB];
+    int oj[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) { os[p] = swap_half(bs[p]); oj[p] = swap_half(bj[p]); }
+#pragma unroll
+    for (int p = 0; p < KB; ++p)
+      if (p < ks && oj[p] != kNoBlock) list_insert<KB>(bs, bj, ks, os[p], oj[p]);
+  }
+  if (!row_ok || half != 0) return;
+  // ascending block order; missing entries (kNoBlock) sort last and become -1
+  int sj[KB];
+#pragma unroll
+  for (int p = 0; p < KB; ++p) sj[p] = kNoBlock;
+#pragma unroll
+  for (int p = 0; p < KB; ++p) {
+    if (p < ks) {
+      int j = bj[p];
+#pragma unroll
+      for (int r = 0; r < KB; ++r) {
+        if (r < ks) {
+          const bool lt = j < sj[r];
+          const int t = sj[r];
+          sj[r] = lt ? j : t;
+          j = lt ? t : j;
+        }
+      }
+    }
+  }
+  int32_t* dst = sel + row * ks;
+#pragma unroll
+  for (int p = 0; p < KB; ++p)
+    if (p < ks) dst[p] = (sj[p] == kNoBlock) ? -1 : sj[p];
+}
+
+template <typename T, int D, int NP>
+static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const Work& w,
+                             const T* parts, int32_t* sel, hipStream_t s, int64_t ntiles,
+                             int64_t padded) {
+  dim3 grid((unsigned)padded), blk(512);
+#define MOBA_GATE(KBV)                                                                        \
+  hipLaunchKernelGGL((k_gate<T, D, NP, KBV>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,  \
+                     w.blk_local, parts, p.nb, p.hq, p.hkv, p.hg, p.block, p.ks, ntiles,     \
+                     padded, sel)
+  if (p.ks <= 2) MOBA_GATE(2);
+  else if (p.ks <= 4) MOBA_GATE(4);
+  else if (p.ks <= 8) MOBA_GATE(8);
+  else MOBA_GATE(16);
+#undef MOBA_GATE
+}
+
+hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, const Work& w,
+                       int32_t* sel, hipStream_t s) {
+  if (p.ks == 0 || p.nb == 0) return hipSuccess;
+  const int tt = 32 * (8 / p.hg);
+  const int64_t nu = (p.block + tt - 1) / tt;
+  const int64_t ntiles = p.nb * nu * (p.hq / p.hg);
+  const int64_t padded = (ntiles + 7) / 8 * 8;
+  if (p.dtype == MOBA_DTYPE_BF16) {
+    if (p.d == 128)
+      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, sel, s, ntiles,
+                                     padded);
+    else
+      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, sel, s, ntiles,
+                                    padded);
+  } else {
+    if (p.d == 128)
+      gate_dispatch_kb<float, 128, 1>(p, (const float*)q, cu_dev, w, w.kbar, sel, s, ntiles,
+                                      padded);
+    else
+      gate_dispatch_kb<float, 64, 1>(p, (const float*)q, cu_dev, w, w.kbar, sel, s, ntiles,
+                                     padded);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -1,0 +1,174 @@
+/*
+ * moba.h -- C ABI of the MoBA (Mixture of Block Attention) causal prefill
+ * forward library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (MoBA: Mixture of Block Attention for
+ * Long-Context LLMs, README, "Trainable Block Sparse Attention" and
+ * "Parameter-less Gating Mechanism"; FAQ entries from issue #27; Kimi发布MoBA
+ * 突破性实现无限上下文, "MoBA：基于块的混合注意力机制" and "PyTorch实现关键要点"):
+ * every sequence's keys are cut into blocks of block_size tokens (the last
+ * block may be shorter) and each block is mean-pooled. For every (token,
+ * query-head) row, the unscaled dot product of the query with the pooled keys
+ * of the row's kv-head scores every past block of the same sequence; the
+ * top-(topk-1) past blocks are kept (ties go to the lower block index), the
+ * row's own block is always attended with a causal mask, and future blocks
+ * never are. Softmax attention (scale 1/sqrt(head_dim) unless overridden)
+ * runs over the union of those key sets, computed as one causal partial over
+ * the own block and one partial per kept block, combined exactly through
+ * their log-sum-exp.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout: packed variable-length "THD" tensors, contiguous and row-major:
+ *   q, out: [T, Hq, D]; k, v: [T, Hkv, D]; T = cu_seqlens[num_seqs].
+ *   Sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]). Blocks restart at
+ *   every sequence start; nothing crosses a sequence boundary.
+ * GQA: query head h reads kv-head h / (Hq / Hkv).
+ * cu_seqlens: num_seqs+1 int32 entries, cu[0] = 0, non-decreasing (empty
+ *   sequences allowed). Two copies are passed: cu_seqlens_host (host memory,
+ *   read during the call for validation and launch sizes) and cu_seqlens_dev
+ *   (device memory, read by the kernels). They must hold the same values.
+ * Device pointers: q, k, v, out, workspace, sel_out, lse_out, kbar_out and
+ *   every *_dev pointer are device memory owned by the caller. The library
+ *   allocates no device memory, keeps no pointer after the call returns, and
+ *   never synchronises the device.
+ * Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *   stream). MOBA_OK means "validated and enqueued"; faults inside a kernel
+ *   surface at the caller's next synchronisation.
+ * Errors: arguments are checked on the host before anything is enqueued; on any
+ *   error nothing is enqueued and nothing is written. moba_last_error() gives a
+ *   message for the calling thread's last failed call.
+ * Determinism: outputs are bitwise identical for identical inputs.
+ * Limits: D in {64, 128}; block_size a positive multiple of 64; topk-1 <= 16;
+ *   T*Hq and T*Hq*(topk-1) below 2^31; at most 16384 blocks per sequence.
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_ABI_VERSION 1
+
+typedef enum {
+  MOBA_OK = 0,
+  MOBA_ERR_INVALID_ARG = 1,   /* null pointer, bad count, inconsistent shapes */
+  MOBA_ERR_UNSUPPORTED = 2,   /* valid request outside the supported limits */
+  MOBA_ERR_WORKSPACE = 3,     /* workspace smaller than moba_workspace_bytes() */
+  MOBA_ERR_HIP = 4            /* the HIP runtime refused a launch */
+} moba_status_t;
+
+typedef enum {
+  MOBA_DTYPE_F32 = 0,         /* q, k, v, out in fp32; fp32 MFMA, fp32 accumulate */
+  MOBA_DTYPE_BF16 = 1         /* q, k, v, out in bf16; bf16 MFMA, fp32 accumulate */
+} moba_dtype_t;
+
+typedef struct {
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* D, 64 or 128 */
+  int32_t dtype;              /* a moba_dtype_t */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(D) */
+} moba_shape_t;
+
+/* Version of this ABI (MOBA_ABI_VERSION). */
+int32_t moba_abi_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none). The string
+ * stays valid until the thread's next call into the library. */
+const char* moba_last_error(void);
+
+/* Device workspace bytes that moba_forward needs for this batch: the pooled
+ * keys, the selected block ids, the routing lists and the per-part partial
+ * outputs. Host-only; returns 0 and sets the last error if the arguments are
+ * invalid. */
+size_t moba_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                            const moba_shape_t* shape, int32_t block_size, int32_t topk);
+
+/* MoBA causal prefill forward (see the top of this file for what it computes).
+ *   out:     [T, Hq, D] in the input dtype, written in full.
+ *   topk:    >= 1; counts the row's own block, so topk-1 past blocks are kept
+ *            (all of them when a row has fewer). topk = 1 is block-diagonal
+ *            causal attention.
+ *   sel_out: optional (NULL to skip), int32 [T, Hq, topk-1]: the kept past
+ *            blocks of every row as sequence-local block ids in ascending
+ *            order, padded with -1. Ignored when topk == 1.
+ *   lse_out: optional (NULL to skip), fp32 [T, Hq]: natural-log log-sum-exp of
+ *            the scaled logits over each row's attended keys.
+ *   workspace: at least moba_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+moba_status_t moba_forward(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                           int32_t num_seqs, const moba_shape_t* shape, int32_t block_size,
+                           int32_t topk, void* out, void* workspace, size_t workspace_bytes,
+                           int32_t* sel_out, float* lse_out, void* stream);
+
+/* Dense causal flash attention with the same kernels (one block per sequence):
+ * every row attends to keys 0..t of its own sequence. The comparison point for
+ * MoBA's speed-up (README, "Seamlessly Transition between Full and Sparse
+ * Attention"). Needs no workspace.
+ *   out: [T, Hq, D] in the input dtype.  lse_out: optional fp32 [T, Hq]. */
+moba_status_t moba_dense_causal_forward(const void* q, const void* k, const void* v,
+                                        const int32_t* cu_seqlens_dev,
+                                        const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        const moba_shape_t* shape, void* out, float* lse_out,
+                                        void* stream);
+
+/* The block mean-pool step alone (Kimi发布MoBA突破性实现无限上下文, "PyTorch实现
+ * 关键要点": one mean-pooled key per block). Only k is read.
+ *   kbar_out:  fp32 [NB, Hkv, D], NB = sum_n ceil(S_n / block_size), blocks
+ *              numbered sequence by sequence; the last block of a sequence is
+ *              averaged over its true length. Sums run in fp32 in a fixed order.
+ *   workspace: at least moba_workspace_bytes(cu_seqlens_host, num_seqs, shape,
+ *              block_size, 1) bytes, 256-byte aligned (holds the block table). */
+moba_status_t moba_block_pool(const void* k, const int32_t* cu_seqlens_dev,
+                              const int32_t* cu_seqlens_host, int32_t num_seqs,
+                              const moba_shape_t* shape, int32_t block_size, float* kbar_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of routing lists and routed entries for a batch, for sizing the
+ * buffers of moba_route. A list is a (global block, kv-head) pair, numbered
+ * block-major: list = global_block * Hkv + kv_head. Host-only. Returns MOBA_OK
+ * or MOBA_ERR_INVALID_ARG. */
+moba_status_t moba_route_sizes(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                               const moba_shape_t* shape, int32_t block_size, int32_t topk,
+                               int64_t* num_lists, int64_t* num_entries);
+
+/* The routing step alone: the MoE-style inversion of a selection map (MoBA
+ * README, abstract: MoE principles applied to attention; Kimi article, "PyTorch
+ * 实现关键要点": the data is reorganised by selected block before attention).
+ *   sel_dev:        int32 [T, Hq, topk-1] as written by moba_forward's sel_out
+ *                   (valid ids first, ascending, then -1).
+ *   list_offsets:   int32 [num_lists + 1] out: list L holds entries
+ *                   [list_offsets[L], list_offsets[L+1]).
+ *   entries:        int32 [num_entries] out: entry = row * (topk-1) + slot, where
+ *                   row = token * Hq + head and sel[row][slot] names the block;
+ *                   rows ascend within each list.
+ *   workspace:      as for moba_forward with the same arguments.
+ * Requires topk >= 2. */
+moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
+                         const int32_t* cu_seqlens_host, int32_t num_seqs,
+                         const moba_shape_t* shape, int32_t block_size, int32_t topk,
+                         int32_t* list_offsets, int32_t* entries, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Per-stage timing with HIP events, for benchmarks. While enabled, every call
+ * records an event pair around each stage's launches on the call's stream.
+ * moba_timing_read() waits for the recorded events, writes per stage the summed
+ * milliseconds and the number of timed launches, then clears the record.
+ * Stage ids: 0 pool, 1 gate, 2 route, 3 self-block attention, 4 selected-block
+ * attention, 5 merge, 6 dense causal attention. Returns the number of stages
+ * written. At most 4096 event pairs are kept; later ones are not recorded. */
+moba_status_t moba_timing_enable(int32_t enable);
+int32_t moba_timing_read(double* stage_ms, int32_t* stage_launches, int32_t max_stages);
+const char* moba_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H */

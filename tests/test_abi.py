@@ -1,0 +1,130 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/moba.h declares, and rejects bad arguments on the host before any
+launch. No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_sparse_attention_causal_amd as moba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moba.h")
+
+FAKE = ctypes.c_void_p(0x10000000)   # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moba.LIB_PATH):
+        from block_sparse_attention_causal_amd import build
+        build.build()
+    return moba._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moba_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_core_calls():
+    names = declared_functions()
+    for n in ("moba_forward", "moba_workspace_bytes", "moba_dense_causal_forward",
+              "moba_last_error", "moba_block_pool", "moba_route"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(moba.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(declared_functions()) == set(moba.exported_symbols())
+    assert lib.moba_abi_version() == 1
+
+
+def _shape(hq=32, hkv=8, d=128, dtype=1, scale=0.0):
+    return moba.moba_shape_t(hq, hkv, d, dtype, scale)
+
+
+def _cu(lens):
+    cu = [0]
+    for s in lens:
+        cu.append(cu[-1] + s)
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def _fwd(lib, cu, shape, block, topk, ws_bytes=1 << 40, ws=FAKE):
+    return lib.moba_forward(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(cu.data_ptr()),
+                            cu.numel() - 1, ctypes.byref(shape), block, topk, FAKE, ws, ws_bytes,
+                            None, None, None)
+
+
+@pytest.mark.parametrize("kw,block,topk,code", [
+    (dict(hq=6, hkv=4), 2048, 3, moba.MOBA_ERR_INVALID_ARG),
+    (dict(hq=0), 2048, 3, moba.MOBA_ERR_INVALID_ARG),
+    (dict(d=96), 2048, 3, moba.MOBA_ERR_UNSUPPORTED),
+    (dict(dtype=7), 2048, 3, moba.MOBA_ERR_UNSUPPORTED),
+    (dict(), 100, 3, moba.MOBA_ERR_UNSUPPORTED),
+    (dict(), 0, 3, moba.MOBA_ERR_INVALID_ARG),
+    (dict(), 2048, 0, moba.MOBA_ERR_INVALID_ARG),
+    (dict(), 2048, 18, moba.MOBA_ERR_UNSUPPORTED),
+])
+def test_invalid_shapes_are_rejected(lib, kw, block, topk, code):
+    st = _fwd(lib, _cu([4096]), _shape(**kw), block, topk)
+    assert st == code
+    assert lib.moba_last_error().decode() != ""
+
+
+def test_bad_cu_seqlens(lib):
+    bad = torch.tensor([0, 100, 50], dtype=torch.int32)
+    assert _fwd(lib, bad, _shape(), 64, 3) == moba.MOBA_ERR_INVALID_ARG
+    bad0 = torch.tensor([5, 100], dtype=torch.int32)
+    assert _fwd(lib, bad0, _shape(), 64, 3) == moba.MOBA_ERR_INVALID_ARG
+
+
+def test_workspace_checks(lib):
+    cu = _cu([4096])
+    assert _fwd(lib, cu, _shape(), 2048, 3, ws_bytes=1000) == moba.MOBA_ERR_WORKSPACE
+    assert _fwd(lib, cu, _shape(), 2048, 3, ws=ctypes.c_void_p(0x10000010)) == \
+        moba.MOBA_ERR_INVALID_ARG
+    assert _fwd(lib, cu, _shape(), 2048, 3, ws=None) == moba.MOBA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    cu = torch.tensor([0, 0, 0], dtype=torch.int32)
+    assert _fwd(lib, cu, _shape(), 2048, 3, ws_bytes=0, ws=None) == moba.MOBA_OK
+
+
+def test_workspace_bytes_and_route_sizes(lib):
+    n = moba.moba_workspace_bytes([0, 32768], 32, 8, 128, torch.bfloat16, 2048, 3)
+    T, rows = 32768, 32768 * 32
+    # the fp32 partial outputs dominate: one self part and topk-1 selected parts per row
+    assert n >= rows * 128 * 4 * 3
+    nl, ne = moba.moba_route_sizes([0, 32768], 32, 8, 128, torch.bfloat16, 2048, 3)
+    assert nl == 16 * 8
+    assert ne == sum(2048 * 32 * min(2, i) for i in range(16))
+    # block-diagonal attention needs no routing buffers
+    assert moba.moba_workspace_bytes([0, T], 32, 8, 128, torch.bfloat16, 2048, 1) < n
+    with pytest.raises(moba.MobaError):
+        moba.moba_workspace_bytes([0, T], 32, 8, 128, torch.bfloat16, 100, 3)
+
+
+def test_route_requires_topk_two(lib):
+    cu = _cu([1024])
+    st = lib.moba_route(FAKE, FAKE, ctypes.c_void_p(cu.data_ptr()), 1, ctypes.byref(_shape()), 64,
+                        1, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == moba.MOBA_ERR_INVALID_ARG
+
+
+def test_stage_names(lib):
+    assert [moba.moba_stage_name(i) for i in range(7)] == list(moba.STAGES)
+    assert moba.moba_stage_name(99) == ""
+
+
+def test_binding_refuses_cpu_tensors():
+    q = torch.zeros(64, 2, 64)
+    with pytest.raises(ValueError):
+        moba.moba_forward(q, q, q, [0, 64], 64, 3)
