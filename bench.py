@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark: MoBA causal prefill forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 1m]
+
+One step = one moba_forward call over the whole batch (pool, gate, route,
+selected-block attention, self-block attention, merge), inputs resident in HBM.
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed live
+with HIP events on the launch stream), the dense causal comparison from the same
+library, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoBA fwd tokens/s + MFMA util at S=128K/1M; speedup vs dense causal flash-attn"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 MFMA / vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+CONFIG_NAMES = {"tiny": "moba_fwd_tiny_2k_fp32", "llama32k": "moba_fwd_llama8b_32k",
+                "varlen131k": "moba_fwd_varlen_131k", "1m": "moba_fwd_1m",
+                "fine256k": "moba_fwd_fine_blocks_256k"}
+
+
+def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
+    """Algorithmic work per forward call, per stage (what the method must do)."""
+    ks = topk - 1
+    rows_sel_pairs = 0      # sum over rows of min(ks, i) * B   (selected keys)
+    self_pairs = 0          # sum over rows of own-block keys (causal)
+    gate_pairs = 0          # sum over rows of past blocks i
+    merge_parts = 0         # sum over rows of (1 + min(ks, i))
+    nb_total = 0
+    T = sum(seqlens)
+    for s in seqlens:
+        nb = (s + block - 1) // block
+        nb_total += nb
+        for i in range(nb):
+            L = min(block, s - i * block)
+            rows_sel_pairs += L * min(ks, i) * block
+            self_pairs += L * (L + 1) // 2
+            gate_pairs += L * i
+            merge_parts += L * (1 + min(ks, i))
+    return {
+        "attn_selected_flop": 4.0 * d * hq * rows_sel_pairs,
+        "attn_self_flop": 4.0 * d * hq * self_pairs,
+        "gate_flop": 2.0 * d * hq * gate_pairs,
+        "dense_flop": 4.0 * d * hq * sum(s * (s + 1) // 2 for s in seqlens),
+        # bytes: pool reads K and writes fp32 pooled keys; gate reads Q and writes
+        # the selection; merge reads every fp32 part (D values + lse) and writes out
+        "pool_bytes": elem_bytes * T * hkv * d + 4.0 * nb_total * hkv * d,
+        "gate_bytes": elem_bytes * T * hq * d + 4.0 * T * hq * ks,
+        "merge_bytes": hq * merge_parts * (4.0 * d + 4.0) + elem_bytes * T * hq * d,
+    }
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_causal_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, if it still applies."""
+    path = os.path.join(ROOT, "profiles", "traffic_attn_selected_1m.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest() or vals.get("kernel") != kernel_key:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, hq, budget_s, seed):
+    """The oracle, untuned, on a bounded sample of the workload's rows."""
+    import numpy as np
+    import oracle
+    from synth_inputs import sample_tokens
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    threads = min(threads, 16)
+    kf = oracle._f32(inp.k)
+    vf = oracle._f32(inp.v)
+
+    def run(ntok, sseed):
+        toks = sample_tokens(inp.seqlens, inp.block, ntok, seed=sseed)
+        toks = np.sort(np.random.default_rng(sseed).permutation(toks)[:ntok])
+        tt, hh = np.repeat(toks, hq), np.tile(np.arange(hq), len(toks))
+        t0 = time.perf_counter()
+        oracle.rows(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.block, inp.topk, tt, hh,
+                    k_f32=kf, v_f32=vf, nthreads=threads)
+        return len(toks), time.perf_counter() - t0
+
+    n0, t0 = run(8, seed + 100)                   # calibration
+    per_tok = t0 / max(n0, 1)
+    ntok = int(max(8, min(4096, budget_s / max(per_tok, 1e-6))))
+    n, t = run(ntok, seed + 200)
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d sampled tokens x %d q-heads of the workload (oracle fp64, pools every "
+                      "block, then gate + select + attend per row); %.1f s wall" % (n, hq, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="1m", choices=sorted(CONFIG_NAMES))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dense-steps", type=int, default=1)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_causal_amd as moba
+    from synth_inputs import CONFIGS, make_config
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] building inputs %s" % args.config, file=sys.stderr, flush=True)
+    inp = make_config(args.config, seed=args.seed, device=dev)
+    q, k, v = inp.q, inp.k, inp.v
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    cu_host = inp.cu_seqlens
+    cu_dev = cu_host.to(dev)
+    nbytes = moba.moba_workspace_bytes(cu_host, hq, hkv, d, q.dtype, inp.block, inp.topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    elem = q.element_size()
+    work = work_counts(inp.seqlens, hq, hkv, d, inp.block, inp.topk, elem)
+
+    def step():
+        moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,
+                          cu_seqlens_dev=cu_dev)
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_timing:
+        moba.moba_timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    stages = moba.moba_timing_read() if not args.no_timing else {}
+    moba.moba_timing_enable(False)
+    print("[bench] %d steps: %.3f ms/step" % (args.steps, ms), file=sys.stderr, flush=True)
+
+    # per-stage averages and rooflines
+    peak_mfma = PEAK_BF16_TFLOPS if q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+    stage_rep = {}
+    for name, (tot_ms, n) in stages.items():
+        if n == 0:
+            continue
+        avg = tot_ms / n
+        rep = {"avg_ms": avg, "launches": n}
+        if name in ("attn_selected", "attn_self"):
+            tf = work[name + "_flop"] / (avg * 1e-3) / 1e12
+            rep.update(bound="mfma", achieved_tflops=tf, frac=tf / peak_mfma)
+        elif name == "gate":
+            gbs = work["gate_bytes"] / (avg * 1e-3) / 1e9
+            tf = work["gate_flop"] / (avg * 1e-3) / 1e12
+            rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
+                       achieved_tflops=tf)
+        elif name in ("pool", "merge"):
+            gbs = work[name + "_bytes"] / (avg * 1e-3) / 1e9
+            rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)
+        stage_rep[name] = rep
+    roofline = None
+    if "attn_selected" in stage_rep:
+        s = stage_rep["attn_selected"]
+        traffic = load_traffic("attn_selected")
+        roofline = {"kernel": "attn_selected", "bound": "mfma",
+                    "achieved": round(s["achieved_tflops"], 2), "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": round(s["frac"], 4),
+                    "traffic": traffic,
+                    "avg_launch_ms": round(s["avg_ms"], 4),
+                    "algorithmic_flop_per_launch": work["attn_selected_flop"]}
+    attn_flop = work["attn_selected_flop"] + work["attn_self_flop"]
+
+    dense = None
+    if not args.no_dense:
+        print("[bench] dense causal comparison", file=sys.stderr, flush=True)
+        dout = torch.empty_like(q)
+        moba.moba_dense_causal_forward(q, k, v, cu_host, out=dout, cu_seqlens_dev=cu_dev)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.dense_steps):
+            moba.moba_dense_causal_forward(q, k, v, cu_host, out=dout, cu_seqlens_dev=cu_dev)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.dense_steps
+        dense = {"ms": dms, "tflops": work["dense_flop"] / (dms * 1e-3) / 1e12,
+                 "mfma_frac": work["dense_flop"] / (dms * 1e-3) / 1e12 / peak_mfma}
+        del dout
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, hq, args.cpu_budget, args.seed)
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic: seeded N(0,1) Q/K/V with planted needle blocks",
+        "config": {"workload": CONFIG_NAMES[args.config], "seqlens": inp.seqlens,
+                   "tokens": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
+                   "block_size": inp.block, "topk": inp.topk, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "effective_attn_tflops": attn_flop / (ms * 1e-3) / 1e12,
+        "attn_mfma_frac_of_step": attn_flop / (ms * 1e-3) / 1e12 / peak_mfma,
+        "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
+        "dense_causal": dense,
+        "stages": stage_rep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
