@@ -33,6 +33,7 @@ CONFIG_NAMES = {"tiny": "moba_fwd_tiny_2k_fp32", "llama32k": "moba_fwd_llama8b_3
 def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
     """Algorithmic work per forward call, per stage (what the method must do)."""
     ks = topk - 1
+    part_bytes = 2 if elem_bytes == 2 else 4   # partial outputs: fp16 for bf16 inputs
     rows_sel_pairs = 0      # sum over rows of min(ks, i) * B   (selected keys)
     self_pairs = 0          # sum over rows of own-block keys (causal)
     gate_pairs = 0          # sum over rows of past blocks i
@@ -54,10 +55,10 @@ def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
         "gate_flop": 2.0 * d * hq * gate_pairs,
         "dense_flop": 4.0 * d * hq * sum(s * (s + 1) // 2 for s in seqlens),
         # bytes: pool reads K and writes fp32 pooled keys; gate reads Q and writes
-        # the selection; merge reads every fp32 part (D values + lse) and writes out
+        # the selection; merge reads every part (D values + lse) and writes out
         "pool_bytes": elem_bytes * T * hkv * d + 4.0 * nb_total * hkv * d,
         "gate_bytes": elem_bytes * T * hq * d + 4.0 * T * hq * ks,
-        "merge_bytes": hq * merge_parts * (4.0 * d + 4.0) + elem_bytes * T * hq * d,
+        "merge_bytes": hq * merge_parts * (part_bytes * d + 4.0) + elem_bytes * T * hq * d,
     }
 
 
@@ -107,9 +108,11 @@ def cpu_baseline(inp, hq, budget_s, seed):
                     k_f32=kf, v_f32=vf, nthreads=threads)
         return len(toks), time.perf_counter() - t0
 
-    n0, t0 = run(8, seed + 100)                   # calibration
-    per_tok = t0 / max(n0, 1)
-    ntok = int(max(8, min(4096, budget_s / max(per_tok, 1e-6))))
+    # calibration: two small samples separate the fixed pooling cost from the per-token cost
+    n0, t0 = run(8, seed + 100)
+    n1, t1 = run(64, seed + 101)
+    per_tok = max(t1 - t0, 1e-6) / max(n1 - n0, 1)
+    ntok = int(max(8, min(8192, (budget_s - t0) / per_tok)))
     n, t = run(ntok, seed + 200)
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d sampled tokens x %d q-heads of the workload (oracle fp64, pools every "
@@ -128,6 +131,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -153,6 +158,15 @@ def main():
     out = torch.empty_like(q)
     elem = q.element_size()
     work = work_counts(inp.seqlens, hq, hkv, d, inp.block, inp.topk, elem)
+
+    if args.copy_calibration_mib > 0:
+        # one plain streaming kernel of known size: reads and writes N MiB of fp32
+        src = torch.ones((args.copy_calibration_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,

@@ -41,7 +41,7 @@ struct AttnArgs {
   const int32_t* list_offsets;
   const int32_t* tile_offsets;
   const int32_t* entries;
-  float* o_part;      // SELF with ks > 0: [T*hq, D]; SELECTED: [T*hq*ks, D]
+  void* o_part;       // SELF with ks > 0: [T*hq, D]; SELECTED: [T*hq*ks, D] (PartType<T>)
   float* lse_part;
   void* out;          // DENSE, or SELF with ks == 0: final output [T*hq, D]
   float* lse_out;     // optional with `out`
@@ -138,12 +138,58 @@ template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
   return r;
 }
 
+// Writes the 32 normalised output rows of every wave. The accumulator layout
+// gives each lane 4-value slivers of one row, so a direct store would touch 32
+// scattered rows 16 bytes at a time. Instead each wave transposes its rows
+// through LDS (the key loop is over, the arena is free) and then stores whole
+// rows: consecutive lanes cover one row's bytes contiguously.
+template <typename O, int D>
+__device__ __forceinline__ void store_rows(O* __restrict__ dst, char* smem, const f32x16 (&o)[D / 32],
+                                           float inv, int64_t dst_index, int w, int lane) {
+  constexpr int V = 16 / (int)sizeof(O);          // elements per 16-byte piece
+  constexpr int SLD = D + V;                       // padded staging row
+  constexpr int PPR = D / V;                       // pieces per row
+  constexpr int RPI = 64 / PPR;                    // rows per wave-wide store
+  typedef O vec4_t __attribute__((ext_vector_type(4)));
+  typedef O vec_t __attribute__((ext_vector_type(V)));
+  O* stage = reinterpret_cast<O*>(smem) + w * 32 * SLD;
+  const int half = lane >> 5, r32 = lane & 31;
+  __syncthreads();                                 // every wave is done with K/V
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      vec4_t val;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) val[b] = from_f32<O>(o[dt][4 * aa + b] * inv);
+      *reinterpret_cast<vec4_t*>(stage + r32 * SLD + 32 * dt + 8 * aa + 4 * half) = val;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / PPR, pc = lane % PPR;
+    const int64_t di = __shfl(dst_index, rr, 64);
+    if (di >= 0)
+      *reinterpret_cast<vec_t*>(dst + di * D + pc * V) =
+          *reinterpret_cast<const vec_t*>(stage + rr * SLD + pc * V);
+  }
+}
+
 template <typename T, int D, int MODE>
 __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
   typedef KVStage<T, D> Stage;
   typedef typename Frag<T>::type frag_t;
-  __shared__ __attribute__((aligned(16))) T ks_lds[2][KC * Stage::KLD];
-  __shared__ __attribute__((aligned(16))) T vt_lds[2][D * Stage::VLD];
+  // One LDS arena: two K buffers and two transposed-V buffers during the key
+  // loop, then the output staging area of the epilogue.
+  constexpr int KBUF = KC * Stage::KLD, VBUF = D * Stage::VLD;
+  constexpr int ARENA = (2 * KBUF + 2 * VBUF) * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem[ARENA];
+  static_assert(8 * 32 * (D + 16 / sizeof(typename PartType<T>::type)) *
+                        sizeof(typename PartType<T>::type) <= ARENA &&
+                    8 * 32 * (D + 16 / sizeof(T)) * sizeof(T) <= ARENA,
+                "output staging must fit in the LDS arena");
+  T* const ks_base = reinterpret_cast<T*>(smem);
+  T* const vt_base = ks_base + 2 * KBUF;
 
   const int64_t logical = xcd_logical(blockIdx.x, a.padded);
   if (logical >= a.ntiles) return;
@@ -230,7 +276,7 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
   Stage st;
   const int nch = (int)((kend - kbeg + KC - 1) / KC);
   st.load(k, v, kbeg, kend, a.hkv, g);
-  st.store(ks_lds[0], vt_lds[0]);
+  st.store(ks_base, vt_base);
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -251,8 +297,8 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
       }
     }
     if (act[0] || act[1]) {
-      const T* kl = ks_lds[buf];
-      const T* vl = vt_lds[buf];
+      const T* kl = ks_base + buf * KBUF;
+      const T* vl = vt_base + buf * VBUF;
       f32x16 s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -285,7 +331,6 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
       mloc = fmaxf(mloc, swap_half(mloc));
       const float m_new = fmaxf(m_run, mloc);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -294,12 +339,18 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
           x[kt][e] = fast_exp2(x[kt][e] - m_use);
           psum += x[kt][e];
         }
-      l_run = l_run * alpha + psum;
+      // Rescale only when some row's running max moved; otherwise alpha is
+      // exactly 1 for every lane and the multiply would change nothing.
+      if (__ballot(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      }
+      l_run += psum;
       m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         if (!act[kt]) continue;
@@ -314,42 +365,27 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
         }
       }
     }
-    if (c + 1 < nch) st.store(ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
+    if (c + 1 < nch) st.store(ks_base + (buf ^ 1) * KBUF, vt_base + (buf ^ 1) * VBUF);
     __syncthreads();
   }
 
   // epilogue: combine the two half-row sums, normalise, write
   const float l_tot = l_run + swap_half(l_run);
-  if (row < 0) return;
-  const float inv = 1.f / l_tot;
-  const float lse = (m_run + fast_log2(l_tot)) * kLn2;
+  const float inv = (row >= 0) ? 1.f / l_tot : 0.f;
   const bool final_out = (MODE == MODE_DENSE) || (MODE == MODE_SELF && a.ks == 0);
-  if (final_out) {
-    T* dst = (T*)a.out + dst_index * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        typedef T vec4_t __attribute__((ext_vector_type(4)));
-        vec4_t val;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) val[b] = from_f32<T>(o[dt][4 * aa + b] * inv);
-        *reinterpret_cast<vec4_t*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
-      }
-    if (a.lse_out && half == 0) a.lse_out[dst_index] = lse;
-  } else {
-    float* dst = a.o_part + dst_index * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        f32x4 val;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) val[b] = o[dt][4 * aa + b] * inv;
-        *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
-      }
-    if (half == 0) a.lse_part[dst_index] = lse;
+  if (row >= 0 && half == 0) {
+    const float lse = (m_run + fast_log2(l_tot)) * kLn2;
+    if (final_out) {
+      if (a.lse_out) a.lse_out[dst_index] = lse;
+    } else {
+      a.lse_part[dst_index] = lse;
+    }
   }
+  if (final_out)
+    store_rows<T, D>((T*)a.out, smem, o, inv, dst_index, w, lane);
+  else
+    store_rows<typename PartType<T>::type, D>((typename PartType<T>::type*)a.o_part, smem, o,
+                                              inv, dst_index, w, lane);
 }
 
 template <int MODE>

@@ -14,9 +14,9 @@ namespace moba {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_merge(const int32_t* __restrict__ cu, int nseq, int hq,
                                                int block, int ks, int64_t rows,
-                                               const float* __restrict__ o_self,
+                                               const typename PartType<T>::type* __restrict__ o_self,
                                                const float* __restrict__ lse_self,
-                                               const float* __restrict__ o_sel,
+                                               const typename PartType<T>::type* __restrict__ o_sel,
                                                const float* __restrict__ lse_sel,
                                                T* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int TPR = D / 4;            // threads per row, 4 floats each
@@ -30,16 +30,21 @@ __global__ void __launch_bounds__(256) k_merge(const int32_t* __restrict__ cu, i
   const int nsel = min(ks, i);
   float m = lse_self[row];
   for (int sl = 0; sl < nsel; ++sl) m = fmaxf(m, lse_sel[row * ks + sl]);
+  typedef typename PartType<T>::type P;
+  typedef P pvec4_t __attribute__((ext_vector_type(4)));
   float wgt = fast_exp2((lse_self[row] - m) * kLog2e);
   float den = wgt;
-  f32x4 x = *reinterpret_cast<const f32x4*>(o_self + row * D + 4 * c);
-  f32x4 acc = x * wgt;
+  pvec4_t x = *reinterpret_cast<const pvec4_t*>(o_self + row * D + 4 * c);
+  f32x4 acc;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = to_f32(x[b]) * wgt;
   for (int sl = 0; sl < nsel; ++sl) {
     const int64_t e = row * ks + sl;
     wgt = fast_exp2((lse_sel[e] - m) * kLog2e);
     den += wgt;
-    x = *reinterpret_cast<const f32x4*>(o_sel + e * D + 4 * c);
-    acc += x * wgt;
+    x = *reinterpret_cast<const pvec4_t*>(o_sel + e * D + 4 * c);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] += to_f32(x[b]) * wgt;
   }
   const float inv = 1.f / den;
   typedef T vec4_t __attribute__((ext_vector_type(4)));
@@ -59,19 +64,21 @@ hipError_t launch_merge(const Plan& p, const int32_t* cu_dev, const Work& w, voi
   if (p.dtype == MOBA_DTYPE_BF16) {
     if (p.d == 128)
       hipLaunchKernelGGL((k_merge<bf16, 128>), grid, blk, 0, s, cu_dev, p.nseq, p.hq, p.block,
-                         p.ks, rows, w.o_self, w.lse_self, w.o_sel, w.lse_sel, (bf16*)out, lse_out);
+                         p.ks, rows, (const f16*)w.o_self, w.lse_self, (const f16*)w.o_sel, w.lse_sel,
+                         (bf16*)out, lse_out);
     else
       hipLaunchKernelGGL((k_merge<bf16, 64>), grid, blk, 0, s, cu_dev, p.nseq, p.hq, p.block,
-                         p.ks, rows, w.o_self, w.lse_self, w.o_sel, w.lse_sel, (bf16*)out, lse_out);
+                         p.ks, rows, (const f16*)w.o_self, w.lse_self, (const f16*)w.o_sel, w.lse_sel,
+                         (bf16*)out, lse_out);
   } else {
     if (p.d == 128)
       hipLaunchKernelGGL((k_merge<float, 128>), grid, blk, 0, s, cu_dev, p.nseq, p.hq, p.block,
-                         p.ks, rows, w.o_self, w.lse_self, w.o_sel, w.lse_sel, (float*)out,
-                         lse_out);
+                         p.ks, rows, (const float*)w.o_self, w.lse_self, (const float*)w.o_sel,
+                         w.lse_sel, (float*)out, lse_out);
     else
       hipLaunchKernelGGL((k_merge<float, 64>), grid, blk, 0, s, cu_dev, p.nseq, p.hq, p.block,
-                         p.ks, rows, w.o_self, w.lse_self, w.o_sel, w.lse_sel, (float*)out,
-                         lse_out);
+                         p.ks, rows, (const float*)w.o_self, w.lse_self, (const float*)w.o_sel,
+                         w.lse_sel, (float*)out, lse_out);
   }
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@
 namespace moba {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -65,11 +66,19 @@ template <> __device__ __forceinline__ f32x8 zero8<f32x8>() {
   return z;
 }
 
+// Storage type of the per-part partial outputs: fp16 for bf16 inputs (normalised
+// outputs are bounded by max |v|, so fp16's range is ample and its rounding is 4x
+// finer than bf16's), fp32 for fp32 inputs.
+template <typename T> struct PartType { typedef float type; };
+template <> struct PartType<bf16> { typedef f16 type; };
+
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }     // RNE
 
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, kWave); }

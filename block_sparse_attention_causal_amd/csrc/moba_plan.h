@@ -63,9 +63,9 @@ struct Work {
   int32_t* list_offsets; // [nlists + 1]
   int32_t* tile_offsets; // [nlists + 1]
   int32_t* entries;      // [nentries] row * ks + slot, grouped by list
-  float* o_self;         // [T * hq, d]
+  void* o_self;          // [T * hq, d] partial outputs (fp16 for bf16 inputs, else fp32)
   float* lse_self;       // [T * hq]
-  float* o_sel;          // [T * hq * ks, d]
+  void* o_sel;           // [T * hq * ks, d] partial outputs, same type
   float* lse_sel;        // [T * hq * ks]
 };
 

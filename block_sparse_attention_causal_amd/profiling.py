@@ -1,0 +1,148 @@
+"""Summaries of rocprofv3 output for the MoBA kernels (text tables for profiles/).
+
+    python -m block_sparse_attention_causal_amd.profiling stats DIR
+        per-kernel calls / average / total duration from a --kernel-trace --stats run
+    python -m block_sparse_attention_causal_amd.profiling traffic FETCH_DIR WRITE_DIR \
+            --copy-mib N --kernel attn_selected
+        HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE, then
+        WRITE_SIZE), scaled by what the same counters read for a plain copy kernel
+        (torch.neg over N MiB of fp32: N MiB read, N MiB written).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import os
+import re
+import sys
+from collections import defaultdict
+
+# kernel key -> pattern on the (demangled or mangled) kernel name
+KERNELS = {
+    "attn_selected": r"k_attn<[^,]+, \d+, 1>|k_attnI\w+Li1EEEv",
+    "attn_self": r"k_attn<[^,]+, \d+, 0>|k_attnI\w+Li0EEEv",
+    "attn_dense": r"k_attn<[^,]+, \d+, 2>|k_attnI\w+Li2EEEv",
+    "gate": r"k_gate",
+    "pool": r"k_pool",
+    "merge": r"k_merge",
+    "route_count": r"k_route_count",
+    "route_lists": r"k_route_lists",
+    "route_offsets": r"k_route_offsets",
+    "route_scatter": r"k_route_scatter",
+    "setup": r"k_setup|k_block_info",
+    "copy_calibration": r"neg_kernel",
+}
+
+
+def kernel_key(name: str) -> str:
+    for key, pat in KERNELS.items():
+        if re.search(pat, name):
+            return key
+    return "other"
+
+
+def _find(dirpath: str, suffix: str) -> list[str]:
+    return sorted(glob.glob(os.path.join(dirpath, "**", "*" + suffix), recursive=True))
+
+
+def _col(header, *cands):
+    low = [h.lower() for h in header]
+    for c in cands:
+        if c.lower() in low:
+            return low.index(c.lower())
+    raise KeyError("none of %s in %s" % (cands, header))
+
+
+def stats(dirpath: str) -> str:
+    files = _find(dirpath, "kernel_stats.csv")
+    if not files:
+        raise FileNotFoundError("no *kernel_stats.csv under " + dirpath)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            r = csv.reader(fh)
+            hdr = next(r)
+            i_n, i_c = _col(hdr, "Name", "KernelName"), _col(hdr, "Calls")
+            i_t, i_a = _col(hdr, "TotalDurationNs"), _col(hdr, "AverageNs")
+            for row in r:
+                rows.append((kernel_key(row[i_n]), row[i_n], int(row[i_c]), float(row[i_t]),
+                             float(row[i_a])))
+    rows.sort(key=lambda x: -x[3])
+    out = ["| kernel | calls | avg ms | total ms | name |", "|---|---|---|---|---|"]
+    for key, name, calls, tot, avg in rows:
+        out.append("| %s | %d | %.4f | %.3f | %s |" % (key, calls, avg / 1e6, tot / 1e6,
+                                                     name[:90]))
+    return "\n".join(out)
+
+
+def _counter_per_dispatch(dirpath: str, counter: str) -> dict:
+    files = _find(dirpath, "counter_collection.csv")
+    if not files:
+        raise FileNotFoundError("no *counter_collection.csv under " + dirpath)
+    per = defaultdict(lambda: defaultdict(float))   # key -> dispatch -> value
+    for f in files:
+        with open(f) as fh:
+            r = csv.reader(fh)
+            hdr = next(r)
+            i_n = _col(hdr, "Kernel_Name", "Kernel-Name", "KernelName")
+            i_d = _col(hdr, "Dispatch_Id", "Dispatch-Id", "DispatchId", "Correlation_Id")
+            i_cn = _col(hdr, "Counter_Name", "Counter-Name")
+            i_cv = _col(hdr, "Counter_Value", "Counter-Value")
+            for row in r:
+                if row[i_cn] != counter:
+                    continue
+                per[kernel_key(row[i_n])][row[i_d]] += float(row[i_cv])
+    return {k: sorted(v.values()) for k, v in per.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_mib: int, kernel: str) -> str:
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    cal_bytes = copy_mib * 1024.0 * 1024.0
+    # the calibration copy is the largest elementwise dispatch of the run
+    f_copy = max(fetch.get("copy_calibration", [0.0])) * 1024.0
+    w_copy = max(write.get("copy_calibration", [0.0])) * 1024.0
+    f_scale = cal_bytes / f_copy if f_copy > 0 else float("nan")
+    w_scale = cal_bytes / w_copy if w_copy > 0 else float("nan")
+    fk = fetch.get(kernel, [])
+    wk = write.get(kernel, [])
+    f_mean = sum(fk) / len(fk) * 1024.0 if fk else float("nan")
+    w_mean = sum(wk) / len(wk) * 1024.0 if wk else float("nan")
+    lines = [
+        "kernel: %s" % kernel,
+        "launches_fetch: %d" % len(fk),
+        "launches_write: %d" % len(wk),
+        "fetch_bytes_raw_per_launch: %.6g" % f_mean,
+        "write_bytes_raw_per_launch: %.6g" % w_mean,
+        "copy_calibration_bytes: %.6g" % cal_bytes,
+        "copy_fetch_raw: %.6g" % f_copy,
+        "copy_write_raw: %.6g" % w_copy,
+        "fetch_scale: %.6g" % f_scale,
+        "write_scale: %.6g" % w_scale,
+        "hbm_read_bytes_per_launch: %.6g" % (f_mean * f_scale),
+        "hbm_write_bytes_per_launch: %.6g" % (w_mean * w_scale),
+        "hbm_bytes_per_launch: %.6g" % (f_mean * f_scale + w_mean * w_scale),
+    ]
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--kernel", default="attn_selected")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats(a.dir))
+    else:
+        print(traffic(a.fetch_dir, a.write_dir, a.copy_mib, a.kernel))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
