@@ -72,13 +72,20 @@ struct KVStage {
 
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
                                        int64_t c0, int64_t kend, int hkv, int g) {
+    if (c0 + KC <= kend) load_impl<false>(k, v, c0, kend, hkv, g);   // uniform branch
+    else load_impl<true>(k, v, c0, kend, hkv, g);
+  }
+
+  template <bool GUARD>
+  __device__ __forceinline__ void load_impl(const T* __restrict__ k, const T* __restrict__ v,
+                                            int64_t c0, int64_t kend, int hkv, int g) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int r = 0; r < KPIECES; ++r) {
       const int pc = tid + 512 * r;
       const int key = pc / (D / VEC), col = pc % (D / VEC);
       const int64_t s = c0 + key;
-      if (s < kend) {
+      if (!GUARD || s < kend) {
         kr[r] = *reinterpret_cast<const vec_t*>(k + (s * hkv + g) * D + col * VEC);
       } else {
 #pragma unroll
@@ -90,7 +97,7 @@ struct KVStage {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int64_t s = c0 + 4 * kg + b;
-        if (s < kend) {
+        if (!GUARD || s < kend) {
           vr[b] = *reinterpret_cast<const vec4_t*>(v + (s * hkv + g) * D + 4 * dg);
         } else {
 #pragma unroll
@@ -170,13 +177,13 @@ __device__ __forceinline__ void store_rows(O* __restrict__ dst, char* smem, cons
     const int rr = it * RPI + lane / PPR, pc = lane % PPR;
     const int64_t di = __shfl(dst_index, rr, 64);
     if (di >= 0)
-      *reinterpret_cast<vec_t*>(dst + di * D + pc * V) =
-          *reinterpret_cast<const vec_t*>(stage + rr * SLD + pc * V);
+      __builtin_nontemporal_store(*reinterpret_cast<const vec_t*>(stage + rr * SLD + pc * V),
+                                  reinterpret_cast<vec_t*>(dst + di * D + pc * V));
   }
 }
 
 template <typename T, int D, int MODE>
-__global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn(AttnArgs a) {
   typedef KVStage<T, D> Stage;
   typedef typename Frag<T>::type frag_t;
   // One LDS arena: two K buffers and two transposed-V buffers during the key
@@ -264,7 +271,7 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
   frag_t qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    qf[kk] = (row >= 0) ? load8(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+    qf[kk] = (row >= 0) ? load8_stream(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -273,99 +280,113 @@ __global__ void __launch_bounds__(512) k_attn(AttnArgs a) {
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  Stage st;
-  const int nch = (int)((kend - kbeg + KC - 1) / KC);
-  st.load(k, v, kbeg, kend, a.hkv, g);
-  st.store(ks_base, vt_base);
-  __syncthreads();
-
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    const int64_t c0 = kbeg + (int64_t)c * KC;
-    if (c + 1 < nch) st.load(k, v, c0 + KC, kend, a.hkv, g);
-
-    // which 32-key tiles of this chunk the wave needs, and whether to mask
-    bool act[2];
-    bool need_mask = false;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (MODE == MODE_SELECTED) {
-        act[kt] = wave_live;
-      } else {
-        act[kt] = wave_live && (c0 + 32 * kt <= wtok0 + 31) && (c0 + 32 * kt < kend);
-        need_mask = need_mask || (act[kt] && (c0 + 32 * kt + 31 > wtok0));
-      }
-    }
-    if (act[0] || act[1]) {
-      const T* kl = ks_base + buf * KBUF;
-      const T* vl = vt_base + buf * VBUF;
-      f32x16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
-        if (act[kt]) {
-#pragma unroll
+  // Multiply one staged chunk (LDS buffer `buf`, keys c0 .. c0+63) into the
+  // wave's running softmax state.
+  auto compute = [&](int buf, int64_t c0) {
+      // Does this wave need the chunk at all (causal: some key <= some row), and
+      // does any key of it lie after one of the wave's rows (then mask)?
+      const bool wave_needs = (MODE == MODE_SELECTED) ? wave_live : (wave_live && c0 <= wtok0 + 31);
+      const bool need_mask = (MODE != MODE_SELECTED) && (c0 + KC - 1 > wtok0);
+      if (wave_needs) {
+          const T* kl = ks_base + buf * KBUF;
+        const T* vl = vt_base + buf * VBUF;
+        // S^T for the chunk's two 32-key tiles: two independent MFMA chains, the
+        // LDS fragments read two steps ahead of their use
+        f32x16 s0, s1;
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+        {
+          const T* k0 = kl + r32 * Stage::KLD + 8 * half;
+          const T* k1 = k0 + 32 * Stage::KLD;
+          frag_t ring[4];
+          ring[0] = load8(k0);
+          ring[1] = load8(k1);
+          ring[2] = load8(k0 + 16);
+          ring[3] = load8(k1 + 16);
+  #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
-            frag_t af = load8(kl + (32 * kt + r32) * Stage::KLD + 16 * kk + 8 * half);
-            s[kt] = mma_k16(af, qf[kk], s[kt]);
+            s0 = mma_k16(ring[(2 * kk) & 3], qf[kk], s0);
+            if (kk + 2 < D / 16) ring[(2 * kk) & 3] = load8(k0 + 16 * (kk + 2));
+            s1 = mma_k16(ring[(2 * kk + 1) & 3], qf[kk], s1);
+            if (kk + 2 < D / 16) ring[(2 * kk + 1) & 3] = load8(k1 + 16 * (kk + 2));
           }
         }
-      }
-      // scale to the log2 domain, mask, running max
-      float x[2][16];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
+        if (need_mask) {
+          const int64_t tok = wtok0 + r32;
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t key = c0 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (key > tok) s0[e] = -INFINITY;
+            if (key + 32 > tok) s1[e] = -INFINITY;
+          }
+        }
+        // running max on the raw scores (the scale is positive), then one fma + exp2
+        float mx = vmax(s0[0], s1[0]);
+  #pragma unroll
+        for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
+        mx = vmax(mx, swap_half(mx));
+        const float m_new = vmax(m_run, mx * a.scale_log2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        float p0[16], p1[16];
+        float psum = 0.f;
+  #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float val = act[kt] ? s[kt][e] * a.scale_log2 : -INFINITY;
-          if (MODE != MODE_SELECTED && need_mask) {
-            const int64_t key = c0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key > wtok0 + r32) val = -INFINITY;
-          }
-          x[kt][e] = val;
-          mloc = fmaxf(mloc, val);
+          p0[e] = fast_exp2(fmaf(s0[e], a.scale_log2, -m_use));
+          p1[e] = fast_exp2(fmaf(s1[e], a.scale_log2, -m_use));
+          psum += p0[e] + p1[e];
         }
-      }
-      mloc = fmaxf(mloc, swap_half(mloc));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          x[kt][e] = fast_exp2(x[kt][e] - m_use);
-          psum += x[kt][e];
+        // Rescale only when some row's running max moved; otherwise alpha is
+        // exactly 1 for every lane and the multiply would change nothing.
+        if (__ballot(m_new != m_run)) {
+          const float alpha = fast_exp2(m_run - m_use);
+          l_run *= alpha;
+  #pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
         }
-      // Rescale only when some row's running max moved; otherwise alpha is
-      // exactly 1 for every lane and the multiply would change nothing.
-      if (__ballot(m_new != m_run)) {
-        const float alpha = fast_exp2(m_run - m_use);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-      }
-      l_run += psum;
-      m_run = m_new;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (!act[kt]) continue;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const frag_t pf = pack8<T>(&x[kt][8 * mm]);
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            frag_t vf = load8(vl + (32 * dt + r32) * Stage::VLD + 32 * kt + 16 * mm + 8 * half);
-            o[dt] = mma_k16(vf, pf, o[dt]);
+        l_run += psum;
+        m_run = m_new;
+        // O^T += V^T P^T; P^T comes straight from the score registers
+        frag_t pf[4];
+        pf[0] = pack8<T>(&p0[0]);
+        pf[1] = pack8<T>(&p0[8]);
+        pf[2] = pack8<T>(&p1[0]);
+        pf[3] = pack8<T>(&p1[8]);
+        {
+          const T* v0 = vl + r32 * Stage::VLD + 8 * half;
+          constexpr int NF = (D / 32) * 4;   // V^T fragments per chunk, step f = 4 * dt + qq
+          frag_t ring[4];
+  #pragma unroll
+          for (int f = 0; f < 4; ++f) ring[f] = load8(v0 + (f >> 2) * 32 * Stage::VLD + 16 * (f & 3));
+  #pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            o[f >> 2] = mma_k16(ring[f & 3], pf[f & 3], o[f >> 2]);
+            if (f + 4 < NF) ring[f & 3] = load8(v0 + ((f + 4) >> 2) * 32 * Stage::VLD + 16 * (f & 3));
           }
         }
       }
-    }
-    if (c + 1 < nch) st.store(ks_base + (buf ^ 1) * KBUF, vt_base + (buf ^ 1) * VBUF);
+  };
+
+  // Two register sets hold chunks in flight: the loads of chunk c+2 are issued
+  // before chunk c is multiplied and land in LDS only after chunk c+1 has been
+  // multiplied, so each load has two compute phases to arrive. Two LDS buffers.
+  const int nch = (int)((kend - kbeg + KC - 1) / KC);
+  Stage st0, st1;
+  st0.load(k, v, kbeg, kend, a.hkv, g);
+  if (nch > 1) st1.load(k, v, kbeg + KC, kend, a.hkv, g);
+  st0.store(ks_base, vt_base);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    const int64_t c0 = kbeg + (int64_t)c * KC;
+    if (c + 2 < nch) st0.load(k, v, c0 + 2 * KC, kend, a.hkv, g);
+    compute(0, c0);
+    if (c + 1 < nch) st1.store(ks_base + KBUF, vt_base + VBUF);
+    __syncthreads();
+    if (c + 1 >= nch) break;
+    if (c + 3 < nch) st1.load(k, v, c0 + 3 * KC, kend, a.hkv, g);
+    compute(1, c0 + KC);
+    if (c + 2 < nch) st0.store(ks_base, vt_base);
     __syncthreads();
   }
 

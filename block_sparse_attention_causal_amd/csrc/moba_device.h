@@ -52,6 +52,20 @@ __device__ __forceinline__ f32x8 load8(const float* p) {
   return r;
 }
 
+// Streaming (non-temporal) variants for data read once, so that it does not
+// push reusable K/V lines out of L2.
+__device__ __forceinline__ bf16x8 load8_stream(const bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+}
+__device__ __forceinline__ f32x8 load8_stream(const float* p) {
+  f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 template <typename T> __device__ __forceinline__ T zero8();
 template <> __device__ __forceinline__ bf16x8 zero8<bf16x8>() {
   bf16x8 z;
@@ -85,6 +99,10 @@ __device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, k
 __device__ __forceinline__ int swap_half(int x) { return __shfl_xor(x, 32, kWave); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// IEEE 754-2019 maximum (NaN-propagating); gfx950 has a 3-input form, and unlike
+// fmaxf it needs no canonicalising of its operands.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (id % 8). Remap the
