@@ -69,7 +69,7 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
   P.d = shape->head_dim;
   P.dtype = shape->dtype;
   P.group = P.hq / P.hkv;
-  P.hg = gcd_int(P.group, 8);
+  P.hg = gcd_int(P.group, kGateWaves);
   P.block = need_block ? block : 0;
   P.topk = need_block ? topk : 1;
   P.ks = P.topk - 1;

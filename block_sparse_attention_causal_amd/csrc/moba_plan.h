@@ -11,8 +11,13 @@
 namespace moba {
 
 constexpr int kRowsPerWave = 32;           // one 32-row MFMA tile per wave
-constexpr int kWavesPerWG = 8;             // attention / gate workgroups: 512 threads
-constexpr int kRowsPerTile = kRowsPerWave * kWavesPerWG;   // routed rows per attention tile
+constexpr int kGateWaves = 8;              // gate workgroups: 512 threads
+// Attention workgroups: 8 waves (512 threads), one per CU; all eight share each
+// staged K/V chunk. (Two 4-wave workgroups per CU measured slower: each stages
+// its own copy of every chunk and only one chunk fits in flight.)
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kRowsPerTile = kRowsPerWave * kAttnWaves;   // routed rows per attention tile
 constexpr int kMaxSelected = 16;           // topk - 1 limit (per-lane register lists)
 constexpr int kMaxBlocksPerSeq = 16384;    // per-sequence block counters live in LDS
 
@@ -22,7 +27,7 @@ struct Plan {
   int64_t T = 0;
   int32_t hq = 0, hkv = 0, d = 0, dtype = 0;
   int32_t group = 1;        // Hq / Hkv
-  int32_t hg = 1;           // heads of one group that share a workgroup: gcd(group, 8)
+  int32_t hg = 1;           // heads of one group that share a gate workgroup: gcd(group, 8)
   int32_t block = 0, topk = 1, ks = 0;   // ks = topk - 1
   float scale = 0.f;
   // derived sizes
