@@ -19,7 +19,8 @@ __global__ void __launch_bounds__(256) k_merge(const int32_t* __restrict__ cu, i
                                                const typename PartType<T>::type* __restrict__ o_sel,
                                                const float* __restrict__ lse_sel,
                                                T* __restrict__ out, float* __restrict__ lse_out) {
-  constexpr int TPR = D / 4;            // threads per row, 4 floats each
+  typedef typename PartType<T>::type P;
+  constexpr int TPR = D / 8;            // threads per row, 8 values each
   constexpr int RPW = 256 / TPR;        // rows per workgroup
   const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
   if (row >= rows) return;
@@ -28,30 +29,39 @@ __global__ void __launch_bounds__(256) k_merge(const int32_t* __restrict__ cu, i
   const int n = seq_of_token(cu, nseq, tok);
   const int i = (int)((tok - cu[n]) / block);
   const int nsel = min(ks, i);
-  float m = lse_self[row];
+  const float ls = lse_self[row];
+  float m = ls;
   for (int sl = 0; sl < nsel; ++sl) m = fmaxf(m, lse_sel[row * ks + sl]);
-  typedef typename PartType<T>::type P;
-  typedef P pvec4_t __attribute__((ext_vector_type(4)));
-  float wgt = fast_exp2((lse_self[row] - m) * kLog2e);
+  float wgt = fast_exp2((ls - m) * kLog2e);
   float den = wgt;
-  pvec4_t x = *reinterpret_cast<const pvec4_t*>(o_self + row * D + 4 * c);
-  f32x4 acc;
+  float acc[8];
+  {
+    const P* src = o_self + row * D + 8 * c;
+    float x[8];
+    load8_part(src, x);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = to_f32(x[b]) * wgt;
+    for (int b = 0; b < 8; ++b) acc[b] = x[b] * wgt;
+  }
   for (int sl = 0; sl < nsel; ++sl) {
     const int64_t e = row * ks + sl;
     wgt = fast_exp2((lse_sel[e] - m) * kLog2e);
     den += wgt;
-    x = *reinterpret_cast<const pvec4_t*>(o_sel + e * D + 4 * c);
+    float x[8];
+    load8_part(o_sel + e * D + 8 * c, x);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] += to_f32(x[b]) * wgt;
+    for (int b = 0; b < 8; ++b) acc[b] += x[b] * wgt;
   }
   const float inv = 1.f / den;
   typedef T vec4_t __attribute__((ext_vector_type(4)));
-  vec4_t r;
+  vec4_t r0, r1;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) r[b] = from_f32<T>(acc[b] * inv);
-  *reinterpret_cast<vec4_t*>(out + row * D + 4 * c) = r;
+  for (int b = 0; b < 4; ++b) {
+    r0[b] = from_f32<T>(acc[b] * inv);
+    r1[b] = from_f32<T>(acc[4 + b] * inv);
+  }
+  T* dst = out + row * D + 8 * c;
+  __builtin_nontemporal_store(r0, reinterpret_cast<vec4_t*>(dst));
+  __builtin_nontemporal_store(r1, reinterpret_cast<vec4_t*>(dst + 4));
   if (lse_out && c == 0) lse_out[row] = m + fast_log2(den) * kLn2;
 }
 
@@ -59,7 +69,7 @@ hipError_t launch_merge(const Plan& p, const int32_t* cu_dev, const Work& w, voi
                         float* lse_out, hipStream_t s) {
   const int64_t rows = p.T * p.hq;
   if (p.ks == 0 || rows == 0) return hipSuccess;
-  const int rpw = 256 / (p.d / 4);
+  const int rpw = 256 / (p.d / 8);
   dim3 grid((unsigned)((rows + rpw - 1) / rpw)), blk(256);
   if (p.dtype == MOBA_DTYPE_BF16) {
     if (p.d == 128)

@@ -66,6 +66,20 @@ __device__ __forceinline__ f32x8 load8_stream(const float* p) {
   return r;
 }
 
+// Eight consecutive partial-output values, read once (non-temporal), as fp32.
+__device__ __forceinline__ void load8_part(const f16* p, float (&x)[8]) {
+  typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+  const f16x8 v = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(p));
+#pragma unroll
+  for (int b = 0; b < 8; ++b) x[b] = (float)v[b];
+}
+__device__ __forceinline__ void load8_part(const float* p, float (&x)[8]) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+
 template <typename T> __device__ __forceinline__ T zero8();
 template <> __device__ __forceinline__ bf16x8 zero8<bf16x8>() {
   bf16x8 z;

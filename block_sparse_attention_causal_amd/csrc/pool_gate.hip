@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LD = D + PAD;
   constexpr int VEC = 16 / sizeof(T);
-  __shared__ __attribute__((aligned(16))) T kb[NP][32][LD];
+  __shared__ __attribute__((aligned(16))) T kb[2][NP][32][LD];
 
   const int64_t logical = xcd_logical(blockIdx.x, padded);
   if (logical >= ntiles) return;
@@ -266,26 +266,48 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
     const int64_t part_stride = nb * hkv * D;
     float ws = -INFINITY;
     int wj = kNoBlock;
-    for (int j0 = 0; j0 < i; j0 += 32) {
-      __syncthreads();
-      // stage 32 candidate blocks x NP parts of pooled keys
-      constexpr int PIECES = NP * 32 * (D / VEC);
-      for (int pc = threadIdx.x; pc < PIECES; pc += 512) {
-        const int part = pc / (32 * (D / VEC));
-        const int rr = (pc / (D / VEC)) % 32;
-        const int col = pc % (D / VEC);
-        typedef T vec_t __attribute__((ext_vector_type(VEC)));
-        vec_t x;
-        if (j0 + rr < i) {
-          x = *reinterpret_cast<const vec_t*>(kparts + part * part_stride +
-                                              ((gbase + j0 + rr) * hkv + g) * D + col * VEC);
-        } else {
+    // Pooled keys of 32 candidate blocks x NP parts per chunk, double-buffered
+    // in LDS; the next chunk is fetched into registers while this one is used.
+    constexpr int PIECES = NP * 32 * (D / VEC);
+    constexpr int PPT = (PIECES + 511) / 512;             // pieces per thread
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t pre[PPT];
+    auto fetch = [&](int j0) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) x[e] = (T)0.0f;
+      for (int r = 0; r < PPT; ++r) {
+        const int pc = threadIdx.x + 512 * r;
+        if (PIECES % 512 == 0 || pc < PIECES) {
+          const int part = pc / (32 * (D / VEC));
+          const int rr = (pc / (D / VEC)) % 32;
+          const int col = pc % (D / VEC);
+          if (j0 + rr < i) {
+            pre[r] = *reinterpret_cast<const vec_t*>(kparts + part * part_stride +
+                                                     ((gbase + j0 + rr) * hkv + g) * D + col * VEC);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) pre[r][e] = (T)0.0f;
+          }
         }
-        *reinterpret_cast<vec_t*>(&kb[part][rr][col * VEC]) = x;
       }
-      __syncthreads();
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int r = 0; r < PPT; ++r) {
+        const int pc = threadIdx.x + 512 * r;
+        if (PIECES % 512 == 0 || pc < PIECES) {
+          const int part = pc / (32 * (D / VEC));
+          const int rr = (pc / (D / VEC)) % 32;
+          const int col = pc % (D / VEC);
+          *reinterpret_cast<vec_t*>(&kb[buf][part][rr][col * VEC]) = pre[r];
+        }
+      }
+    };
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    int buf = 0;
+    for (int j0 = 0; j0 < i; j0 += 32) {
+      if (j0 + 32 < i) fetch(j0 + 32);
       f32x16 acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -293,22 +315,39 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
       for (int part = 0; part < NP; ++part) {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          frag_t a = load8(&kb[part][r32][16 * kk + 8 * half]);
+          frag_t a = load8(&kb[buf][part][r32][16 * kk + 8 * half]);
           acc = mma_k16(a, qf[kk], acc);
         }
       }
+      // Candidates of this lane arrive in increasing block order, and every
+      // block already in the list is lower, so a candidate enters only with a
+      // strictly larger score than the list's worst (a tie keeps the lower
+      // block). Blocks >= i (last chunk only) are not candidates.
+      if (j0 + 32 > i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = j0 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const float s = acc[e];
-        if (j < i && better(s, j, ws, wj)) {
-          list_insert<KB>(bs, bj, ks, s, j);
+        for (int e = 0; e < 16; ++e)
+          if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
+      }
+      float mx = acc[0];
 #pragma unroll
-          for (int p = 0; p < KB; ++p)
-            if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
+      for (int e = 1; e < 16; e += 2)
+        mx = (e + 1 < 16) ? vmax(vmax(mx, acc[e]), acc[e + 1]) : vmax(mx, acc[e]);
+      if (mx > ws) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (acc[e] > ws) {
+            list_insert<KB>(bs, bj, ks, acc[e], j0 + 8 * (e >> 2) + 4 * half + (e & 3));
+#pragma unroll
+            for (int p = 0; p < KB; ++p)
+              if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
+          }
         }
       }
+      if (j0 + 32 < i) stash(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
+    (void)wj;
     // merge with the partner lane's list (same row, the other 16 of each 32)
     float os[KB];
     int oj[KB];
