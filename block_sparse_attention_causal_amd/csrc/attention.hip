@@ -72,20 +72,41 @@ struct KVStage {
 
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
                                        int64_t c0, int64_t kend, int hkv, int g) {
-    if (c0 + KC <= kend) load_impl<false>(k, v, c0, kend, hkv, g);   // uniform branch
-    else load_impl<true>(k, v, c0, kend, hkv, g);
+    if (c0 + KC <= kend) load_full(k, v, c0, hkv, g);   // uniform branch
+    else load_guarded(k, v, c0, kend, hkv, g);
   }
 
-  template <bool GUARD>
-  __device__ __forceinline__ void load_impl(const T* __restrict__ k, const T* __restrict__ v,
-                                            int64_t c0, int64_t kend, int hkv, int g) {
+  // A whole chunk: one wave-uniform base pointer, 32-bit per-lane offsets.
+  __device__ __forceinline__ void load_full(const T* __restrict__ k, const T* __restrict__ v,
+                                            int64_t c0, int hkv, int g) {
+    const int tid = threadIdx.x;
+    const int row_stride = hkv * D;
+    const T* kb = k + (c0 * hkv + g) * D;
+    const T* vb = v + (c0 * hkv + g) * D;
+#pragma unroll
+    for (int r = 0; r < KPIECES; ++r) {
+      const int pc = tid + 512 * r;
+      const int key = pc / (D / VEC), col = pc % (D / VEC);
+      kr[r] = *reinterpret_cast<const vec_t*>(kb + (key * row_stride + col * VEC));
+    }
+    if (tid < VTASKS) {
+      const int kg = tid % (KC / 4), dg = tid / (KC / 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        vr[b] = *reinterpret_cast<const vec4_t*>(vb + ((4 * kg + b) * row_stride + 4 * dg));
+    }
+  }
+
+  // The last, partial chunk of a key range: keys past kend read as zero.
+  __device__ __forceinline__ void load_guarded(const T* __restrict__ k, const T* __restrict__ v,
+                                               int64_t c0, int64_t kend, int hkv, int g) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int r = 0; r < KPIECES; ++r) {
       const int pc = tid + 512 * r;
       const int key = pc / (D / VEC), col = pc % (D / VEC);
       const int64_t s = c0 + key;
-      if (!GUARD || s < kend) {
+      if (s < kend) {
         kr[r] = *reinterpret_cast<const vec_t*>(k + (s * hkv + g) * D + col * VEC);
       } else {
 #pragma unroll
@@ -97,7 +118,7 @@ struct KVStage {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int64_t s = c0 + 4 * kg + b;
-        if (!GUARD || s < kend) {
+        if (s < kend) {
           vr[b] = *reinterpret_cast<const vec4_t*>(v + (s * hkv + g) * D + 4 * dg);
         } else {
 #pragma unroll
@@ -325,8 +346,21 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   #pragma unroll
         for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
         mx = vmax(mx, swap_half(mx));
-        const float m_new = vmax(m_run, mx * a.scale_log2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        // m_run is each row's reference max (log2 domain). It is raised only
+        // when some row's max exceeds it by more than 8: until then p <= 2^8,
+        // harmless in fp32 sums and bf16 P, and O and l share the reference, so
+        // the result is the same softmax. This removes most O rescales.
+        const float m_cand = vmax(m_run, mx * a.scale_log2);
+        if (__ballot(m_cand > m_run + 8.f)) {
+          const float alpha = fast_exp2(m_run - m_cand);   // 0 while m_run = -inf
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+          m_run = m_cand;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float p0[16], p1[16];
         float psum = 0.f;
   #pragma unroll
@@ -335,18 +369,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
           p1[e] = fast_exp2(fmaf(s1[e], a.scale_log2, -m_use));
           psum += p0[e] + p1[e];
         }
-        // Rescale only when some row's running max moved; otherwise alpha is
-        // exactly 1 for every lane and the multiply would change nothing.
-        if (__ballot(m_new != m_run)) {
-          const float alpha = fast_exp2(m_run - m_use);
-          l_run *= alpha;
-  #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-  #pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-        }
         l_run += psum;
-        m_run = m_new;
         // O^T += V^T P^T; P^T comes straight from the score registers
         frag_t pf[4];
         pf[0] = pack8<T>(&p0[0]);
