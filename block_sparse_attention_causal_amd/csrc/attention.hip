@@ -70,61 +70,30 @@ struct KVStage {
   vec_t kr[KPIECES];
   vec4_t vr[4];
 
+  // One branch-free load path. Keys past the range end (only in the last,
+  // partial chunk of a causal tile) are clamped to the last valid key: those
+  // rows are finite data that the causal mask gives zero weight (every such key
+  // lies after every row of the tile). Selected-block ranges are whole blocks,
+  // a multiple of 64 keys, and never clamp. (Separate full/partial paths made
+  // the compiler wait for each prefetch right after issuing it.)
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
                                        int64_t c0, int64_t kend, int hkv, int g) {
-    if (c0 + KC <= kend) load_full(k, v, c0, hkv, g);   // uniform branch
-    else load_guarded(k, v, c0, kend, hkv, g);
-  }
-
-  // A whole chunk: one wave-uniform base pointer, 32-bit per-lane offsets.
-  __device__ __forceinline__ void load_full(const T* __restrict__ k, const T* __restrict__ v,
-                                            int64_t c0, int hkv, int g) {
     const int tid = threadIdx.x;
     const int row_stride = hkv * D;
+    const int last = (int)min((int64_t)(KC - 1), kend - 1 - c0);
     const T* kb = k + (c0 * hkv + g) * D;
     const T* vb = v + (c0 * hkv + g) * D;
 #pragma unroll
     for (int r = 0; r < KPIECES; ++r) {
       const int pc = tid + 512 * r;
-      const int key = pc / (D / VEC), col = pc % (D / VEC);
+      const int key = min(pc / (D / VEC), last), col = pc % (D / VEC);
       kr[r] = *reinterpret_cast<const vec_t*>(kb + (key * row_stride + col * VEC));
     }
     if (tid < VTASKS) {
       const int kg = tid % (KC / 4), dg = tid / (KC / 4);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        vr[b] = *reinterpret_cast<const vec4_t*>(vb + ((4 * kg + b) * row_stride + 4 * dg));
-    }
-  }
-
-  // The last, partial chunk of a key range: keys past kend read as zero.
-  __device__ __forceinline__ void load_guarded(const T* __restrict__ k, const T* __restrict__ v,
-                                               int64_t c0, int64_t kend, int hkv, int g) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int r = 0; r < KPIECES; ++r) {
-      const int pc = tid + 512 * r;
-      const int key = pc / (D / VEC), col = pc % (D / VEC);
-      const int64_t s = c0 + key;
-      if (s < kend) {
-        kr[r] = *reinterpret_cast<const vec_t*>(k + (s * hkv + g) * D + col * VEC);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) kr[r][e] = (T)0.0f;
-      }
-    }
-    if (tid < VTASKS) {
-      const int kg = tid % (KC / 4), dg = tid / (KC / 4);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t s = c0 + 4 * kg + b;
-        if (s < kend) {
-          vr[b] = *reinterpret_cast<const vec4_t*>(v + (s * hkv + g) * D + 4 * dg);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vr[b][e] = (T)0.0f;
-        }
-      }
+        vr[b] = *reinterpret_cast<const vec4_t*>(vb + (min(4 * kg + b, last) * row_stride + 4 * dg));
     }
   }
 
@@ -397,17 +366,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nch = (int)((kend - kbeg + KC - 1) / KC);
   Stage st0, st1;
   st0.load(k, v, kbeg, kend, a.hkv, g);
-  if (nch > 1) st1.load(k, v, kbeg + KC, kend, a.hkv, g);
+  st1.load(k, v, kbeg + (int64_t)min(1, nch - 1) * KC, kend, a.hkv, g);
   st0.store(ks_base, vt_base);
   __syncthreads();
   for (int c = 0; c < nch; c += 2) {
     const int64_t c0 = kbeg + (int64_t)c * KC;
-    if (c + 2 < nch) st0.load(k, v, c0 + 2 * KC, kend, a.hkv, g);
+    // Prefetches are issued unconditionally (past the end: the last chunk again,
+    // unused) so that every path has the same loads in flight and the wait
+    // before each LDS store only covers the older set.
+    st0.load(k, v, kbeg + (int64_t)min(c + 2, nch - 1) * KC, kend, a.hkv, g);
     compute(0, c0);
     if (c + 1 < nch) st1.store(ks_base + KBUF, vt_base + VBUF);
     __syncthreads();
     if (c + 1 >= nch) break;
-    if (c + 3 < nch) st1.load(k, v, c0 + 3 * KC, kend, a.hkv, g);
+    st1.load(k, v, kbeg + (int64_t)min(c + 3, nch - 1) * KC, kend, a.hkv, g);
     compute(1, c0 + KC);
     if (c + 2 < nch) st0.store(ks_base, vt_base);
     __syncthreads();

@@ -280,13 +280,11 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
           const int part = pc / (32 * (D / VEC));
           const int rr = (pc / (D / VEC)) % 32;
           const int col = pc % (D / VEC);
-          if (j0 + rr < i) {
-            pre[r] = *reinterpret_cast<const vec_t*>(kparts + part * part_stride +
-                                                     ((gbase + j0 + rr) * hkv + g) * D + col * VEC);
-          } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) pre[r][e] = (T)0.0f;
-          }
+          // blocks >= i (last chunk only) are clamped to block i-1 and their
+          // scores discarded below; one branch-free load path
+          const int jj = min(j0 + rr, i - 1);
+          pre[r] = *reinterpret_cast<const vec_t*>(kparts + part * part_stride +
+                                                   ((gbase + jj) * hkv + g) * D + col * VEC);
         }
       }
     };
