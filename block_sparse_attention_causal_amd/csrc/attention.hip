@@ -121,6 +121,66 @@ struct KVStage {
   }
 };
 
+// ---------------------------------------------------------------------------
+// 16-bit inputs: K and V chunks go straight from global memory into LDS with
+// gfx950's direct loads (global_load_lds_dwordx4: lane i's 16 bytes land at
+// base + 16 i), so no registers hold chunks in flight and three chunks can be
+// outstanding. Both are stored row-major, 256-byte rows (D = 128) of sixteen
+// 16-byte pieces; piece p of row r sits at position p ^ swz(r) so that the
+// fragment reads of 16 consecutive rows hit distinct banks. V^T fragments are
+// read with ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte reads of lanes i/4, i/4+4, i/4+8, i/4+12, so
+// pointing the group at a 4-row x 16-column block of V gives lane i column i of
+// those four rows: four consecutive keys of one head dimension.
+__device__ __forceinline__ int swz(int r) {
+  r &= 15;
+  return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (r & 8);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Eight transposed 8-byte LDS reads from two base addresses at the immediate
+// row offsets of a V^T head-dim tile (mm = 1: +16 rows, kt = 1: +32 rows of 256
+// bytes), waited for inside the same block. Written as inline assembly because
+// the builtin makes the compiler wait for every direct global->LDS load in
+// flight; here the caller's own wait + barrier order the data.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void ds_read_tr8(uint32_t a0, uint32_t a1, i32x2 (&r)[8]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %9\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:4096\n"
+      "ds_read_b64_tr_b16 %3, %9 offset:4096\n"
+      "ds_read_b64_tr_b16 %4, %8 offset:8192\n"
+      "ds_read_b64_tr_b16 %5, %9 offset:8192\n"
+      "ds_read_b64_tr_b16 %6, %8 offset:12288\n"
+      "ds_read_b64_tr_b16 %7, %9 offset:12288\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1)
+      : "memory");
+#endif
+}
+
+// A bare s_barrier (the host pass of the compiler sees only an empty body).
+__device__ __forceinline__ void bare_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
+
+// s_waitcnt with vmcnt(n) (n < 64) and lgkmcnt(0), expcnt untouched (gfx9 encoding).
+#define MOBA_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+
 template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
 template <> __device__ __forceinline__ bf16x8 pack8<bf16>(const float* x) {
   bf16x8 r;
@@ -174,12 +234,18 @@ __device__ __forceinline__ void store_rows(O* __restrict__ dst, char* smem, cons
 
 template <typename T, int D, int MODE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn(AttnArgs a) {
+  // The host pass only needs this kernel's signature (for its launch stub); the
+  // body uses device-only builtins and is compiled in the device pass alone.
+#if defined(__HIP_DEVICE_COMPILE__)
   typedef KVStage<T, D> Stage;
   typedef typename Frag<T>::type frag_t;
   // One LDS arena: two K buffers and two transposed-V buffers during the key
   // loop, then the output staging area of the epilogue.
   constexpr int KBUF = KC * Stage::KLD, VBUF = D * Stage::VLD;
-  constexpr int ARENA = (2 * KBUF + 2 * VBUF) * (int)sizeof(T);
+  constexpr int ARENA_REG = (2 * KBUF + 2 * VBUF) * (int)sizeof(T);
+  constexpr int ARENA_DMA = 4 * 2 * KC * D * (int)sizeof(T);      // four K+V buffers
+  constexpr int ARENA = ((sizeof(T) == 2 && D == 128 && kAttnWaves == 8) && ARENA_DMA > ARENA_REG)
+                            ? ARENA_DMA : ARENA_REG;
   __shared__ __attribute__((aligned(16))) char smem[ARENA];
   static_assert(8 * 32 * (D + 16 / sizeof(typename PartType<T>::type)) *
                         sizeof(typename PartType<T>::type) <= ARENA &&
@@ -270,119 +336,208 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Multiply one staged chunk (LDS buffer `buf`, keys c0 .. c0+63) into the
-  // wave's running softmax state.
-  auto compute = [&](int buf, int64_t c0) {
-      // Does this wave need the chunk at all (causal: some key <= some row), and
-      // does any key of it lie after one of the wave's rows (then mask)?
-      const bool wave_needs = (MODE == MODE_SELECTED) ? wave_live : (wave_live && c0 <= wtok0 + 31);
-      const bool need_mask = (MODE != MODE_SELECTED) && (c0 + KC - 1 > wtok0);
-      if (wave_needs) {
-          const T* kl = ks_base + buf * KBUF;
-        const T* vl = vt_base + buf * VBUF;
-        // S^T for the chunk's two 32-key tiles: two independent MFMA chains, the
-        // LDS fragments read two steps ahead of their use
-        f32x16 s0, s1;
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
-        {
-          const T* k0 = kl + r32 * Stage::KLD + 8 * half;
-          const T* k1 = k0 + 32 * Stage::KLD;
-          frag_t ring[4];
-          ring[0] = load8(k0);
-          ring[1] = load8(k1);
-          ring[2] = load8(k0 + 16);
-          ring[3] = load8(k1 + 16);
-  #pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            s0 = mma_k16(ring[(2 * kk) & 3], qf[kk], s0);
-            if (kk + 2 < D / 16) ring[(2 * kk) & 3] = load8(k0 + 16 * (kk + 2));
-            s1 = mma_k16(ring[(2 * kk + 1) & 3], qf[kk], s1);
-            if (kk + 2 < D / 16) ring[(2 * kk + 1) & 3] = load8(k1 + 16 * (kk + 2));
-          }
-        }
-        if (need_mask) {
-          const int64_t tok = wtok0 + r32;
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int64_t key = c0 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key > tok) s0[e] = -INFINITY;
-            if (key + 32 > tok) s1[e] = -INFINITY;
-          }
-        }
-        // running max on the raw scores (the scale is positive), then one fma + exp2
-        float mx = vmax(s0[0], s1[0]);
-  #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
-        mx = vmax(mx, swap_half(mx));
-        // m_run is each row's reference max (log2 domain). It is raised only
-        // when some row's max exceeds it by more than 8: until then p <= 2^8,
-        // harmless in fp32 sums and bf16 P, and O and l share the reference, so
-        // the result is the same softmax. This removes most O rescales.
-        const float m_cand = vmax(m_run, mx * a.scale_log2);
-        if (__ballot(m_cand > m_run + 8.f)) {
-          const float alpha = fast_exp2(m_run - m_cand);   // 0 while m_run = -inf
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-          m_run = m_cand;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float p0[16], p1[16];
-        float psum = 0.f;
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p0[e] = fast_exp2(fmaf(s0[e], a.scale_log2, -m_use));
-          p1[e] = fast_exp2(fmaf(s1[e], a.scale_log2, -m_use));
-          psum += p0[e] + p1[e];
-        }
-        l_run += psum;
-        // O^T += V^T P^T; P^T comes straight from the score registers
-        frag_t pf[4];
-        pf[0] = pack8<T>(&p0[0]);
-        pf[1] = pack8<T>(&p0[8]);
-        pf[2] = pack8<T>(&p1[0]);
-        pf[3] = pack8<T>(&p1[8]);
-        {
-          const T* v0 = vl + r32 * Stage::VLD + 8 * half;
-          constexpr int NF = (D / 32) * 4;   // V^T fragments per chunk, step f = 4 * dt + qq
-          frag_t ring[4];
-  #pragma unroll
-          for (int f = 0; f < 4; ++f) ring[f] = load8(v0 + (f >> 2) * 32 * Stage::VLD + 16 * (f & 3));
-  #pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            o[f >> 2] = mma_k16(ring[f & 3], pf[f & 3], o[f >> 2]);
-            if (f + 4 < NF) ring[f & 3] = load8(v0 + ((f + 4) >> 2) * 32 * Stage::VLD + 16 * (f & 3));
-          }
-        }
-      }
+  // ---- fragment fetchers for the two LDS layouts ----------------------------
+  // DMA layout (16-bit inputs): per buffer K then V, each KC rows x D elements.
+  constexpr bool kDMA = (sizeof(T) == 2) && (D == 128) && (kAttnWaves == 8);
+  constexpr int DBUF = 2 * KC * D;                 // elements per DMA buffer (K + V)
+  const int hx = half ^ swz(r32);                  // K piece xor for this lane's rows
+  const int ml = lane & 15;
+  const int vrow = 4 * half + (ml >> 2);           // V row (within 16) of this lane's tr reads
+  const int vp = 2 * ((lane >> 4) & 1) + ((ml & 3) >> 1);
+  const int vx0 = vp ^ swz(vrow), vx1 = vp ^ swz(vrow + 8);
+  const int vbyte = (ml & 1) * 4;                  // element offset inside the 16-byte piece
+  // LDS byte address of this lane's tr-read row in the V part of buffer 0
+  const uint32_t vt_lds0 = lds_addr(ks_base) + (uint32_t)(KC * D * 2) + (uint32_t)(vrow * D * 2) +
+                           (uint32_t)(vbyte * 2);
+  auto kfrag = [&](int buf, int kt, int kk) __attribute__((always_inline)) -> frag_t {
+    if constexpr (kDMA) {
+      const T* kb = ks_base + buf * DBUF + (32 * kt + r32) * D;
+      return load8(kb + 8 * ((2 * kk) ^ hx));
+    } else {
+      return load8(ks_base + buf * KBUF + (32 * kt + r32) * Stage::KLD + 16 * kk + 8 * half);
+    }
+  };
+  auto vfrag = [&](int buf, int dt, int qq) __attribute__((always_inline)) -> frag_t {
+    if constexpr (kDMA) {
+      // keys 32kt + 16mm + {4h .. 4h+3} and the same + 8; head dim 32dt + r32
+      const int kt = qq >> 1, mm = qq & 1;
+      const T* vb = ks_base + buf * DBUF + KC * D + (32 * kt + 16 * mm + vrow) * D;
+      const T* p0 = vb + 8 * ((4 * dt) ^ vx0) + vbyte;
+      const T* p1 = vb + 8 * D + 8 * ((4 * dt) ^ vx1) + vbyte;
+      const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      i16x8 r;
+      r[0] = x0[0]; r[1] = x0[1]; r[2] = x0[2]; r[3] = x0[3];
+      r[4] = x1[0]; r[5] = x1[1]; r[6] = x1[2]; r[7] = x1[3];
+      return __builtin_bit_cast(frag_t, r);
+    } else {
+      return load8(vt_base + buf * VBUF + (32 * dt + r32) * Stage::VLD + 16 * qq + 8 * half);
+    }
   };
 
-  // Two register sets hold chunks in flight: the loads of chunk c+2 are issued
-  // before chunk c is multiplied and land in LDS only after chunk c+1 has been
-  // multiplied, so each load has two compute phases to arrive. Two LDS buffers.
+  // Multiply one staged chunk (LDS buffer `buf`, keys c0 .. c0+63) into the
+  // wave's running softmax state.
+  auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
+    // Does this wave need the chunk at all (causal: some key <= some row), and
+    // does any key of it lie after one of the wave's rows (then mask)?
+    const bool wave_needs = (MODE == MODE_SELECTED) ? wave_live : (wave_live && c0 <= wtok0 + 31);
+    const bool need_mask = (MODE != MODE_SELECTED) && (c0 + KC - 1 > wtok0);
+    if (!wave_needs) return;
+    // S^T for the chunk's two 32-key tiles: two independent MFMA chains, the
+    // LDS fragments read two steps ahead of their use
+    f32x16 s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+    {
+      frag_t ring[4];
+      ring[0] = kfrag(buf, 0, 0);
+      ring[1] = kfrag(buf, 1, 0);
+      ring[2] = kfrag(buf, 0, 1);
+      ring[3] = kfrag(buf, 1, 1);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s0 = mma_k16(ring[(2 * kk) & 3], qf[kk], s0);
+        if (kk + 2 < D / 16) ring[(2 * kk) & 3] = kfrag(buf, 0, kk + 2);
+        s1 = mma_k16(ring[(2 * kk + 1) & 3], qf[kk], s1);
+        if (kk + 2 < D / 16) ring[(2 * kk + 1) & 3] = kfrag(buf, 1, kk + 2);
+      }
+    }
+    if (need_mask) {
+      const int64_t tok = wtok0 + r32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t key = c0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key > tok) s0[e] = -INFINITY;
+        if (key + 32 > tok) s1[e] = -INFINITY;
+      }
+    }
+    // running max on the raw scores (the scale is positive), then one fma + exp2
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
+    mx = vmax(mx, swap_half(mx));
+    // m_run is each row's reference max (log2 domain). It is raised only when
+    // some row's max exceeds it by more than 8: until then p <= 2^8, harmless
+    // in fp32 sums and bf16 P, and O and l share the reference, so the result
+    // is the same softmax. This removes most O rescales.
+    const float m_cand = vmax(m_run, mx * a.scale_log2);
+    if (__ballot(m_cand > m_run + 8.f)) {
+      const float alpha = fast_exp2(m_run - m_cand);   // 0 while m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      m_run = m_cand;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float p0[16], p1[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p0[e] = fast_exp2(fmaf(s0[e], a.scale_log2, -m_use));
+      p1[e] = fast_exp2(fmaf(s1[e], a.scale_log2, -m_use));
+      psum += p0[e] + p1[e];
+    }
+    l_run += psum;
+    // O^T += V^T P^T; P^T comes straight from the score registers
+    frag_t pf[4];
+    pf[0] = pack8<T>(&p0[0]);
+    pf[1] = pack8<T>(&p0[8]);
+    pf[2] = pack8<T>(&p1[0]);
+    pf[3] = pack8<T>(&p1[8]);
+    if constexpr (kDMA) {
+      // per head-dim tile: one block of eight transposed reads, then 4 MFMAs
+      const uint32_t vb = vt_lds0 + (uint32_t)buf * (DBUF * 2);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        i32x2 r[8];
+        ds_read_tr8(vb + (uint32_t)(((4 * dt) ^ vx0) * 16), vb + 2048u + (uint32_t)(((4 * dt) ^ vx1) * 16), r);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          typedef int i32x4 __attribute__((ext_vector_type(4)));
+          i32x4 f4;
+          f4[0] = r[2 * qq][0]; f4[1] = r[2 * qq][1];
+          f4[2] = r[2 * qq + 1][0]; f4[3] = r[2 * qq + 1][1];
+          o[dt] = mma_k16(__builtin_bit_cast(frag_t, f4), pf[qq], o[dt]);
+        }
+      }
+    } else {
+      constexpr int NF = (D / 32) * 4;   // V^T fragments per chunk, step f = 4 * dt + qq
+      frag_t ring[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) ring[f] = vfrag(buf, f >> 2, f & 3);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        o[f >> 2] = mma_k16(ring[f & 3], pf[f & 3], o[f >> 2]);
+        if (f + 4 < NF) ring[f & 3] = vfrag(buf, (f + 4) >> 2, f & 3);
+      }
+    }
+  };
+
   const int nch = (int)((kend - kbeg + KC - 1) / KC);
-  Stage st0, st1;
-  st0.load(k, v, kbeg, kend, a.hkv, g);
-  st1.load(k, v, kbeg + (int64_t)min(1, nch - 1) * KC, kend, a.hkv, g);
-  st0.store(ks_base, vt_base);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    const int64_t c0 = kbeg + (int64_t)c * KC;
-    // Prefetches are issued unconditionally (past the end: the last chunk again,
-    // unused) so that every path has the same loads in flight and the wait
-    // before each LDS store only covers the older set.
-    st0.load(k, v, kbeg + (int64_t)min(c + 2, nch - 1) * KC, kend, a.hkv, g);
-    compute(0, c0);
-    if (c + 1 < nch) st1.store(ks_base + KBUF, vt_base + VBUF);
+  if constexpr (kDMA) {
+    // Four LDS buffers, three chunks in flight. Every wave issues 4 direct
+    // loads per chunk (2 of K, 2 of V), always, with the chunk index clamped at
+    // the end, so "chunk c+1 has landed" is exactly vmcnt(8) at the end of
+    // iteration c. The barrier is a bare s_barrier after that explicit wait
+    // (the compiler would otherwise wait for every load in flight).
+    const int row_stride = a.hkv * D;
+    const int rowA = 8 * w + (lane >> 4), rowB = rowA + 4;
+    const int pieceA = (lane & 15) ^ swz(rowA), pieceB = (lane & 15) ^ swz(rowB);
+    auto issue = [&](int c) __attribute__((always_inline)) {
+      const int cc = min(c, nch - 1);
+      const int64_t c0 = kbeg + (int64_t)cc * KC;
+      const int last = (int)min((int64_t)(KC - 1), kend - 1 - c0);
+      const T* kb = k + (c0 * a.hkv + g) * D;
+      const T* vb = v + (c0 * a.hkv + g) * D;
+      T* dst = ks_base + (c & 3) * DBUF + (128 * w) * 8;
+      const int offA = min(rowA, last) * row_stride + 8 * pieceA;
+      const int offB = min(rowB, last) * row_stride + 8 * pieceB;
+      __builtin_amdgcn_global_load_lds(kb + offA, (lds_void*)(dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kb + offB, (lds_void*)(dst + 64 * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + offA, (lds_void*)(dst + KC * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + offB, (lds_void*)(dst + KC * D + 64 * 8), 16, 0, 0);
+    };
+    issue(0);
+    issue(1);
+    issue(2);
+    MOBA_WAIT_VM_LGKM0(8);
+    bare_barrier();
+    for (int c = 0; c < nch; ++c) {
+      issue(c + 3);
+      compute(c & 3, kbeg + (int64_t)c * KC);
+      MOBA_WAIT_VM_LGKM0(8);
+      bare_barrier();
+    }
+    // the clamped tail loads must land before the epilogue reuses the arena
+    MOBA_WAIT_VM_LGKM0(0);
+    bare_barrier();
+  } else {
+    // Two register sets hold chunks in flight: the loads of chunk c+2 are
+    // issued before chunk c is multiplied and land in LDS only after chunk c+1
+    // has been multiplied, so each load has two compute phases to arrive.
+    Stage st0, st1;
+    st0.load(k, v, kbeg, kend, a.hkv, g);
+    st1.load(k, v, kbeg + (int64_t)min(1, nch - 1) * KC, kend, a.hkv, g);
+    st0.store(ks_base, vt_base);
     __syncthreads();
-    if (c + 1 >= nch) break;
-    st1.load(k, v, kbeg + (int64_t)min(c + 3, nch - 1) * KC, kend, a.hkv, g);
-    compute(1, c0 + KC);
-    if (c + 2 < nch) st0.store(ks_base, vt_base);
-    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+      const int64_t c0 = kbeg + (int64_t)c * KC;
+      // Prefetches are issued unconditionally (past the end: the last chunk
+      // again, unused) so that every path has the same loads in flight and the
+      // wait before each LDS store only covers the older set.
+      st0.load(k, v, kbeg + (int64_t)min(c + 2, nch - 1) * KC, kend, a.hkv, g);
+      compute(0, c0);
+      if (c + 1 < nch) st1.store(ks_base + KBUF, vt_base + VBUF);
+      __syncthreads();
+      if (c + 1 >= nch) break;
+      st1.load(k, v, kbeg + (int64_t)min(c + 3, nch - 1) * KC, kend, a.hkv, g);
+      compute(1, c0 + KC);
+      if (c + 2 < nch) st0.store(ks_base, vt_base);
+      __syncthreads();
+    }
   }
 
   // epilogue: combine the two half-row sums, normalise, write
@@ -402,6 +557,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   else
     store_rows<typename PartType<T>::type, D>((typename PartType<T>::type*)a.o_part, smem, o,
                                               inv, dst_index, w, lane);
+#endif
 }
 
 template <int MODE>
