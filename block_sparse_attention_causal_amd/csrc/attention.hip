@@ -139,35 +139,23 @@ __device__ __forceinline__ int swz(int r) {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Eight transposed 8-byte LDS reads from two base addresses at the immediate
-// row offsets of a V^T head-dim tile (mm = 1: +16 rows, kt = 1: +32 rows of 256
-// bytes), waited for inside the same block. Written as inline assembly because
-// the builtin makes the compiler wait for every direct global->LDS load in
-// flight; here the caller's own wait + barrier order the data.
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void ds_read_tr8(uint32_t a0, uint32_t a1, i32x2 (&r)[8]) {
+// One direct global->LDS load of 16 bytes per lane (lane i's bytes land at
+// lds + 16 i). Issued from inline assembly so that the compiler, unaware of
+// these LDS writes, does not pad every later LDS read with conservative waits;
+// the caller orders them with an explicit vmcnt wait and a barrier. No register
+// receives data, so nothing is left in flight in a register.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n"
-      "ds_read_b64_tr_b16 %1, %9\n"
-      "ds_read_b64_tr_b16 %2, %8 offset:4096\n"
-      "ds_read_b64_tr_b16 %3, %9 offset:4096\n"
-      "ds_read_b64_tr_b16 %4, %8 offset:8192\n"
-      "ds_read_b64_tr_b16 %5, %9 offset:8192\n"
-      "ds_read_b64_tr_b16 %6, %8 offset:12288\n"
-      "ds_read_b64_tr_b16 %7, %9 offset:12288\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a0), "v"(a1)
-      : "memory");
+  asm volatile("global_load_lds_dwordx4 %1, off"
+               :
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
+               : "memory");
 #endif
 }
 
@@ -346,9 +334,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int vp = 2 * ((lane >> 4) & 1) + ((ml & 3) >> 1);
   const int vx0 = vp ^ swz(vrow), vx1 = vp ^ swz(vrow + 8);
   const int vbyte = (ml & 1) * 4;                  // element offset inside the 16-byte piece
-  // LDS byte address of this lane's tr-read row in the V part of buffer 0
-  const uint32_t vt_lds0 = lds_addr(ks_base) + (uint32_t)(KC * D * 2) + (uint32_t)(vrow * D * 2) +
-                           (uint32_t)(vbyte * 2);
   auto kfrag = [&](int buf, int kt, int kk) __attribute__((always_inline)) -> frag_t {
     if constexpr (kDMA) {
       const T* kb = ks_base + buf * DBUF + (32 * kt + r32) * D;
@@ -447,23 +432,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     pf[1] = pack8<T>(&p0[8]);
     pf[2] = pack8<T>(&p1[0]);
     pf[3] = pack8<T>(&p1[8]);
-    if constexpr (kDMA) {
-      // per head-dim tile: one block of eight transposed reads, then 4 MFMAs
-      const uint32_t vb = vt_lds0 + (uint32_t)buf * (DBUF * 2);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        i32x2 r[8];
-        ds_read_tr8(vb + (uint32_t)(((4 * dt) ^ vx0) * 16), vb + 2048u + (uint32_t)(((4 * dt) ^ vx1) * 16), r);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          typedef int i32x4 __attribute__((ext_vector_type(4)));
-          i32x4 f4;
-          f4[0] = r[2 * qq][0]; f4[1] = r[2 * qq][1];
-          f4[2] = r[2 * qq + 1][0]; f4[3] = r[2 * qq + 1][1];
-          o[dt] = mma_k16(__builtin_bit_cast(frag_t, f4), pf[qq], o[dt]);
-        }
-      }
-    } else {
+    {
       constexpr int NF = (D / 32) * 4;   // V^T fragments per chunk, step f = 4 * dt + qq
       frag_t ring[4];
 #pragma unroll
@@ -484,6 +453,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // iteration c. The barrier is a bare s_barrier after that explicit wait
     // (the compiler would otherwise wait for every load in flight).
     const int row_stride = a.hkv * D;
+    const uint32_t smem_lds = lds_addr(ks_base);
     const int rowA = 8 * w + (lane >> 4), rowB = rowA + 4;
     const int pieceA = (lane & 15) ^ swz(rowA), pieceB = (lane & 15) ^ swz(rowB);
     auto issue = [&](int c) __attribute__((always_inline)) {
@@ -492,14 +462,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int last = (int)min((int64_t)(KC - 1), kend - 1 - c0);
       const T* kb = k + (c0 * a.hkv + g) * D;
       const T* vb = v + (c0 * a.hkv + g) * D;
-      T* dst = ks_base + (c & 3) * DBUF + (128 * w) * 8;
+      const uint32_t dst = smem_lds + (uint32_t)((c & 3) * DBUF * 2 + 128 * w * 16);
       const int offA = min(rowA, last) * row_stride + 8 * pieceA;
       const int offB = min(rowB, last) * row_stride + 8 * pieceB;
-      __builtin_amdgcn_global_load_lds(kb + offA, (lds_void*)(dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(kb + offB, (lds_void*)(dst + 64 * 8), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + offA, (lds_void*)(dst + KC * D), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + offB, (lds_void*)(dst + KC * D + 64 * 8), 16, 0, 0);
+      dma16(kb + offA, dst);
+      dma16(kb + offB, dst + 1024u);
+      dma16(vb + offA, dst + (uint32_t)(KC * D * 2));
+      dma16(vb + offB, dst + (uint32_t)(KC * D * 2) + 1024u);
     };
+    // The direct loads are invisible to the compiler's wait bookkeeping, so
+    // the Q fragments are waited for here, explicitly, before any is issued.
+    MOBA_WAIT_VM_LGKM0(0);
     issue(0);
     issue(1);
     issue(2);
