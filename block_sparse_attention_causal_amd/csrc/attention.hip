@@ -126,15 +126,19 @@ struct KVStage {
 // gfx950's direct loads (global_load_lds_dwordx4: lane i's 16 bytes land at
 // base + 16 i), so no registers hold chunks in flight and three chunks can be
 // outstanding. Both are stored row-major, 256-byte rows (D = 128) of sixteen
-// 16-byte pieces; piece p of row r sits at position p ^ swz(r) so that the
-// fragment reads of 16 consecutive rows hit distinct banks. V^T fragments are
+// 16-byte pieces; piece p of row r sits at position p ^ swz(r). gfx950's LDS
+// has 64 four-byte banks (one 256-byte row) and serves 16 lanes of a 16-byte
+// read, or 32 lanes of an 8-byte read, per clock. The K reads put 16
+// consecutive rows in one clock (swz must be a bijection on 0..15); the V^T
+// reads put four pieces of each of 4 consecutive rows in one clock (the four
+// rows must land in different piece quads). Transposing the row index's two
+// 2-bit halves satisfies both. V^T fragments are
 // read with ds_read_b64_tr_b16: within each 16-lane group, lane i receives
 // element i % 4 of the 8-byte reads of lanes i/4, i/4+4, i/4+8, i/4+12, so
 // pointing the group at a 4-row x 16-column block of V gives lane i column i of
 // those four rows: four consecutive keys of one head dimension.
 __device__ __forceinline__ int swz(int r) {
-  r &= 15;
-  return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (r & 8);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
