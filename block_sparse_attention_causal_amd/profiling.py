@@ -7,6 +7,8 @@
         HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE, then
         WRITE_SIZE), scaled by what the same counters read for a plain copy kernel
         (torch.neg over N MiB of fp32: N MiB read, N MiB written).
+    python -m block_sparse_attention_causal_amd.profiling counters DIR
+        per-kernel mean of every counter of one --pmc run (one row per kernel)
 """
 from __future__ import annotations
 
@@ -127,6 +129,32 @@ def traffic(fetch_dir: str, write_dir: str, copy_mib: int, kernel: str) -> str:
     return "\n".join(lines)
 
 
+def counters(dirpath: str) -> str:
+    files = _find(dirpath, "counter_collection.csv")
+    if not files:
+        raise FileNotFoundError("no *counter_collection.csv under " + dirpath)
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))  # key -> ctr -> disp
+    for f in files:
+        with open(f) as fh:
+            r = csv.reader(fh)
+            hdr = next(r)
+            i_n = _col(hdr, "Kernel_Name", "Kernel-Name", "KernelName")
+            i_d = _col(hdr, "Dispatch_Id", "Dispatch-Id", "DispatchId", "Correlation_Id")
+            i_cn = _col(hdr, "Counter_Name", "Counter-Name")
+            i_cv = _col(hdr, "Counter_Value", "Counter-Value")
+            for row in r:
+                per[kernel_key(row[i_n])][row[i_cn]][row[i_d]] += float(row[i_cv])
+    names = sorted({c for k in per.values() for c in k})
+    out = ["| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+    for key in sorted(per):
+        vals = []
+        for c in names:
+            d = per[key].get(c, {})
+            vals.append("%.4g" % (sum(d.values()) / len(d)) if d else "")
+        out.append("| %s | %s |" % (key, " | ".join(vals)))
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -137,9 +165,13 @@ def main(argv=None):
     t.add_argument("write_dir")
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--kernel", default="attn_selected")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.dir))
+    elif a.cmd == "counters":
+        print(counters(a.dir))
     else:
         print(traffic(a.fetch_dir, a.write_dir, a.copy_mib, a.kernel))
 
