@@ -4,7 +4,8 @@
     python bench.py [--steps K] [--warmup W] [--config 1m]
 
 One step = one moba_forward call over the whole batch (pool, gate, route,
-selected-block attention, self-block attention, merge), inputs resident in HBM.
+selected-block attention, self-block attention with the merge of the parts in
+its epilogue), inputs resident in HBM.
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed live
 with HIP events on the launch stream), the dense causal comparison from the same
 library, and the CPU oracle timed on a bounded sample of the same workload.
@@ -37,7 +38,7 @@ def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
     rows_sel_pairs = 0      # sum over rows of min(ks, i) * B   (selected keys)
     self_pairs = 0          # sum over rows of own-block keys (causal)
     gate_pairs = 0          # sum over rows of past blocks i
-    merge_parts = 0         # sum over rows of (1 + min(ks, i))
+    sel_parts = 0           # sum over rows of min(ks, i)
     nb_total = 0
     T = sum(seqlens)
     for s in seqlens:
@@ -48,17 +49,18 @@ def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
             rows_sel_pairs += L * min(ks, i) * block
             self_pairs += L * (L + 1) // 2
             gate_pairs += L * i
-            merge_parts += L * (1 + min(ks, i))
+            sel_parts += L * min(ks, i)
     return {
         "attn_selected_flop": 4.0 * d * hq * rows_sel_pairs,
         "attn_self_flop": 4.0 * d * hq * self_pairs,
         "gate_flop": 2.0 * d * hq * gate_pairs,
         "dense_flop": 4.0 * d * hq * sum(s * (s + 1) // 2 for s in seqlens),
         # bytes: pool reads K and writes fp32 pooled keys; gate reads Q and writes
-        # the selection; merge reads every part (D values + lse) and writes out
+        # the selection; the merge (self-block epilogue) reads the selected parts
+        # (D values + lse) and writes out
         "pool_bytes": elem_bytes * T * hkv * d + 4.0 * nb_total * hkv * d,
         "gate_bytes": elem_bytes * T * hq * d + 4.0 * T * hq * ks,
-        "merge_bytes": hq * merge_parts * (part_bytes * d + 4.0) + elem_bytes * T * hq * d,
+        "merge_bytes": hq * sel_parts * (part_bytes * d + 4.0) + elem_bytes * T * hq * d,
     }
 
 
@@ -202,12 +204,15 @@ def main():
         if name in ("attn_selected", "attn_self"):
             tf = work[name + "_flop"] / (avg * 1e-3) / 1e12
             rep.update(bound="mfma", achieved_tflops=tf, frac=tf / peak_mfma)
+            if name == "attn_self":
+                # its epilogue also streams the merge's bytes
+                rep["merge_gbs"] = work["merge_bytes"] / (avg * 1e-3) / 1e9
         elif name == "gate":
             gbs = work["gate_bytes"] / (avg * 1e-3) / 1e9
             tf = work["gate_flop"] / (avg * 1e-3) / 1e12
             rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
                        achieved_tflops=tf)
-        elif name in ("pool", "merge"):
+        elif name == "pool":
             gbs = work[name + "_bytes"] / (avg * 1e-3) / 1e9
             rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)
         stage_rep[name] = rep

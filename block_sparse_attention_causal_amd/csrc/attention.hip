@@ -1,9 +1,12 @@
-// a4a / a4b / a6: flash attention on the matrix cores.
+// a4a / a4b / a5 / a6: flash attention on the matrix cores, with the merge of
+// the parts in the self-block kernel's epilogue.
 //
 // Kimi发布MoBA突破性实现无限上下文, "PyTorch实现关键要点": flash attention runs
 // separately over each query's own block (causal) and over the blocks the gate
 // selected, and the parts are then combined with an online-softmax merge.
 // MoBA README FAQ (issue #27): the own block is attended with a causal mask.
+// The selected-block kernel runs first and leaves its parts in the workspace;
+// the self-block kernel merges them into its own result as it writes the rows.
 //
 // One kernel template serves three tile kinds:
 //   SELF     tile = up to 256 rows of one block: 32 consecutive tokens per wave,
@@ -43,8 +46,10 @@ struct AttnArgs {
   const int32_t* entries;
   void* o_part;       // SELF with ks > 0: [T*hq, D]; SELECTED: [T*hq*ks, D] (PartType<T>)
   float* lse_part;
-  void* out;          // DENSE, or SELF with ks == 0: final output [T*hq, D]
+  void* out;          // DENSE and SELF: final output [T*hq, D]
   float* lse_out;     // optional with `out`
+  const void* sel_o;        // SELF with ks > 0: selected-block partials to merge
+  const float* sel_lse;     //   [T*hq*ks, D] (PartType<T>) and their lse
   int64_t nb, nlists, ntiles, padded;
   int nseq, hq, hkv, hg, block, ks, nu;
   float scale_log2;
@@ -224,6 +229,128 @@ __device__ __forceinline__ void store_rows(O* __restrict__ dst, char* smem, cons
   }
 }
 
+// Self-block epilogue with the merge of the parts (a5) folded in: the selected
+// blocks' parts were written by the selected-block kernel, which runs first.
+// Kimi发布MoBA突破性实现无限上下文, "PyTorch实现关键要点": the parts of a row are
+// combined with an online softmax. Each part p is a normalised output o_p with
+// the log-sum-exp lse_p of its disjoint key set, so over their union
+//   out = sum_p exp(lse_p - m) o_p / sum_p exp(lse_p - m),  m = max_p lse_p,
+//   lse = m + log(sum_p exp(lse_p - m)).
+// The own part is rounded to the partials' type first (as a stored partial
+// would be); a row of query block i has min(ks, i) selected parts. The rows are
+// staged through LDS so each lane combines and stores 16 contiguous bytes.
+template <typename T, int D>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, char* smem,
+                                           const f32x16 (&o)[D / 32], float inv, float lse_own,
+                                           int64_t dst_index, int nsel, int w, int lane) {
+  typedef typename PartType<T>::type P;
+  constexpr int V = 16 / (int)sizeof(P);          // elements per 16-byte piece
+  constexpr int SLD = D + V;                       // padded staging row
+  constexpr int PPR = D / V;                       // pieces per row
+  constexpr int RPI = 64 / PPR;                    // rows per wave-wide pass
+  typedef P pvec4_t __attribute__((ext_vector_type(4)));
+  typedef P pvec_t __attribute__((ext_vector_type(V)));
+  typedef T tvec_t __attribute__((ext_vector_type(V)));
+  P* stage = reinterpret_cast<P*>(smem) + w * 32 * SLD;
+  const int half = lane >> 5, r32 = lane & 31;
+  const P* __restrict__ o_sel = (const P*)a.sel_o;
+  __syncthreads();                                 // every wave is done with K/V
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      pvec4_t val;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) val[b] = from_f32<P>(o[dt][4 * aa + b] * inv);
+      *reinterpret_cast<pvec4_t*>(stage + r32 * SLD + 32 * dt + 8 * aa + 4 * half) = val;
+    }
+  __syncthreads();
+  // Each lane handles one 16-byte piece of rows rr = it * RPI + lane / PPR.
+  // Up to two selected parts (top-3 and below) every load of all of the lane's
+  // rows is issued before any is used, so the epilogue pays one memory latency
+  // instead of one per row and part.
+  constexpr int NIT = 32 / RPI;
+  const int pc = lane % PPR;
+  int64_t di[NIT];
+  float ls[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    di[it] = __shfl(dst_index, it * RPI + lane / PPR, 64);
+    ls[it] = __shfl(lse_own, it * RPI + lane / PPR, 64);
+  }
+  auto finish = [&](int it, float m, float den, const float (&acc)[V])
+      __attribute__((always_inline)) {
+    const float rinv = 1.f / den;
+    tvec_t r;
+#pragma unroll
+    for (int b = 0; b < V; ++b) r[b] = from_f32<T>(acc[b] * rinv);
+    __builtin_nontemporal_store(r, reinterpret_cast<tvec_t*>((T*)a.out + di[it] * D + pc * V));
+    if (a.lse_out && pc == 0) a.lse_out[di[it]] = m + fast_log2(den) * kLn2;
+  };
+  auto own_part = [&](int it, float wgt, float (&acc)[V]) __attribute__((always_inline)) {
+    const int rr = it * RPI + lane / PPR;
+    const pvec_t x = *reinterpret_cast<const pvec_t*>(stage + rr * SLD + pc * V);
+#pragma unroll
+    for (int b = 0; b < V; ++b) acc[b] = to_f32(x[b]) * wgt;
+  };
+  if (a.ks <= 2) {
+    float lsel[NIT][2];
+    pvec_t px[NIT][2];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        lsel[it][sl] = -INFINITY;
+        px[it][sl] = pvec_t{};
+        if (di[it] >= 0 && sl < nsel) {
+          const int64_t e = di[it] * a.ks + sl;
+          lsel[it][sl] = a.sel_lse[e];
+          px[it][sl] = __builtin_nontemporal_load(
+              reinterpret_cast<const pvec_t*>(o_sel + e * D + pc * V));
+        }
+      }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (di[it] < 0) continue;
+      const float m = fmaxf(fmaxf(ls[it], lsel[it][0]), lsel[it][1]);
+      float wgt = fast_exp2((ls[it] - m) * kLog2e);
+      float den = wgt;
+      float acc[V];
+      own_part(it, wgt, acc);
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        if (sl >= nsel) break;
+        wgt = fast_exp2((lsel[it][sl] - m) * kLog2e);
+        den += wgt;
+#pragma unroll
+        for (int b = 0; b < V; ++b) acc[b] += to_f32(px[it][sl][b]) * wgt;
+      }
+      finish(it, m, den, acc);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (di[it] < 0) continue;
+      float m = ls[it];
+      for (int sl = 0; sl < nsel; ++sl) m = fmaxf(m, a.sel_lse[di[it] * a.ks + sl]);
+      float wgt = fast_exp2((ls[it] - m) * kLog2e);
+      float den = wgt;
+      float acc[V];
+      own_part(it, wgt, acc);
+      for (int sl = 0; sl < nsel; ++sl) {
+        const int64_t e = di[it] * a.ks + sl;
+        wgt = fast_exp2((a.sel_lse[e] - m) * kLog2e);
+        den += wgt;
+        const pvec_t x = __builtin_nontemporal_load(
+            reinterpret_cast<const pvec_t*>(o_sel + e * D + pc * V));
+#pragma unroll
+        for (int b = 0; b < V; ++b) acc[b] += to_f32(x[b]) * wgt;
+      }
+      finish(it, m, den, acc);
+    }
+  }
+}
+
 template <typename T, int D, int MODE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn(AttnArgs a) {
   // The host pass only needs this kernel's signature (for its launch stub); the
@@ -261,6 +388,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   int64_t dst_index = -1;     // where this lane's result goes (row or entry)
   int64_t wtok0 = 0;          // first token of the wave (causal modes)
   bool wave_live;             // the wave has at least one row
+  int blk_i = 0;              // SELF: the tile's block index inside its sequence
 
   if (MODE == MODE_SELECTED) {
     const int64_t tile = logical;
@@ -292,6 +420,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       hs = (int)(rest % nhs);
       const int64_t b = a.nb - 1 - rest / nhs;
       const int n = a.blk_seq[b], i = a.blk_local[b];
+      blk_i = i;
       blk_start = (int64_t)a.cu[n] + (int64_t)i * a.block;
       blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
     } else {
@@ -520,20 +649,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // epilogue: combine the two half-row sums, normalise, write
   const float l_tot = l_run + swap_half(l_run);
   const float inv = (row >= 0) ? 1.f / l_tot : 0.f;
-  const bool final_out = (MODE == MODE_DENSE) || (MODE == MODE_SELF && a.ks == 0);
-  if (row >= 0 && half == 0) {
-    const float lse = (m_run + fast_log2(l_tot)) * kLn2;
-    if (final_out) {
-      if (a.lse_out) a.lse_out[dst_index] = lse;
-    } else {
-      a.lse_part[dst_index] = lse;
-    }
-  }
-  if (final_out)
-    store_rows<T, D>((T*)a.out, smem, o, inv, dst_index, w, lane);
-  else
+  const float lse = (m_run + fast_log2(l_tot)) * kLn2;
+  if (MODE == MODE_SELF && a.ks > 0) {
+    merge_rows<T, D>(a, smem, o, inv, lse, dst_index, min(a.ks, blk_i), w, lane);
+  } else if (MODE == MODE_SELECTED) {
+    if (row >= 0 && half == 0) a.lse_part[dst_index] = lse;
     store_rows<typename PartType<T>::type, D>((typename PartType<T>::type*)a.o_part, smem, o,
                                               inv, dst_index, w, lane);
+  } else {
+    if (row >= 0 && half == 0 && a.lse_out) a.lse_out[dst_index] = lse;
+    store_rows<T, D>((T*)a.out, smem, o, inv, dst_index, w, lane);
+  }
 #endif
 }
 
@@ -592,8 +718,8 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
   AttnArgs a = base_args(p, q, k, v, cu_dev);
   a.blk_seq = w.blk_seq;
   a.blk_local = w.blk_local;
-  a.o_part = w.o_self;
-  a.lse_part = w.lse_self;
+  a.sel_o = w.o_sel;
+  a.sel_lse = w.lse_sel;
   a.out = out;
   a.lse_out = lse_out;
   const int tt = 32 * (8 / p.hg);

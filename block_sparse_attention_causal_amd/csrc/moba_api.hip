@@ -124,8 +124,6 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
     P.off_tile_offsets = take(sizeof(int32_t) * (P.nlists + 1));
     P.off_entries = take(sizeof(int32_t) * P.nentries);
     const size_t part = (P.dtype == MOBA_DTYPE_BF16) ? sizeof(f16) : sizeof(float);
-    P.off_o_self = take(part * rows * P.d);
-    P.off_lse_self = take(sizeof(float) * rows);
     P.off_o_sel = take(part * rows * P.ks * P.d);
     P.off_lse_sel = take(sizeof(float) * rows * P.ks);
   }
@@ -150,8 +148,6 @@ Work carve(const Plan& p, void* base) {
     w.list_offsets = (int32_t*)(b + p.off_list_offsets);
     w.tile_offsets = (int32_t*)(b + p.off_tile_offsets);
     w.entries = (int32_t*)(b + p.off_entries);
-    w.o_self = (void*)(b + p.off_o_self);
-    w.lse_self = (float*)(b + p.off_lse_self);
     w.o_sel = (void*)(b + p.off_o_sel);
     w.lse_sel = (float*)(b + p.off_lse_sel);
   }
@@ -269,13 +265,6 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
     e = launch_attn_self(p, q, k, v, cu_seqlens_dev, w, out, lse_out, s);
   }
   if (e != hipSuccess) return hip_status(e, "self-block attention");
-  if (p.ks > 0) {
-    {
-      StageScope t(ST_MERGE, s);
-      e = launch_merge(p, cu_seqlens_dev, w, out, lse_out, s);
-    }
-    if (e != hipSuccess) return hip_status(e, "merge");
-  }
   g_err[0] = 0;
   return MOBA_OK;
 }

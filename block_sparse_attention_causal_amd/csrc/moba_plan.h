@@ -43,7 +43,7 @@ struct Plan {
   size_t off_kbar = 0, off_kbar_split = 0, off_sel = 0;
   size_t off_hist = 0, off_chunk_off = 0, off_list_count = 0, off_list_offsets = 0;
   size_t off_tile_offsets = 0, off_entries = 0;
-  size_t off_o_self = 0, off_lse_self = 0, off_o_sel = 0, off_lse_sel = 0;
+  size_t off_o_sel = 0, off_lse_sel = 0;
   size_t total = 0;
 };
 
@@ -68,9 +68,8 @@ struct Work {
   int32_t* list_offsets; // [nlists + 1]
   int32_t* tile_offsets; // [nlists + 1]
   int32_t* entries;      // [nentries] row * ks + slot, grouped by list
-  void* o_self;          // [T * hq, d] partial outputs (fp16 for bf16 inputs, else fp32)
-  float* lse_self;       // [T * hq]
-  void* o_sel;           // [T * hq * ks, d] partial outputs, same type
+  void* o_sel;           // [T * hq * ks, d] selected-block partial outputs (fp16 for bf16
+                         // inputs, else fp32)
   float* lse_sel;        // [T * hq * ks]
 };
 
@@ -86,13 +85,12 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
                         int32_t* list_offsets, int32_t* entries, hipStream_t s);
 hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, const void* v,
                                 const int32_t* cu_dev, const Work& w, hipStream_t s);
-// Self-block causal attention. With ks == 0 it writes the final output.
+// Self-block causal attention; writes the final output, merging the
+// selected-block parts (ks > 0) in its epilogue.
 hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const void* v,
                             const int32_t* cu_dev, const Work& w, void* out, float* lse_out,
                             hipStream_t s);
 hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const void* v,
                              const int32_t* cu_dev, void* out, float* lse_out, hipStream_t s);
-hipError_t launch_merge(const Plan& p, const int32_t* cu_dev, const Work& w, void* out,
-                        float* lse_out, hipStream_t s);
 
 }  // namespace moba

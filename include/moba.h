@@ -83,9 +83,9 @@ int32_t moba_abi_version(void);
 const char* moba_last_error(void);
 
 /* Device workspace bytes that moba_forward needs for this batch: the pooled
- * keys, the selected block ids, the routing lists and the per-part partial
- * outputs. Host-only; returns 0 and sets the last error if the arguments are
- * invalid. */
+ * keys, the selected block ids, the routing lists and the selected-block
+ * partial outputs (the self-block kernel merges them into `out`). Host-only;
+ * returns 0 and sets the last error if the arguments are invalid. */
 size_t moba_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
                             const moba_shape_t* shape, int32_t block_size, int32_t topk);
 
@@ -160,8 +160,10 @@ moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
  * records an event pair around each stage's launches on the call's stream.
  * moba_timing_read() waits for the recorded events, writes per stage the summed
  * milliseconds and the number of timed launches, then clears the record.
- * Stage ids: 0 pool, 1 gate, 2 route, 3 self-block attention, 4 selected-block
- * attention, 5 merge, 6 dense causal attention. Returns the number of stages
+ * Stage ids: 0 pool, 1 gate, 2 route, 3 self-block attention (which also
+ * merges the parts), 4 selected-block attention, 5 merge (no separate launch:
+ * always 0 launches; the id is kept so that the others stay fixed), 6 dense
+ * causal attention. Returns the number of stages
  * written. At most 4096 event pairs are kept; later ones are not recorded. */
 moba_status_t moba_timing_enable(int32_t enable);
 int32_t moba_timing_read(double* stage_ms, int32_t* stage_launches, int32_t max_stages);

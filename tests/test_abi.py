@@ -101,11 +101,11 @@ def test_empty_batch_is_a_no_op(lib):
 def test_workspace_bytes_and_route_sizes(lib):
     n = moba.moba_workspace_bytes([0, 32768], 32, 8, 128, torch.bfloat16, 2048, 3)
     T, rows = 32768, 32768 * 32
-    # the partial outputs dominate: one self part and topk-1 selected parts per row,
-    # stored as fp16 for bf16 inputs
-    assert n >= rows * 128 * 2 * 3
+    # the partial outputs dominate: topk-1 selected-block parts per row (the
+    # self-block kernel merges them into out), fp16 for bf16 inputs
+    assert n >= rows * 128 * 2 * 2
     assert moba.moba_workspace_bytes([0, 32768], 32, 8, 128, torch.float32, 2048, 3) >= \
-        rows * 128 * 4 * 3
+        rows * 128 * 4 * 2
     nl, ne = moba.moba_route_sizes([0, 32768], 32, 8, 128, torch.bfloat16, 2048, 3)
     assert nl == 16 * 8
     assert ne == sum(2048 * 32 * min(2, i) for i in range(16))
