@@ -56,6 +56,8 @@ def _load():
         "moba_workspace_bytes": ([p, i32, shp, i32, i32], sz),
         "moba_forward": ([p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p], ctypes.c_int),
         "moba_dense_causal_forward": ([p, p, p, p, p, i32, shp, p, p, p], ctypes.c_int),
+        "moba_attention_forward": ([i32, p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p],
+                                   ctypes.c_int),
         "moba_block_pool": ([p, p, p, i32, shp, i32, p, p, sz, p], ctypes.c_int),
         "moba_route_sizes": ([p, i32, shp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)],
                              ctypes.c_int),
@@ -76,7 +78,8 @@ def exported_symbols():
     """Names the binding resolves in libmoba.so (loading fails if any is missing)."""
     _load()
     return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
-            "moba_dense_causal_forward", "moba_block_pool", "moba_route_sizes", "moba_route",
+            "moba_dense_causal_forward", "moba_attention_forward", "moba_block_pool",
+            "moba_route_sizes", "moba_route",
             "moba_timing_enable", "moba_timing_read", "moba_stage_name"]
 
 
@@ -195,6 +198,40 @@ def moba_dense_causal_forward(q, k, v, cu_seqlens, *, out=None, return_lse=False
     _check(_load().moba_dense_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_dev), _ptr(host),
                                              host.numel() - 1, ctypes.byref(shape), _ptr(out),
                                              _ptr(lse), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+MOBA_MODE_SPARSE, MOBA_MODE_FULL = 0, 1
+
+
+def moba_attention(q, k, v, cu_seqlens, block_size, topk, *, full=False, out=None,
+                   workspace=None, return_lse=False, softmax_scale=0.0, cu_seqlens_dev=None):
+    """One attention layer of a hybrid stack: MoBA (full=False) or full causal
+    attention (full=True) through moba_attention_forward; returns out [T,Hq,D]
+    (and the log-sum-exp [T,Hq] with return_lse)."""
+    _check_qkv(q, k, v)
+    dev = q.device
+    T, hq, d = q.shape
+    host, cu_dev = _cu(cu_seqlens, dev)
+    if cu_seqlens_dev is not None:
+        cu_dev = cu_seqlens_dev
+    shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
+    lib = _load()
+    mode = MOBA_MODE_FULL if full else MOBA_MODE_SPARSE
+    if not full and workspace is None:
+        nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                          int(block_size), int(topk))
+        if nbytes == 0 and moba_last_error():
+            raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+        workspace = _workspace(nbytes, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(T, hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.moba_attention_forward(mode, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_dev), _ptr(host),
+                                      host.numel() - 1, ctypes.byref(shape), int(block_size),
+                                      int(topk), _ptr(out), _ptr(workspace),
+                                      workspace.numel() if workspace is not None else 0, None,
+                                      _ptr(lse), _stream(dev)))
     return (out, lse) if return_lse else out
 
 

@@ -295,6 +295,23 @@ moba_status_t moba_dense_causal_forward(const void* q, const void* k, const void
   return MOBA_OK;
 }
 
+moba_status_t moba_attention_forward(int32_t mode, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens_dev,
+                                     const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                     const moba_shape_t* shape, int32_t block_size,
+                                     int32_t topk, void* out, void* workspace,
+                                     size_t workspace_bytes, int32_t* sel_out, float* lse_out,
+                                     void* stream) {
+  if (mode == MOBA_MODE_SPARSE)
+    return moba_forward(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, shape, block_size,
+                        topk, out, workspace, workspace_bytes, sel_out, lse_out, stream);
+  if (mode == MOBA_MODE_FULL)
+    return moba_dense_causal_forward(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, shape,
+                                     out, lse_out, stream);
+  return fail(MOBA_ERR_INVALID_ARG, "mode %d is neither MOBA_MODE_SPARSE nor MOBA_MODE_FULL",
+              mode);
+}
+
 moba_status_t moba_block_pool(const void* k, const int32_t* cu_seqlens_dev,
                               const int32_t* cu_seqlens_host, int32_t num_seqs,
                               const moba_shape_t* shape, int32_t block_size, float* kbar_out,

@@ -118,6 +118,26 @@ moba_status_t moba_dense_causal_forward(const void* q, const void* k, const void
                                         const moba_shape_t* shape, void* out, float* lse_out,
                                         void* stream);
 
+/* Per-call switch between sparse (MoBA) and full causal attention, for hybrid
+ * stacks in which some layers, or some phases of training, run full attention
+ * and the rest MoBA with the same weights (README, "Seamlessly Transition
+ * between Full and Sparse Attention"; MoBA是什么, "MoBA的技术原理").
+ *   mode: MOBA_MODE_SPARSE is moba_forward with every argument as given;
+ *         MOBA_MODE_FULL is moba_dense_causal_forward: block_size, topk,
+ *         workspace, workspace_bytes and sel_out are ignored (0 / NULL allowed).
+ *   Any other mode is MOBA_ERR_INVALID_ARG. */
+typedef enum {
+  MOBA_MODE_SPARSE = 0,
+  MOBA_MODE_FULL = 1
+} moba_mode_t;
+moba_status_t moba_attention_forward(int32_t mode, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens_dev,
+                                     const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                     const moba_shape_t* shape, int32_t block_size,
+                                     int32_t topk, void* out, void* workspace,
+                                     size_t workspace_bytes, int32_t* sel_out, float* lse_out,
+                                     void* stream);
+
 /* The block mean-pool step alone (Kimi发布MoBA突破性实现无限上下文, "PyTorch实现
  * 关键要点": one mean-pooled key per block). Only k is read.
  *   kbar_out:  fp32 [NB, Hkv, D], NB = sum_n ceil(S_n / block_size), blocks

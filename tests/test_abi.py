@@ -131,3 +131,23 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(64, 2, 64)
     with pytest.raises(ValueError):
         moba.moba_forward(q, q, q, [0, 64], 64, 3)
+
+
+def _attn(lib, mode, cu, shape, block, topk, ws_bytes=1 << 40, ws=FAKE):
+    return lib.moba_attention_forward(mode, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(cu.data_ptr()),
+                                      cu.numel() - 1, ctypes.byref(shape), block, topk, FAKE, ws,
+                                      ws_bytes, None, None, None)
+
+
+def test_hybrid_switch_validates_mode_and_routes_arguments(lib):
+    cu = _cu([4096])
+    for mode in (-1, 2, 7):
+        assert _attn(lib, mode, cu, _shape(), 2048, 3) == moba.MOBA_ERR_INVALID_ARG
+        assert "mode" in lib.moba_last_error().decode()
+    # sparse mode checks MoBA's own arguments (block size, top-k, workspace) ...
+    assert _attn(lib, moba.MOBA_MODE_SPARSE, cu, _shape(), 100, 3) == moba.MOBA_ERR_UNSUPPORTED
+    assert _attn(lib, moba.MOBA_MODE_SPARSE, cu, _shape(), 2048, 3, ws_bytes=10) == \
+        moba.MOBA_ERR_WORKSPACE
+    # ... full mode ignores them but still validates the shape
+    assert _attn(lib, moba.MOBA_MODE_FULL, cu, _shape(d=96), 0, 0, ws=None) == \
+        moba.MOBA_ERR_UNSUPPORTED

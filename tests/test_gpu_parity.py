@@ -174,6 +174,35 @@ def test_block_longer_than_sequence_equals_dense():
     assert (out.float() - dense.float()).abs().max().item() <= 2e-2
 
 
+def test_hybrid_switch_runs_each_path():
+    """moba_attention_forward: sparse mode is moba_forward, full mode is the dense
+    causal kernel (bitwise), and a two-layer sparse-then-full stack matches the
+    oracle layer by layer."""
+    _say("hybrid switch, gqa varlen bf16")
+    inp = _to_gpu(make_inputs([1000, 64, 2300], 8, 2, 128, 256, 3, dtype="bf16", seed=21))
+    sparse = moba.moba_attention(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.block, inp.topk)
+    full, lse_full = moba.moba_attention(inp.q, inp.k, inp.v, inp.cu_seqlens, 0, 0, full=True,
+                                         return_lse=True)
+    ref_sparse = moba.moba_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.block, inp.topk)
+    ref_full, ref_lse = moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens,
+                                                       return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sparse, ref_sparse)
+    assert torch.equal(full, ref_full) and torch.equal(lse_full, ref_lse)
+    # layer 2 (full) takes layer 1's (sparse) output as its query, as a stack would
+    q2 = sparse.contiguous()
+    out2 = moba.moba_attention(q2, inp.k, inp.v, inp.cu_seqlens, 0, 0, full=True)
+    torch.cuda.synchronize()
+    ref1 = oracle.all_rows(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.block, inp.topk)
+    err1 = np.abs(sparse.float().cpu().numpy() - ref1["out"]).max()
+    assert err1 <= TOL[inp.q.dtype], err1
+    T, hq, d = q2.shape
+    tt, hh = np.repeat(np.arange(T), hq), np.tile(np.arange(hq), T)
+    ref2 = oracle.causal_rows(q2, inp.k, inp.v, inp.cu_seqlens, tt, hh)
+    err2 = np.abs(out2.float().cpu().numpy().reshape(-1, d) - ref2["out"]).max()
+    assert err2 <= TOL[inp.q.dtype], err2
+
+
 # --- full-size workloads, benchmark launch configuration, sampled rows --------
 
 FULL = ["llama32k", "varlen131k", "fine256k", "1m"]
