@@ -121,6 +121,72 @@ def cpu_baseline(inp, hq, budget_s, seed):
                       "block, then gate + select + attend per row); %.1f s wall" % (n, hq, t)}
 
 
+def bench_decode(moba, torch, q, k, v, block, topk, steps, nseq=16):
+    """Gated decode against a KV cache: the resident K/V re-read as nseq
+    sequences of equal length (a multiple of the block), one new row per
+    sequence (its last token), pooled keys cached beforehand. Times one decode
+    call (gate, attention parts, merge) and counts the algorithmic bytes: for
+    every (row, kv-head), the K and V rows of the union of keys its q-heads
+    attend (own block up to the row, plus each kept block once), the pooled keys
+    the gate scores, and the q and out rows."""
+    import numpy as np
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    G = hq // hkv
+    L = (T // nseq) // block * block
+    if L < block:
+        return None
+    dev = q.device
+    elem = q.element_size()
+    lens = [L] * nseq
+    cu_k = [i * L for i in range(nseq + 1)]
+    cu_q = list(range(nseq + 1))
+    toks = torch.tensor([i * L + L - 1 for i in range(nseq)], device=dev)
+    q_new = q[toks].contiguous()
+    kc, vc = k[:nseq * L], v[:nseq * L]
+    mb = L // block
+    kbar = torch.zeros(nseq * mb, hkv, d, dtype=torch.float32, device=dev)
+    moba.moba_kbar_append(kc, cu_k, [0] * nseq, block, mb, kbar)
+    cu_q_dev = torch.tensor(cu_q, dtype=torch.int32, device=dev)
+    cu_k_dev = torch.tensor(cu_k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q_new)
+    res = moba.moba_decode(q_new, kc, vc, cu_q, cu_k, block, topk, kbar, mb, return_sel=True,
+                           cu_q_dev=cu_q_dev, cu_k_dev=cu_k_dev)
+    sel = res[1].cpu().numpy()
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        moba.moba_decode(q_new, kc, vc, cu_q, cu_k, block, topk, kbar, mb, out=out,
+                         workspace=ws, cu_q_dev=cu_q_dev, cu_k_dev=cu_k_dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        moba.moba_decode(q_new, kc, vc, cu_q, cu_k, block, topk, kbar, mb, out=out,
+                         workspace=ws, cu_q_dev=cu_q_dev, cu_k_dev=cu_k_dev)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    p = L - 1
+    own = p - (p // block) * block + 1
+    i = p // block
+    kv_bytes = 0
+    for n in range(nseq):
+        for g in range(hkv):
+            blocks = set()
+            for h in range(g * G, (g + 1) * G):
+                blocks.update(int(j) for j in sel[n, h] if j >= 0)
+            kv_bytes += (own + len(blocks) * block) * d * 2 * elem
+    gate_bytes = nseq * hq * i * d * 4
+    io_bytes = 2 * nseq * hq * d * elem
+    total = kv_bytes + gate_bytes + io_bytes
+    return {"workload": "decode_%dx%dk_last_token" % (nseq, L // 1024), "sequences": nseq,
+            "cached_tokens_per_sequence": L, "new_rows_per_sequence": 1, "ms_per_step": ms,
+            "tokens_per_s": nseq / (ms * 1e-3), "algorithmic_bytes": total,
+            "achieved_gbs": total / (ms * 1e-3) / 1e9,
+            "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bound": "hbm",
+            "dense_decode_bytes": nseq * hkv * L * d * 2 * elem}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +197,7 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the gated-decode measurement")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -249,6 +316,11 @@ def main():
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, hq, args.cpu_budget, args.seed)
 
+    decode = None
+    if not args.no_decode and inp.topk > 1:
+        print("[bench] gated decode against a KV cache", file=sys.stderr, flush=True)
+        decode = bench_decode(moba, torch, q, k, v, inp.block, inp.topk, steps=20)
+
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -271,6 +343,7 @@ def main():
         "attn_mfma_frac_of_step": attn_flop / (ms * 1e-3) / 1e12 / peak_mfma,
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
         "dense_causal": dense,
+        "decode": decode,
         "stages": stage_rep,
     }
     print(json.dumps(line), flush=True)

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libmoba.so")
 MOBA_OK, MOBA_ERR_INVALID_ARG, MOBA_ERR_UNSUPPORTED, MOBA_ERR_WORKSPACE, MOBA_ERR_HIP = range(5)
 MOBA_DTYPE_F32, MOBA_DTYPE_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: MOBA_DTYPE_F32, torch.bfloat16: MOBA_DTYPE_BF16}
-STAGES = ("pool", "gate", "route", "attn_self", "attn_selected", "merge", "attn_dense")
+STAGES = ("pool", "gate", "route", "attn_self", "attn_selected", "merge", "attn_dense", "decode",
+          "kbar_append")
 
 
 class MobaError(RuntimeError):
@@ -59,6 +60,10 @@ def _load():
         "moba_attention_forward": ([i32, p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p],
                                    ctypes.c_int),
         "moba_block_pool": ([p, p, p, i32, shp, i32, p, p, sz, p], ctypes.c_int),
+        "moba_kbar_append": ([p, p, p, p, p, i32, shp, i32, i32, p, p], ctypes.c_int),
+        "moba_decode_workspace_bytes": ([p, p, i32, shp, i32, i32, i32], sz),
+        "moba_decode_forward": ([p, p, p, p, p, p, p, i32, shp, i32, i32, p, i32, p, p, sz, p, p,
+                                 p], ctypes.c_int),
         "moba_route_sizes": ([p, i32, shp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)],
                              ctypes.c_int),
         "moba_route": ([p, p, p, i32, shp, i32, i32, p, p, p, sz, p], ctypes.c_int),
@@ -79,6 +84,7 @@ def exported_symbols():
     _load()
     return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
             "moba_dense_causal_forward", "moba_attention_forward", "moba_block_pool",
+            "moba_kbar_append", "moba_decode_workspace_bytes", "moba_decode_forward",
             "moba_route_sizes", "moba_route",
             "moba_timing_enable", "moba_timing_read", "moba_stage_name"]
 
@@ -98,10 +104,11 @@ def _shape(hq, hkv, d, dtype, scale=0.0):
     return moba_shape_t(int(hq), int(hkv), int(d), _DTYPE_CODE[dtype], float(scale))
 
 
-def _cu(cu_seqlens, device):
-    """(host int32 tensor, device int32 tensor) for cu_seqlens given as list/tensor."""
+def _cu(cu_seqlens, device, dev_copy=None):
+    """(host int32 tensor, device int32 tensor) for cu_seqlens given as list/tensor;
+    a device copy the caller already holds is used as it is (no copy per call)."""
     host = torch.as_tensor(cu_seqlens, dtype=torch.int32).to("cpu").contiguous()
-    dev = host.to(device)
+    dev = dev_copy if dev_copy is not None else host.to(device)
     return host, dev
 
 
@@ -113,7 +120,7 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_qkv(q, k, v):
+def _check_qkv(q, k, v, same_len=True):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError("%s must be a GPU tensor" % name)
@@ -123,7 +130,7 @@ def _check_qkv(q, k, v):
             raise ValueError("%s must be [T, H, D]" % name)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
-    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+    if k.shape != v.shape or (same_len and q.shape[0] != k.shape[0]) or q.shape[2] != k.shape[2]:
         raise ValueError("inconsistent q/k/v shapes %s %s %s" % (q.shape, k.shape, v.shape))
 
 
@@ -154,9 +161,7 @@ def moba_forward(q, k, v, cu_seqlens, block_size, topk, *, out=None, workspace=N
     dev = q.device
     T, hq, d = q.shape
     hkv = k.shape[1]
-    host, cu_dev = _cu(cu_seqlens, dev)
-    if cu_seqlens_dev is not None:
-        cu_dev = cu_seqlens_dev
+    host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
     shape = _shape(hq, hkv, d, q.dtype, softmax_scale)
     lib = _load()
     nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
@@ -188,9 +193,7 @@ def moba_dense_causal_forward(q, k, v, cu_seqlens, *, out=None, return_lse=False
     _check_qkv(q, k, v)
     dev = q.device
     T, hq, d = q.shape
-    host, cu_dev = _cu(cu_seqlens, dev)
-    if cu_seqlens_dev is not None:
-        cu_dev = cu_seqlens_dev
+    host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
     shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
     if out is None:
         out = torch.empty_like(q)
@@ -212,9 +215,7 @@ def moba_attention(q, k, v, cu_seqlens, block_size, topk, *, full=False, out=Non
     _check_qkv(q, k, v)
     dev = q.device
     T, hq, d = q.shape
-    host, cu_dev = _cu(cu_seqlens, dev)
-    if cu_seqlens_dev is not None:
-        cu_dev = cu_seqlens_dev
+    host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
     shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
     lib = _load()
     mode = MOBA_MODE_FULL if full else MOBA_MODE_SPARSE
@@ -233,6 +234,71 @@ def moba_attention(q, k, v, cu_seqlens, block_size, topk, *, full=False, out=Non
                                       workspace.numel() if workspace is not None else 0, None,
                                       _ptr(lse), _stream(dev)))
     return (out, lse) if return_lse else out
+
+
+def moba_kbar_append(k_cache, cu_k, prev_len, block_size, max_blocks, kbar_cache, *,
+                     cu_k_dev=None):
+    """Pool into kbar_cache [num_seqs * max_blocks, Hkv, D] (fp32) the blocks of each
+    sequence that became complete when its cache grew from prev_len[n] tokens."""
+    if not k_cache.is_cuda or not k_cache.is_contiguous() or k_cache.dim() != 3:
+        raise ValueError("k_cache must be a contiguous GPU tensor [Tk, Hkv, D]")
+    dev = k_cache.device
+    hkv, d = k_cache.shape[1], k_cache.shape[2]
+    host, cdev = _cu(cu_k, dev, cu_k_dev)
+    prev_h = torch.as_tensor(prev_len, dtype=torch.int32).to("cpu").contiguous()
+    prev_d = prev_h.to(dev)
+    if prev_h.numel() != host.numel() - 1:
+        raise ValueError("prev_len needs one entry per sequence")
+    if kbar_cache.dtype != torch.float32 or not kbar_cache.is_cuda:
+        raise ValueError("kbar_cache must be an fp32 GPU tensor")
+    shape = _shape(hkv, hkv, d, k_cache.dtype)
+    _check(_load().moba_kbar_append(_ptr(k_cache), _ptr(cdev), _ptr(host), _ptr(prev_d),
+                                    _ptr(prev_h), host.numel() - 1, ctypes.byref(shape),
+                                    int(block_size), int(max_blocks), _ptr(kbar_cache),
+                                    _stream(dev)))
+    return kbar_cache
+
+
+def moba_decode(q_new, k_cache, v_cache, cu_q, cu_k, block_size, topk, kbar_cache, max_blocks,
+                *, out=None, workspace=None, return_sel=False, return_lse=False,
+                softmax_scale=0.0, cu_q_dev=None, cu_k_dev=None):
+    """MoBA attention of new rows q_new [Tq,Hq,D] (the last tokens of their
+    sequences) against the caches k_cache / v_cache [Tk,Hkv,D]. Returns out, and
+    with return_sel / return_lse the kept blocks [Tq,Hq,topk-1] and lse [Tq,Hq]."""
+    _check_qkv(q_new, k_cache, v_cache, same_len=False)
+    dev = q_new.device
+    Tq, hq, d = q_new.shape
+    hkv = k_cache.shape[1]
+    qh, qd = _cu(cu_q, dev, cu_q_dev)
+    kh, kd = _cu(cu_k, dev, cu_k_dev)
+    shape = _shape(hq, hkv, d, q_new.dtype, softmax_scale)
+    lib = _load()
+    nseq = qh.numel() - 1
+    if kh.numel() - 1 != nseq:
+        raise ValueError("cu_q and cu_k must describe the same sequences")
+    nbytes = lib.moba_decode_workspace_bytes(_ptr(qh), _ptr(kh), nseq, ctypes.byref(shape),
+                                             int(block_size), int(topk), int(max_blocks))
+    if nbytes == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    if workspace is None:
+        workspace = _workspace(nbytes, dev)
+    if out is None:
+        out = torch.empty_like(q_new)
+    sel = torch.empty(Tq, hq, max(topk - 1, 0), dtype=torch.int32, device=dev) \
+        if (return_sel and topk > 1) else None
+    lse = torch.empty(Tq, hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.moba_decode_forward(_ptr(q_new), _ptr(k_cache), _ptr(v_cache), _ptr(qd), _ptr(qh),
+                                   _ptr(kd), _ptr(kh), nseq, ctypes.byref(shape), int(block_size),
+                                   int(topk), _ptr(kbar_cache), int(max_blocks), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _ptr(sel), _ptr(lse),
+                                   _stream(dev)))
+    res = [out]
+    if return_sel:
+        res.append(sel if sel is not None else torch.empty(Tq, hq, 0, dtype=torch.int32,
+                                                           device=dev))
+    if return_lse:
+        res.append(lse)
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def moba_block_pool(k, cu_seqlens, block_size):

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "moba_plan.h"
@@ -156,9 +157,11 @@ Work carve(const Plan& p, void* base) {
 
 // ---------------------------------------------------------------------------
 // Optional per-stage timing.
-enum { ST_POOL = 0, ST_GATE, ST_ROUTE, ST_SELF, ST_SELECTED, ST_MERGE, ST_DENSE, ST_COUNT };
-static const char* kStageNames[ST_COUNT] = {"pool", "gate", "route", "attn_self",
-                                            "attn_selected", "merge", "attn_dense"};
+enum { ST_POOL = 0, ST_GATE, ST_ROUTE, ST_SELF, ST_SELECTED, ST_MERGE, ST_DENSE, ST_DECODE,
+       ST_KBAR, ST_COUNT };
+static const char* kStageNames[ST_COUNT] = {"pool",       "gate",   "route",
+                                            "attn_self",  "attn_selected", "merge",
+                                            "attn_dense", "decode", "kbar_append"};
 constexpr int kMaxTimed = 4096;
 
 struct Timing {
@@ -190,6 +193,87 @@ struct StageScope {
 static moba_status_t hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MOBA_OK;
   return fail(MOBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Checks shared by the decode entry points: shape, block size, top-k, the
+// cache lengths cu_k and the new-row counts cu_q (each new row is one of the
+// last tokens of its sequence's cache), and the pooled-key cache capacity.
+struct DecodePlan {
+  int64_t Tq = 0, rows = 0;
+  int ks = 0, nseg = 0;
+  size_t off_sel = 0, off_part_o = 0, off_part_lse = 0, total = 0;
+};
+
+static moba_status_t check_shape(const moba_shape_t* shape) {
+  if (!shape) return fail(MOBA_ERR_INVALID_ARG, "shape is NULL");
+  if (shape->num_q_heads < 1 || shape->num_kv_heads < 1)
+    return fail(MOBA_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (shape->num_q_heads % shape->num_kv_heads)
+    return fail(MOBA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (shape->head_dim != 64 && shape->head_dim != 128)
+    return fail(MOBA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", shape->head_dim);
+  if (shape->dtype != MOBA_DTYPE_F32 && shape->dtype != MOBA_DTYPE_BF16)
+    return fail(MOBA_ERR_UNSUPPORTED, "dtype %d not supported", shape->dtype);
+  return MOBA_OK;
+}
+
+static moba_status_t check_cu(const int32_t* cu, int32_t nseq, const char* name) {
+  if (!cu) return fail(MOBA_ERR_INVALID_ARG, "%s (host) is NULL", name);
+  if (cu[0] != 0) return fail(MOBA_ERR_INVALID_ARG, "%s[0] must be 0", name);
+  for (int32_t n = 0; n < nseq; ++n)
+    if (cu[n + 1] < cu[n]) return fail(MOBA_ERR_INVALID_ARG, "%s decreases at %d", name, n);
+  return MOBA_OK;
+}
+
+static moba_status_t check_block(int32_t block, int32_t max_blocks, const int32_t* cu_k,
+                                 int32_t nseq) {
+  if (block < 1) return fail(MOBA_ERR_INVALID_ARG, "block_size must be >= 1");
+  if (block % 64) return fail(MOBA_ERR_UNSUPPORTED, "block_size must be a multiple of 64");
+  if (max_blocks < 0) return fail(MOBA_ERR_INVALID_ARG, "max_blocks < 0");
+  for (int32_t n = 0; n < nseq; ++n) {
+    const int64_t len = (int64_t)cu_k[n + 1] - cu_k[n];
+    if ((len + block - 1) / block > max_blocks)
+      return fail(MOBA_ERR_INVALID_ARG, "sequence %d has %lld cached tokens, more than max_blocks "
+                  "* block_size", n, (long long)len);
+  }
+  return MOBA_OK;
+}
+
+static moba_status_t make_decode_plan(const int32_t* cu_q, const int32_t* cu_k, int32_t nseq,
+                                      const moba_shape_t* shape, int32_t block, int32_t topk,
+                                      int32_t max_blocks, DecodePlan* dp) {
+  if (nseq < 0) return fail(MOBA_ERR_INVALID_ARG, "num_seqs < 0");
+  moba_status_t st = check_shape(shape);
+  if (st != MOBA_OK) return st;
+  if ((st = check_cu(cu_q, nseq, "cu_q")) != MOBA_OK) return st;
+  if ((st = check_cu(cu_k, nseq, "cu_k")) != MOBA_OK) return st;
+  if ((st = check_block(block, max_blocks, cu_k, nseq)) != MOBA_OK) return st;
+  if (topk < 1) return fail(MOBA_ERR_INVALID_ARG, "topk must be >= 1");
+  if (topk - 1 > kMaxSelected)
+    return fail(MOBA_ERR_UNSUPPORTED, "topk - 1 must be <= %d", kMaxSelected);
+  for (int32_t n = 0; n < nseq; ++n)
+    if (cu_q[n + 1] - cu_q[n] > cu_k[n + 1] - cu_k[n])
+      return fail(MOBA_ERR_INVALID_ARG, "sequence %d has more new rows than cached tokens", n);
+  DecodePlan& P = *dp;
+  P = DecodePlan();
+  P.Tq = cu_q[nseq];
+  P.rows = P.Tq * shape->num_q_heads;
+  P.ks = topk - 1;
+  P.nseg = decode_segments(block);
+  const int64_t items = P.rows * (P.ks + 1) * P.nseg;
+  if (items * shape->head_dim >= ((int64_t)1 << 40))
+    return fail(MOBA_ERR_UNSUPPORTED, "too many new rows for one call");
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  P.off_sel = take(sizeof(int32_t) * P.rows * (P.ks > 0 ? P.ks : 1));
+  P.off_part_o = take(sizeof(float) * items * shape->head_dim);
+  P.off_part_lse = take(sizeof(float) * items);
+  P.total = off;
+  return MOBA_OK;
 }
 
 }  // namespace moba
@@ -310,6 +394,118 @@ moba_status_t moba_attention_forward(int32_t mode, const void* q, const void* k,
                                      out, lse_out, stream);
   return fail(MOBA_ERR_INVALID_ARG, "mode %d is neither MOBA_MODE_SPARSE nor MOBA_MODE_FULL",
               mode);
+}
+
+size_t moba_decode_workspace_bytes(const int32_t* cu_q_host, const int32_t* cu_k_host,
+                                   int32_t num_seqs, const moba_shape_t* shape,
+                                   int32_t block_size, int32_t topk, int32_t max_blocks) {
+  DecodePlan dp;
+  if (make_decode_plan(cu_q_host, cu_k_host, num_seqs, shape, block_size, topk, max_blocks,
+                       &dp) != MOBA_OK)
+    return 0;
+  g_err[0] = 0;
+  return dp.total;
+}
+
+moba_status_t moba_kbar_append(const void* k_cache, const int32_t* cu_k_dev,
+                               const int32_t* cu_k_host, const int32_t* prev_len_dev,
+                               const int32_t* prev_len_host, int32_t num_seqs,
+                               const moba_shape_t* shape, int32_t block_size, int32_t max_blocks,
+                               float* kbar_cache, void* stream) {
+  if (num_seqs < 0) return fail(MOBA_ERR_INVALID_ARG, "num_seqs < 0");
+  moba_status_t st = check_shape(shape);
+  if (st != MOBA_OK) return st;
+  if ((st = check_cu(cu_k_host, num_seqs, "cu_k")) != MOBA_OK) return st;
+  if ((st = check_block(block_size, max_blocks, cu_k_host, num_seqs)) != MOBA_OK) return st;
+  if (!prev_len_host) return fail(MOBA_ERR_INVALID_ARG, "prev_len_host is NULL");
+  int new_max = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t len = (int64_t)cu_k_host[n + 1] - cu_k_host[n];
+    if (prev_len_host[n] < 0 || prev_len_host[n] > len)
+      return fail(MOBA_ERR_INVALID_ARG, "prev_len[%d] = %d outside [0, %lld]", n,
+                  prev_len_host[n], (long long)len);
+    new_max = std::max(new_max, (int)(len / block_size - prev_len_host[n] / block_size));
+  }
+  if (new_max == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!k_cache || !cu_k_dev || !prev_len_dev || !kbar_cache)
+    return fail(MOBA_ERR_INVALID_ARG, "k_cache, cu_k_dev, prev_len_dev and kbar_cache must be "
+                "non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e;
+  {
+    StageScope t(ST_KBAR, s);
+    e = launch_kbar_append(k_cache, cu_k_dev, prev_len_dev, num_seqs, shape->num_kv_heads,
+                           shape->head_dim, shape->dtype, block_size, max_blocks, new_max,
+                           kbar_cache, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "pooled-key append");
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+moba_status_t moba_decode_forward(const void* q_new, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_q_dev, const int32_t* cu_q_host,
+                                  const int32_t* cu_k_dev, const int32_t* cu_k_host,
+                                  int32_t num_seqs, const moba_shape_t* shape,
+                                  int32_t block_size, int32_t topk, const float* kbar_cache,
+                                  int32_t max_blocks, void* out, void* workspace,
+                                  size_t workspace_bytes, int32_t* sel_out, float* lse_out,
+                                  void* stream) {
+  DecodePlan dp;
+  moba_status_t st = make_decode_plan(cu_q_host, cu_k_host, num_seqs, shape, block_size, topk,
+                                      max_blocks, &dp);
+  if (st != MOBA_OK) return st;
+  if (dp.rows == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!q_new || !k_cache || !v_cache || !cu_q_dev || !cu_k_dev || !out ||
+      (dp.ks > 0 && !kbar_cache))
+    return fail(MOBA_ERR_INVALID_ARG, "q_new, k_cache, v_cache, cu_q_dev, cu_k_dev, out and "
+                "(topk > 1) kbar_cache must be non-NULL");
+  if (!workspace) return fail(MOBA_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (workspace_bytes < dp.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                dp.total);
+  char* b = (char*)workspace;
+  DecodeArgs a = {};
+  a.q = q_new;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.cu_q = cu_q_dev;
+  a.cu_k = cu_k_dev;
+  a.kbar = kbar_cache;
+  a.max_blocks = max_blocks;
+  a.nseq = num_seqs;
+  a.hq = shape->num_q_heads;
+  a.hkv = shape->num_kv_heads;
+  a.block = block_size;
+  a.ks = dp.ks;
+  a.nseg = dp.nseg;
+  a.rows = dp.rows;
+  const float sc = shape->softmax_scale;
+  const float scale = (sc > 0.f && isfinite(sc)) ? sc : 1.0f / sqrtf((float)shape->head_dim);
+  a.scale_log2 = scale * kLog2e;
+  a.sel = (dp.ks > 0 && sel_out) ? sel_out : (int32_t*)(b + dp.off_sel);
+  a.part_o = (float*)(b + dp.off_part_o);
+  a.part_lse = (float*)(b + dp.off_part_lse);
+  a.out = out;
+  a.lse_out = lse_out;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  hipError_t e;
+  {
+    StageScope t(ST_DECODE, s);
+    e = launch_decode(a, shape->head_dim, shape->dtype, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "decode");
+  g_err[0] = 0;
+  return MOBA_OK;
 }
 
 moba_status_t moba_block_pool(const void* k, const int32_t* cu_seqlens_dev,

@@ -93,4 +93,27 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
 hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const void* v,
                              const int32_t* cu_dev, void* out, float* lse_out, hipStream_t s);
 
+// ---- decoding against a KV cache (NEXT-2) ----------------------------------
+struct DecodeArgs {
+  const void* q;            // [Tq, hq, d] new rows
+  const void* k;            // [Tk, hkv, d] cache (new tokens already appended)
+  const void* v;
+  const int32_t* cu_q;      // [nseq + 1] new rows per sequence (device)
+  const int32_t* cu_k;      // [nseq + 1] cache lengths (device)
+  const float* kbar;        // [nseq * max_blocks, hkv, d] pooled-key cache
+  int max_blocks, nseq, hq, hkv, block, ks, nseg;
+  int64_t rows;             // Tq * hq
+  float scale_log2;
+  int32_t* sel;             // [rows, ks] kept blocks
+  float* part_o;            // [rows, ks + 1, nseg, d] per-segment outputs
+  float* part_lse;          // [rows, ks + 1, nseg]
+  void* out;                // [Tq, hq, d]
+  float* lse_out;           // optional [Tq, hq]
+};
+int decode_segments(int block);
+hipError_t launch_decode(const DecodeArgs& a, int d, int dtype, hipStream_t s);
+hipError_t launch_kbar_append(const void* k, const int32_t* cu_dev, const int32_t* prev_dev,
+                              int nseq, int hkv, int d, int dtype, int block, int max_blocks,
+                              int new_max, float* kbar, hipStream_t s);
+
 }  // namespace moba

@@ -87,32 +87,25 @@ hipError_t launch_setup(const Plan& p, const int32_t* cu_dev, const Work& w, hip
 // row-lanes are then added in a fixed order, so the result is deterministic.
 // Also writes the pooled key split into three bf16 terms (hi + mid + lo equals
 // the fp32 value exactly for normal numbers), used by the bf16 gate.
+// Mean of `len` key rows starting at token s0 for kv head g, by one
+// 256-thread workgroup: 16-byte row slices per thread, four rows in flight,
+// then a fixed-order reduction over the row lanes (the same order wherever a
+// block is pooled). Threads c < D return the mean of column c; the rest NaN.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
-                                              const int32_t* __restrict__ cu,
-                                              const int32_t* __restrict__ blk_seq,
-                                              const int32_t* __restrict__ blk_local, int hkv,
-                                              int block, int64_t nb, float* __restrict__ kbar,
-                                              bf16* __restrict__ kbar_split) {
+__device__ __forceinline__ float block_mean(const T* __restrict__ k, int64_t s0, int64_t len,
+                                            int hkv, int g, float (&red)[256 / (D / (16 / sizeof(T)))][D + 1]) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CPR = D / VEC;          // threads per row
   constexpr int RL = 256 / CPR;         // row lanes
-  __shared__ float red[RL][D + 1];
-  const int64_t b = blockIdx.x / hkv;
-  const int g = blockIdx.x % hkv;
-  const int n = blk_seq[b];
-  const int i = blk_local[b];
-  const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
-  const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
   const int cg = threadIdx.x % CPR, rl = threadIdx.x / CPR;
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   const T* src = k + (s0 * hkv + g) * D + cg * VEC;
   const int64_t stride = (int64_t)hkv * D;
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
   int64_t r = rl;
   for (; r + 3 * RL < len; r += 4 * RL) {
-    typedef T vec_t __attribute__((ext_vector_type(VEC)));
     vec_t x0 = *reinterpret_cast<const vec_t*>(src + r * stride);
     vec_t x1 = *reinterpret_cast<const vec_t*>(src + (r + RL) * stride);
     vec_t x2 = *reinterpret_cast<const vec_t*>(src + (r + 2 * RL) * stride);
@@ -127,7 +120,6 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
     for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x3[e]);
   }
   for (; r < len; r += RL) {
-    typedef T vec_t __attribute__((ext_vector_type(VEC)));
     vec_t x0 = *reinterpret_cast<const vec_t*>(src + r * stride);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] += to_f32(x0[e]);
@@ -135,11 +127,33 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
 #pragma unroll
   for (int e = 0; e < VEC; ++e) red[rl][cg * VEC + e] = acc[e];
   __syncthreads();
+  float mean = __builtin_nanf("");
   if (threadIdx.x < D) {
     const int c = threadIdx.x;
     float sum = 0.f;
     for (int l = 0; l < RL; ++l) sum += red[l][c];
-    const float mean = sum / (float)len;
+    mean = sum / (float)len;
+  }
+  return mean;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
+                                              const int32_t* __restrict__ cu,
+                                              const int32_t* __restrict__ blk_seq,
+                                              const int32_t* __restrict__ blk_local, int hkv,
+                                              int block, int64_t nb, float* __restrict__ kbar,
+                                              bf16* __restrict__ kbar_split) {
+  __shared__ float red[256 / (D / (16 / sizeof(T)))][D + 1];
+  const int64_t b = blockIdx.x / hkv;
+  const int g = blockIdx.x % hkv;
+  const int n = blk_seq[b];
+  const int i = blk_local[b];
+  const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
+  const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
+  const float mean = block_mean<T, D>(k, s0, len, hkv, g, red);
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
     const int64_t o = (b * hkv + g) * D + c;
     kbar[o] = mean;
     if (kbar_split) {
@@ -174,6 +188,51 @@ hipError_t launch_pool(const Plan& p, const void* k, const int32_t* cu_dev, cons
     else
       hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, s, (const float*)k, cu_dev,
                          w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+  }
+  return hipGetLastError();
+}
+
+// Pooled-key cache for decoding (NEXT-2): the blocks that became complete
+// when sequence n grew from prev_len[n] to its cache length are pooled into
+// kbar[(n * max_blocks + j) * hkv + g]. Same summation as k_pool, so a cached
+// mean equals the one a prefill over the whole sequence computes.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_kbar_append(const T* __restrict__ k,
+                                                     const int32_t* __restrict__ cu,
+                                                     const int32_t* __restrict__ prev_len,
+                                                     int hkv, int block, int max_blocks,
+                                                     int new_max, float* __restrict__ kbar) {
+  __shared__ float red[256 / (D / (16 / sizeof(T)))][D + 1];
+  const int g = blockIdx.x % hkv;
+  const int jj = (blockIdx.x / hkv) % new_max;
+  const int n = blockIdx.x / hkv / new_max;
+  const int64_t len = (int64_t)cu[n + 1] - cu[n];
+  const int j = prev_len[n] / block + jj;
+  if ((int64_t)(j + 1) * block > len) return;     // not complete (uniform per workgroup)
+  const int64_t s0 = (int64_t)cu[n] + (int64_t)j * block;
+  const float mean = block_mean<T, D>(k, s0, block, hkv, g, red);
+  if (threadIdx.x < D) kbar[(((int64_t)n * max_blocks + j) * hkv + g) * D + threadIdx.x] = mean;
+}
+
+hipError_t launch_kbar_append(const void* k, const int32_t* cu_dev, const int32_t* prev_dev,
+                              int nseq, int hkv, int d, int dtype, int block, int max_blocks,
+                              int new_max, float* kbar, hipStream_t s) {
+  if (nseq == 0 || new_max == 0) return hipSuccess;
+  dim3 grid((unsigned)((int64_t)nseq * new_max * hkv)), blk(256);
+  if (dtype == MOBA_DTYPE_BF16) {
+    if (d == 128)
+      hipLaunchKernelGGL((k_kbar_append<bf16, 128>), grid, blk, 0, s, (const bf16*)k, cu_dev,
+                         prev_dev, hkv, block, max_blocks, new_max, kbar);
+    else
+      hipLaunchKernelGGL((k_kbar_append<bf16, 64>), grid, blk, 0, s, (const bf16*)k, cu_dev,
+                         prev_dev, hkv, block, max_blocks, new_max, kbar);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((k_kbar_append<float, 128>), grid, blk, 0, s, (const float*)k, cu_dev,
+                         prev_dev, hkv, block, max_blocks, new_max, kbar);
+    else
+      hipLaunchKernelGGL((k_kbar_append<float, 64>), grid, blk, 0, s, (const float*)k, cu_dev,
+                         prev_dev, hkv, block, max_blocks, new_max, kbar);
   }
   return hipGetLastError();
 }

@@ -138,6 +138,56 @@ moba_status_t moba_attention_forward(int32_t mode, const void* q, const void* k,
                                      size_t workspace_bytes, int32_t* sel_out, float* lse_out,
                                      void* stream);
 
+/* ---- Decoding against a KV cache (gated decode / chunked-prefill
+ * continuation) ------------------------------------------------------------
+ * README FAQ (issue #27, decoding); "Parameter-less Gating Mechanism". New
+ * rows are the last tokens of their sequences: a row at position p attends its
+ * own block up to p (causal) plus the top-(topk-1) complete past blocks by the
+ * score of its query against their mean-pooled keys -- exactly the prefill's
+ * row p. Layout: the caches are packed like prefill inputs, k_cache, v_cache
+ * [Tk, Hkv, D] with sequence n at tokens [cu_k[n], cu_k[n+1]) and the new
+ * tokens' K/V already appended; q_new [Tq, Hq, D] holds sequence n's new rows
+ * at [cu_q[n], cu_q[n+1]), which are its last cu_q[n+1]-cu_q[n] cached tokens.
+ * The pooled keys live in a caller-owned fp32 cache kbar_cache
+ * [num_seqs * max_blocks, Hkv, D]: block j of sequence n at row
+ * n * max_blocks + j; max_blocks must cover every cache length. */
+
+/* Pool the blocks that became complete when each sequence grew from
+ * prev_len[n] tokens to its cache length (blocks prev_len/B .. len/B - 1) into
+ * kbar_cache, with the same fp32 summation order as moba_block_pool (so the
+ * means equal a prefill's). prev_len: int32 [num_seqs], host and device
+ * copies with the same values, 0 <= prev_len[n] <= length. Blocks not yet
+ * complete are left alone. */
+moba_status_t moba_kbar_append(const void* k_cache, const int32_t* cu_k_dev,
+                               const int32_t* cu_k_host, const int32_t* prev_len_dev,
+                               const int32_t* prev_len_host, int32_t num_seqs,
+                               const moba_shape_t* shape, int32_t block_size, int32_t max_blocks,
+                               float* kbar_cache, void* stream);
+
+/* Device workspace bytes for moba_decode_forward (the kept blocks and the
+ * per-segment partial outputs of every new row). Host-only; 0 and the last
+ * error on invalid arguments. */
+size_t moba_decode_workspace_bytes(const int32_t* cu_q_host, const int32_t* cu_k_host,
+                                   int32_t num_seqs, const moba_shape_t* shape,
+                                   int32_t block_size, int32_t topk, int32_t max_blocks);
+
+/* MoBA attention for the new rows against the cache (see above).
+ *   kbar_cache: must hold every complete block before each new row's block
+ *               (moba_kbar_append after appending K); unused when topk == 1.
+ *   out:     [Tq, Hq, D] in the input dtype.
+ *   sel_out: optional int32 [Tq, Hq, topk-1], as moba_forward's.
+ *   lse_out: optional fp32 [Tq, Hq].
+ *   workspace: at least moba_decode_workspace_bytes(...), 256-byte aligned.
+ * Limits as moba_forward's; block_size a multiple of 64. */
+moba_status_t moba_decode_forward(const void* q_new, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_q_dev, const int32_t* cu_q_host,
+                                  const int32_t* cu_k_dev, const int32_t* cu_k_host,
+                                  int32_t num_seqs, const moba_shape_t* shape,
+                                  int32_t block_size, int32_t topk, const float* kbar_cache,
+                                  int32_t max_blocks, void* out, void* workspace,
+                                  size_t workspace_bytes, int32_t* sel_out, float* lse_out,
+                                  void* stream);
+
 /* The block mean-pool step alone (Kimi发布MoBA突破性实现无限上下文, "PyTorch实现
  * 关键要点": one mean-pooled key per block). Only k is read.
  *   kbar_out:  fp32 [NB, Hkv, D], NB = sum_n ceil(S_n / block_size), blocks
@@ -183,7 +233,8 @@ moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
  * Stage ids: 0 pool, 1 gate, 2 route, 3 self-block attention (which also
  * merges the parts), 4 selected-block attention, 5 merge (no separate launch:
  * always 0 launches; the id is kept so that the others stay fixed), 6 dense
- * causal attention. Returns the number of stages
+ * causal attention, 7 decode (gate, parts and merge of moba_decode_forward),
+ * 8 pooled-key append. Returns the number of stages
  * written. At most 4096 event pairs are kept; later ones are not recorded. */
 moba_status_t moba_timing_enable(int32_t enable);
 int32_t moba_timing_read(double* stage_ms, int32_t* stage_launches, int32_t max_stages);

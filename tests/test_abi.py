@@ -123,7 +123,8 @@ def test_route_requires_topk_two(lib):
 
 
 def test_stage_names(lib):
-    assert [moba.moba_stage_name(i) for i in range(7)] == list(moba.STAGES)
+    assert [moba.moba_stage_name(i) for i in range(len(moba.STAGES))] == list(moba.STAGES)
+    assert moba.moba_stage_name(len(moba.STAGES)) == ""
     assert moba.moba_stage_name(99) == ""
 
 
@@ -151,3 +152,52 @@ def test_hybrid_switch_validates_mode_and_routes_arguments(lib):
     # ... full mode ignores them but still validates the shape
     assert _attn(lib, moba.MOBA_MODE_FULL, cu, _shape(d=96), 0, 0, ws=None) == \
         moba.MOBA_ERR_UNSUPPORTED
+
+
+def _dec(lib, cu_q, cu_k, shape, block, topk, max_blocks, ws_bytes=1 << 40, ws=FAKE, kbar=FAKE):
+    return lib.moba_decode_forward(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(cu_q.data_ptr()), FAKE,
+                                   ctypes.c_void_p(cu_k.data_ptr()), cu_q.numel() - 1,
+                                   ctypes.byref(shape), block, topk, kbar, max_blocks, FAKE, ws,
+                                   ws_bytes, None, None, None)
+
+
+def test_decode_validation(lib):
+    cu_k, cu_q = _cu([5000, 3000]), _cu([1, 1])
+    # cache longer than max_blocks * block_size
+    assert _dec(lib, cu_q, cu_k, _shape(), 2048, 3, 2) == moba.MOBA_ERR_INVALID_ARG
+    # more new rows than cached tokens
+    assert _dec(lib, _cu([1, 4000]), cu_k, _shape(), 2048, 3, 3) == moba.MOBA_ERR_INVALID_ARG
+    assert _dec(lib, cu_q, cu_k, _shape(), 100, 3, 64) == moba.MOBA_ERR_UNSUPPORTED
+    assert _dec(lib, cu_q, cu_k, _shape(d=96), 2048, 3, 3) == moba.MOBA_ERR_UNSUPPORTED
+    assert _dec(lib, cu_q, cu_k, _shape(), 2048, 3, 3, ws_bytes=16) == moba.MOBA_ERR_WORKSPACE
+    assert _dec(lib, cu_q, cu_k, _shape(), 2048, 3, 3, kbar=None) == moba.MOBA_ERR_INVALID_ARG
+    # no new rows is a no-op
+    assert _dec(lib, _cu([0, 0]), cu_k, _shape(), 2048, 3, 3, ws=None) == moba.MOBA_OK
+
+
+def test_decode_workspace_scales_with_new_rows(lib):
+    shp = _shape()
+    q1, q64, k = _cu([1]), _cu([64]), _cu([32768])   # kept alive across the calls
+    one = lib.moba_decode_workspace_bytes(ctypes.c_void_p(q1.data_ptr()),
+                                          ctypes.c_void_p(k.data_ptr()), 1, ctypes.byref(shp),
+                                          2048, 3, 16)
+    many = lib.moba_decode_workspace_bytes(ctypes.c_void_p(q64.data_ptr()),
+                                           ctypes.c_void_p(k.data_ptr()), 1, ctypes.byref(shp),
+                                           2048, 3, 16)
+    # per row-head: 3 parts x 4 segments of 128 fp32 values + lse, and 2 kept ids
+    assert one >= 32 * (3 * 4 * (128 * 4 + 4) + 2 * 4)
+    assert many >= 64 * 32 * (3 * 4 * (128 * 4 + 4))
+
+
+def test_kbar_append_validation(lib):
+    cu_k = _cu([5000, 300])
+    prev = torch.tensor([0, 400], dtype=torch.int32)     # 400 > 300 cached tokens
+    st = lib.moba_kbar_append(FAKE, FAKE, ctypes.c_void_p(cu_k.data_ptr()), FAKE,
+                              ctypes.c_void_p(prev.data_ptr()), 2, ctypes.byref(_shape()), 2048,
+                              3, FAKE, None)
+    assert st == moba.MOBA_ERR_INVALID_ARG
+    ok = torch.tensor([5000, 300], dtype=torch.int32)    # nothing new to pool: a no-op
+    st = lib.moba_kbar_append(None, None, ctypes.c_void_p(cu_k.data_ptr()), None,
+                              ctypes.c_void_p(ok.data_ptr()), 2, ctypes.byref(_shape()), 2048,
+                              3, None, None)
+    assert st == moba.MOBA_OK
