@@ -1,4 +1,4 @@
-"""CPU oracle for the MoBA causal prefill forward pass.
+"""CPU oracle for the MoBA causal prefill forward pass and its backward.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` are its only users. The GPU library never
@@ -54,6 +54,9 @@ def _load():
     lib.moba_oracle_causal_rows.argtypes = [p, p, p, i64, p, p, p, i32, i32, i32, i32, f64,
                                             p, p, i32]
     lib.moba_oracle_causal_rows.restype = ctypes.c_int
+    lib.moba_oracle_backward.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f64, p, p,
+                                         p, i32]
+    lib.moba_oracle_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -171,3 +174,25 @@ def all_rows(q, k, v, cu_seqlens, block: int, topk: int, scale: float = 0.0,
     return {"out": res["out"].reshape(T, hq, d), "lse": res["lse"].reshape(T, hq),
             "sel": res["sel"].reshape(T, hq, max(topk - 1, 0)),
             "margin": res["margin"].reshape(T, hq)}
+
+
+def backward(q, k, v, dout, cu_seqlens, block: int, topk: int, scale: float = 0.0,
+             nthreads: int = 0) -> dict:
+    """Gradients of the MoBA forward with the selection held fixed, exact in fp64.
+
+    q, dout: [T, Hq, D]; k, v: [T, Hkv, D] (torch or numpy, any device).
+    Returns dict(dq [T,Hq,D], dk [T,Hkv,D], dv [T,Hkv,D]) as fp64 numpy arrays.
+    """
+    qf, kf, vf, gf = _f32(q), _f32(k), _f32(v), _f32(dout)
+    cu = _i32(cu_seqlens)
+    T, hq, d = qf.shape
+    hkv = kf.shape[1]
+    dq = np.empty((T, hq, d), dtype=np.float64)
+    dk = np.empty((T, hkv, d), dtype=np.float64)
+    dv = np.empty((T, hkv, d), dtype=np.float64)
+    rc = _load().moba_oracle_backward(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(gf), _ptr(cu),
+                                      len(cu) - 1, hq, hkv, d, block, topk, float(scale),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if rc != 0:
+        raise ValueError("moba_oracle_backward failed with code %d" % rc)
+    return {"dq": dq, "dk": dk, "dv": dv}

@@ -142,6 +142,28 @@ static double dot_ff(const float* a, const float* b, int32_t d) {
   return acc;
 }
 
+/* Steps 3-4 for one row: gate scores sigma[j] of the past blocks j < i (the
+ * unscaled dot product with the pooled keys of the row's kv head; kbar_g points
+ * at block 0 of the row's sequence for that head, consecutive blocks hkv*d
+ * apart), then nsel times the best remaining candidate; a strict '>' keeps the
+ * lower index when scores tie. chosen[0..nsel) in the order taken, taken[j]
+ * marks the kept blocks. */
+static void gate_and_select(const float* q, const double* kbar_g, int64_t i, int32_t hkv,
+                            int32_t d, int64_t nsel, double* sigma, char* taken,
+                            int32_t* chosen) {
+  for (int64_t j = 0; j < i; ++j) {
+    sigma[j] = dot(q, kbar_g + j * hkv * d, d);
+    taken[j] = 0;
+  }
+  for (int64_t m = 0; m < nsel; ++m) {
+    int64_t best = -1;
+    for (int64_t j = 0; j < i; ++j)
+      if (!taken[j] && (best < 0 || sigma[j] > sigma[best])) best = j;
+    taken[best] = 1;
+    chosen[m] = (int32_t)best;
+  }
+}
+
 /* Steps 3-5 for a list of rows.
  *
  * q_rows:   [nrows, d] fp32, the query vector of each requested row.
@@ -215,20 +237,9 @@ int moba_oracle_rows(const float* q_rows, const int32_t* row_tok, const int32_t*
         const int32_t g = h / group;
         const int64_t nsel = (topk - 1 < i) ? topk - 1 : i;
 
-        /* Step 3: gate scores of the past blocks j < i. */
-        for (int64_t j = 0; j < i; ++j) {
-          sigma[j] = dot(q, kbar + ((block_base[n] + j) * hkv + g) * d, d);
-          taken[j] = 0;
-        }
-        /* Step 4: repeatedly take the best remaining candidate. A strict '>'
-         * keeps the lower index when scores tie. */
-        for (int64_t m = 0; m < nsel; ++m) {
-          int64_t best = -1;
-          for (int64_t j = 0; j < i; ++j)
-            if (!taken[j] && (best < 0 || sigma[j] > sigma[best])) best = j;
-          taken[best] = 1;
-          chosen[m] = (int32_t)best;
-        }
+        /* Steps 3-4: gate scores of the past blocks j < i, then selection. */
+        gate_and_select(q, kbar + (block_base[n] * hkv + g) * d, i, hkv, d, nsel, sigma, taken,
+                        chosen);
         if (margin) {
           double worst_kept = INFINITY, best_left = -INFINITY;
           for (int64_t j = 0; j < i; ++j) {
@@ -354,5 +365,129 @@ int moba_oracle_causal_rows(const float* q_rows, const int32_t* row_tok,
     }
     free(logit);
   }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Backward of steps 5 for every row of a batch, with the selection of steps
+ * 1-4 held fixed (top-k is piecewise constant in its inputs, so no gradient
+ * reaches the gate; README, "Trainable Block Sparse Attention": MoBA is trained
+ * through its attention). For a row r with attended set A_r, logits
+ * l_s = c * q_r . k_s, probabilities p_s = softmax over A_r, output
+ * o_r = sum p_s v_s, and the loss gradient dO_r, the chain rule gives
+ *   dP_s = dO_r . v_s,   Delta_r = sum_{s in A_r} p_s dP_s  (= dO_r . o_r),
+ *   dS_s = p_s (dP_s - Delta_r),
+ *   dq_r = c sum_s dS_s k_s,   dk_s += c dS_s q_r,   dv_s += p_s dO_r,
+ * with dk, dv summed over every row (all q heads of the kv group) that attends
+ * key s. Work is split over (sequence, kv head) pairs, each owning its keys'
+ * gradients, so the sums need no locking.
+ *
+ * q, dout: [T, hq, d] fp32;  k, v: [T, hkv, d] fp32.
+ * dq: [T, hq, d] fp64;  dk, dv: [T, hkv, d] fp64 (fully written).
+ */
+int moba_oracle_backward(const float* q, const float* k, const float* v, const float* dout,
+                         const int32_t* cu_seqlens, int32_t nseq, int32_t hq, int32_t hkv,
+                         int32_t d, int32_t block, int32_t topk, double scale, double* dq,
+                         double* dk, double* dv, int32_t nthreads) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || topk < 1 ||
+      !check_layout(cu_seqlens, nseq, hq, hkv, d, block))
+    return ORACLE_BAD_ARG;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+  const int64_t T = cu_seqlens[nseq];
+  int64_t* block_base = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseq > 0 ? nseq : 1));
+  if (!block_base) return ORACLE_NO_MEMORY;
+  const int64_t nb_total = count_blocks(cu_seqlens, nseq, block, block_base);
+  double* kbar = (double*)malloc(sizeof(double) * (size_t)(nb_total * hkv * d + 1));
+  if (!kbar) { free(block_base); return ORACLE_NO_MEMORY; }
+  moba_oracle_pool(k, cu_seqlens, nseq, hkv, d, block, kbar);
+  memset(dk, 0, sizeof(double) * (size_t)(T * hkv * d));
+  memset(dv, 0, sizeof(double) * (size_t)(T * hkv * d));
+  int64_t max_blocks = 0;
+  for (int32_t n = 0; n < nseq; ++n) {
+    int64_t nb = num_blocks_of((int64_t)cu_seqlens[n + 1] - cu_seqlens[n], block);
+    if (nb > max_blocks) max_blocks = nb;
+  }
+  const int32_t group = hq / hkv;
+  int failed = 0;
+
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* sigma = (double*)malloc(sizeof(double) * (size_t)(max_blocks + 1));
+    char* taken = (char*)malloc((size_t)(max_blocks + 1));
+    int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)block * (size_t)topk);
+    double* p = (double*)malloc(sizeof(double) * (size_t)block * (size_t)topk);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)block * (size_t)topk);
+    if (!sigma || !taken || !chosen || !key || !p || !dp) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+      for (int64_t unit = 0; unit < (int64_t)nseq * hkv; ++unit) {
+        const int32_t n = (int32_t)(unit / hkv), g = (int32_t)(unit % hkv);
+        const int64_t start = cu_seqlens[n], len = (int64_t)cu_seqlens[n + 1] - start;
+        for (int64_t t = 0; t < len; ++t) {
+          const int64_t tok = start + t, i = t / block;
+          const int64_t nsel = (topk - 1 < i) ? topk - 1 : i;
+          for (int32_t h = g * group; h < (g + 1) * group; ++h) {
+            const float* qr = q + (tok * hq + h) * d;
+            const float* dor = dout + (tok * hq + h) * d;
+            gate_and_select(qr, kbar + (block_base[n] * hkv + g) * d, i, hkv, d, nsel, sigma,
+                            taken, chosen);
+            /* the attended keys: own block up to t, then the kept blocks */
+            int64_t na = 0;
+            for (int64_t s = start + i * block; s <= tok; ++s) key[na++] = s;
+            for (int64_t m = 0; m < nsel; ++m)
+              for (int64_t s = start + (int64_t)chosen[m] * block;
+                   s < start + ((int64_t)chosen[m] + 1) * block; ++s)
+                key[na++] = s;
+            double mx = -INFINITY;
+            for (int64_t a = 0; a < na; ++a) {
+              p[a] = scale * dot_ff(qr, k + (key[a] * hkv + g) * d, d);
+              if (p[a] > mx) mx = p[a];
+            }
+            double denom = 0.0;
+            for (int64_t a = 0; a < na; ++a) {
+              p[a] = exp(p[a] - mx);
+              denom += p[a];
+            }
+            double delta = 0.0;
+            for (int64_t a = 0; a < na; ++a) {
+              p[a] /= denom;
+              dp[a] = dot_ff(dor, v + (key[a] * hkv + g) * d, d);
+              delta += p[a] * dp[a];
+            }
+            double* dqr = dq + (tok * hq + h) * d;
+            for (int32_t e = 0; e < d; ++e) dqr[e] = 0.0;
+            for (int64_t a = 0; a < na; ++a) {
+              const double ds = p[a] * (dp[a] - delta);
+              const float* ks = k + (key[a] * hkv + g) * d;
+              double* dks = dk + (key[a] * hkv + g) * d;
+              double* dvs = dv + (key[a] * hkv + g) * d;
+              for (int32_t e = 0; e < d; ++e) {
+                dqr[e] += scale * ds * (double)ks[e];
+                dks[e] += scale * ds * (double)qr[e];
+                dvs[e] += p[a] * (double)dor[e];
+              }
+            }
+          }
+        }
+      }
+    }
+    free(sigma);
+    free(taken);
+    free(chosen);
+    free(key);
+    free(p);
+    free(dp);
+  }
+  free(kbar);
+  free(block_base);
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
