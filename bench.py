@@ -187,6 +187,43 @@ def bench_decode(moba, torch, q, k, v, block, topk, steps, nseq=16):
             "dense_decode_bytes": nseq * hkv * L * d * 2 * elem}
 
 
+def bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma, steps):
+    """Backward (dq, dk, dv with the selection held fixed) after one forward that
+    keeps sel and lse; inputs and the upstream gradient resident in HBM.
+    Algorithmic work: the five products of the attention backward over the
+    forward's attended pairs (S and dP recomputed, dQ, dK, dV), 2.5x the
+    forward's two."""
+    from synth_inputs import make_grad
+    q, k, v = inp.q, inp.k, inp.v
+    out, sel, lse = moba.moba_forward(q, k, v, inp.cu_seqlens, inp.block, inp.topk,
+                                      return_sel=True, return_lse=True, cu_seqlens_dev=cu_dev)
+    dout = make_grad(q.shape, q.dtype, seed=3, device=q.device)
+    nbytes = moba.moba_backward_workspace_bytes(inp.cu_seqlens, q.shape[1], k.shape[1],
+                                                q.shape[2], q.dtype, inp.block, inp.topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def run():
+        moba.moba_backward(q, k, v, out, lse, dout, sel, inp.cu_seqlens, inp.block, inp.topk,
+                           dq=dq, dk=dk, dv=dv, workspace=ws, cu_seqlens_dev=cu_dev)
+
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(q.device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 2.5 * attn_flop
+    tf = flop / (ms * 1e-3) / 1e12
+    del out, sel, lse, dout, ws, dq, dk, dv
+    return {"ms": ms, "steps": steps, "tokens_per_s": q.shape[0] / (ms * 1e-3),
+            "algorithmic_flop": flop, "achieved_tflops": tf, "mfma_frac": tf / peak_mfma}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +235,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the gated-decode measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -321,6 +359,12 @@ def main():
         print("[bench] gated decode against a KV cache", file=sys.stderr, flush=True)
         decode = bench_decode(moba, torch, q, k, v, inp.block, inp.topk, steps=20)
 
+    backward = None
+    if not args.no_backward:
+        print("[bench] backward", file=sys.stderr, flush=True)
+        backward = bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma,
+                                  steps=max(1, min(args.steps, 5)))
+
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -344,6 +388,7 @@ def main():
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
         "dense_causal": dense,
         "decode": decode,
+        "backward": backward,
         "stages": stage_rep,
     }
     print(json.dumps(line), flush=True)

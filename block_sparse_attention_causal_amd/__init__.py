@@ -23,7 +23,7 @@ MOBA_OK, MOBA_ERR_INVALID_ARG, MOBA_ERR_UNSUPPORTED, MOBA_ERR_WORKSPACE, MOBA_ER
 MOBA_DTYPE_F32, MOBA_DTYPE_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: MOBA_DTYPE_F32, torch.bfloat16: MOBA_DTYPE_BF16}
 STAGES = ("pool", "gate", "route", "attn_self", "attn_selected", "merge", "attn_dense", "decode",
-          "kbar_append")
+          "kbar_append", "backward")
 
 
 class MobaError(RuntimeError):
@@ -64,6 +64,9 @@ def _load():
         "moba_decode_workspace_bytes": ([p, p, i32, shp, i32, i32, i32], sz),
         "moba_decode_forward": ([p, p, p, p, p, p, p, i32, shp, i32, i32, p, i32, p, p, sz, p, p,
                                  p], ctypes.c_int),
+        "moba_backward_workspace_bytes": ([p, i32, shp, i32, i32], sz),
+        "moba_backward": ([p, p, p, p, p, p, p, p, p, i32, shp, i32, i32, p, p, p, p, sz, p],
+                          ctypes.c_int),
         "moba_route_sizes": ([p, i32, shp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)],
                              ctypes.c_int),
         "moba_route": ([p, p, p, i32, shp, i32, i32, p, p, p, sz, p], ctypes.c_int),
@@ -85,7 +88,7 @@ def exported_symbols():
     return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
             "moba_dense_causal_forward", "moba_attention_forward", "moba_block_pool",
             "moba_kbar_append", "moba_decode_workspace_bytes", "moba_decode_forward",
-            "moba_route_sizes", "moba_route",
+            "moba_backward_workspace_bytes", "moba_backward", "moba_route_sizes", "moba_route",
             "moba_timing_enable", "moba_timing_read", "moba_stage_name"]
 
 
@@ -202,6 +205,53 @@ def moba_dense_causal_forward(q, k, v, cu_seqlens, *, out=None, return_lse=False
                                              host.numel() - 1, ctypes.byref(shape), _ptr(out),
                                              _ptr(lse), _stream(dev)))
     return (out, lse) if return_lse else out
+
+
+def moba_backward_workspace_bytes(cu_seqlens, num_q_heads, num_kv_heads, head_dim, dtype,
+                                  block_size, topk) -> int:
+    host = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous()
+    shape = _shape(num_q_heads, num_kv_heads, head_dim, dtype)
+    n = _load().moba_backward_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                              int(block_size), int(topk))
+    if n == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    return int(n)
+
+
+def moba_backward(q, k, v, out, lse, dout, sel, cu_seqlens, block_size, topk, *, dq=None,
+                  dk=None, dv=None, workspace=None, softmax_scale=0.0, cu_seqlens_dev=None):
+    """Gradients (dq, dk, dv) of moba_forward's out for the upstream gradient
+    dout, with the forward's selection sel [T,Hq,topk-1] and lse [T,Hq] held
+    fixed (both from moba_forward with return_sel / return_lse)."""
+    _check_qkv(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("%s must be a contiguous GPU tensor shaped and typed like q" % name)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != q.shape[:2]:
+        raise ValueError("lse must be a contiguous fp32 tensor [T, Hq]")
+    if topk > 1 and (sel is None or sel.dtype != torch.int32 or not sel.is_contiguous()
+                     or tuple(sel.shape) != (q.shape[0], q.shape[1], topk - 1)):
+        raise ValueError("sel must be the forward's int32 selection [T, Hq, topk-1]")
+    dev = q.device
+    T, hq, d = q.shape
+    host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
+    shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
+    lib = _load()
+    if workspace is None:
+        nbytes = lib.moba_backward_workspace_bytes(_ptr(host), host.numel() - 1,
+                                                   ctypes.byref(shape), int(block_size), int(topk))
+        if nbytes == 0 and moba_last_error():
+            raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+        workspace = _workspace(nbytes, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib.moba_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                             _ptr(sel) if topk > 1 else None, _ptr(cu_dev), _ptr(host),
+                             host.numel() - 1, ctypes.byref(shape), int(block_size), int(topk),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                             _stream(dev)))
+    return dq, dk, dv
 
 
 MOBA_MODE_SPARSE, MOBA_MODE_FULL = 0, 1

@@ -55,11 +55,6 @@ struct AttnArgs {
   float scale_log2;
 };
 
-// Position of key k (0..63 inside a chunk) in the transposed V copy: inside
-// each group of 16 keys, bits 2 and 3 of the index are swapped.
-__device__ __forceinline__ int vt_pos_of_group4(int kg) {  // kg = key / 4
-  return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-}
 
 template <typename T, int D>
 struct KVStage {
@@ -178,19 +173,6 @@ __device__ __forceinline__ void bare_barrier() {
 // s_waitcnt with vmcnt(n) (n < 64) and lgkmcnt(0), expcnt untouched (gfx9 encoding).
 #define MOBA_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
 
-template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
-template <> __device__ __forceinline__ bf16x8 pack8<bf16>(const float* x) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
-  return r;
-}
-template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
-  f32x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = x[e];
-  return r;
-}
 
 // Writes the 32 normalised output rows of every wave. The accumulator layout
 // gives each lane 4-value slivers of one row, so a direct store would touch 32

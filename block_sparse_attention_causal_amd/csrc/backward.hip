@@ -1,0 +1,548 @@
+// NEXT-1: backward of the MoBA attention (dQ, dK, dV through the own block and
+// the selected blocks; the selection is held fixed — top-k is piecewise
+// constant, so no gradient reaches the gate: MoBA README, "Trainable Block
+// Sparse Attention").
+//
+// For a row r with attended set A_r, p_s = exp(c q_r.k_s - lse_r) (lse_r from
+// the forward, over the whole set A_r), dO_r the incoming gradient:
+//   Delta_r = dO_r . O_r                   (k_bwd_delta)
+//   dS_s    = p_s (dO_r . v_s - Delta_r)
+//   dQ_r    = c sum_s dS_s k_s             (query-major: k_bwd_dq, one pass per part)
+//   dK_s    = c sum_r dS_s q_r             (key-major: k_bwd_dkdv, all rows that
+//   dV_s    =   sum_r p_s dO_r              attend the key, own block and routed)
+// Both passes reuse the forward's routing lists (rebuilt from the forward's
+// selection): the selected-block dQ pass walks the lists' tiles like the
+// forward, and the dK/dV pass walks, for each key tile of a block, the block's
+// own later rows and then the rows routed to it — so every key's gradient is
+// summed by one workgroup, without atomics, and the result is deterministic.
+//
+// Matrix-core layout as in the forward (32x32x16 MFMA; fp32 inputs feed the
+// same data to eight 32x32x2 MFMAs): a register operand from the accumulator
+// layout (dS^T, P, dS) pairs with an LDS operand transposed with the row order
+// of vt_pos_of_group4.
+#include "moba_plan.h"
+
+namespace moba {
+
+enum { BWD_SELF = 0, BWD_SELECTED = 1 };
+constexpr int BKC = 64;       // keys per chunk (dQ pass)
+constexpr int BRC = 32;       // rows per chunk (dK/dV pass)
+constexpr int BDQ_WAVES = 8;  // dQ pass: 8 waves x 32 rows, the forward's tiles
+constexpr int BKV_WAVES = 4;  // dK/dV pass: 4 waves x 32 keys = 128 keys per tile
+
+// ---------------------------------------------------------------------------
+// Delta_r = sum_d dO_r[d] O_r[d] in fp32, D/8 lanes per row.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_bwd_delta(const T* __restrict__ out,
+                                                   const T* __restrict__ dout, int64_t rows,
+                                                   float* __restrict__ delta) {
+  constexpr int TPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const T* o = out + row * D + 8 * c;
+    const T* g = dout + row * D + 8 * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(to_f32(o[e]), to_f32(g[e]), acc);
+  }
+#pragma unroll
+  for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Staging of R rows of a [*, D] matrix into LDS twice: row-major (row stride
+// LD) and transposed (column stride TLD, rows permuted by vt_pos_of_group4).
+// Each thread of NT moves 16-byte pieces; `rowptr(r)` gives row r's global
+// address or nullptr (zeros).
+template <typename T, int D, int R, int NT>
+struct RowStage {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int LD = D + VEC;
+  static constexpr int TLD = R + VEC;
+  static constexpr int PIECES = R * (D / VEC);
+  static constexpr int PPT = (PIECES + NT - 1) / NT;
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  vec_t x[PPT];
+
+  template <typename F>
+  __device__ __forceinline__ void load(F rowptr) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pc = (int)threadIdx.x + u * NT;
+      const int r = pc / (D / VEC), c = pc % (D / VEC);
+      const T* src = (pc < PIECES) ? rowptr(r) : nullptr;
+      if (src) {
+        x[u] = *reinterpret_cast<const vec_t*>(src + c * VEC);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[u][e] = (T)0.0f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store_rows(T* rows_lds) const {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pc = (int)threadIdx.x + u * NT;
+      if (pc >= PIECES) break;
+      const int r = pc / (D / VEC), c = pc % (D / VEC);
+      *reinterpret_cast<vec_t*>(rows_lds + r * LD + c * VEC) = x[u];
+    }
+  }
+  __device__ __forceinline__ void store(T* rows_lds, T* trans_lds) const {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pc = (int)threadIdx.x + u * NT;
+      if (pc >= PIECES) break;
+      const int r = pc / (D / VEC), c = pc % (D / VEC);
+      *reinterpret_cast<vec_t*>(rows_lds + r * LD + c * VEC) = x[u];
+      const int pos = vt_pos_of_group4(r >> 2) + (r & 3);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) trans_lds[(c * VEC + e) * TLD + pos] = x[u][e];
+    }
+  }
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;       // forward log-sum-exp per row (natural log)
+  const float* delta;     // [T * hq]
+  const int32_t* cu;
+  const int32_t* blk_seq;
+  const int32_t* blk_local;
+  const int32_t* blk_base;
+  const int32_t* list_offsets;
+  const int32_t* tile_offsets;
+  const int32_t* entries;
+  float* dq_sel;          // [T * hq * ks, D] selected-block dQ parts (scaled), by entry value
+  void* dq;               // [T, hq, D]
+  void* dk;               // [T, hkv, D]
+  void* dv;
+  int64_t nb, nlists, ntiles, padded;
+  int nseq, hq, hkv, hg, block, ks, nu, kvt;   // kvt = key tiles per block
+  float scale, scale_log2;
+};
+
+// ---------------------------------------------------------------------------
+// dQ, query-major. SELF tiles: up to 256 rows of one block (32 consecutive
+// tokens per wave, the HG heads of one kv group side by side), keys from the
+// block start to the tile's last token, causal. SELECTED tiles: up to 256
+// routed (row, slot) entries of one list, keys = the whole block. Per wave and
+// 64-key chunk: S^T = K Q^T and dP^T = V dO^T (K, V row-major in LDS, Q^T and
+// dO^T in registers), P^T = exp2(S^T c log2e - lse log2e), dS^T = P^T (dP^T -
+// Delta), dQ^T += K^T dS^T (K^T transposed in LDS). SELECTED writes the
+// scaled part per entry; SELF, which runs after, adds the row's parts.
+template <typename T, int D, int MODE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_bwd_dq(BwdArgs a) {
+  typedef typename Frag<T>::type frag_t;
+  typedef RowStage<T, D, BKC, 512> Stage;
+  __shared__ __attribute__((aligned(16))) T smem[2 * BKC * Stage::LD + D * Stage::TLD];
+  T* const k_rows = smem;
+  T* const v_rows = smem + BKC * Stage::LD;
+  T* const k_trans = smem + 2 * BKC * Stage::LD;
+  const int64_t logical = xcd_logical(blockIdx.x, a.padded);
+  if (logical >= a.ntiles) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int group = a.hq / a.hkv;
+  const T* __restrict__ q = (const T*)a.q;
+  const T* __restrict__ k = (const T*)a.k;
+  const T* __restrict__ v = (const T*)a.v;
+  const T* __restrict__ dout = (const T*)a.dout;
+
+  int g;
+  int64_t kbeg, kend;
+  int64_t row = -1, dst_index = -1, wtok0 = 0;
+  int blk_i = 0;
+  if (MODE == BWD_SELECTED) {
+    const int64_t tile = logical;
+    const int32_t* toffs = a.tile_offsets;
+    if (tile >= toffs[a.nlists]) return;
+    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int64_t b = L / a.hkv;
+    g = L % a.hkv;
+    const int n = a.blk_seq[b], j = a.blk_local[b];
+    kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
+    kend = kbeg + a.block;
+    const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kRowsPerTile +
+                       (int64_t)w * kRowsPerWave;
+    const int64_t e1 = a.list_offsets[L + 1];
+    if (e0 + r32 < e1) {
+      const int32_t ev = a.entries[e0 + r32];
+      dst_index = ev;
+      row = ev / a.ks;
+    }
+  } else {
+    const int tt = 32 * (8 / a.hg);
+    const int nhs = a.hq / a.hg;
+    const int u = a.nu - 1 - (int)(logical % a.nu);
+    const int64_t rest = logical / a.nu;
+    const int hs = (int)(rest % nhs);
+    const int64_t b = a.nb - 1 - rest / nhs;
+    const int n = a.blk_seq[b], i = a.blk_local[b];
+    blk_i = i;
+    const int64_t blk_start = (int64_t)a.cu[n] + (int64_t)i * a.block;
+    const int64_t blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
+    const int64_t tok0 = blk_start + (int64_t)u * tt;
+    if (tok0 >= blk_end) return;
+    const int h = hs * a.hg + (w % a.hg);
+    g = h / group;
+    wtok0 = tok0 + (int64_t)(w / a.hg) * 32;
+    kbeg = blk_start;
+    kend = min(tok0 + tt, blk_end);
+    if (wtok0 + r32 < blk_end) {
+      row = (wtok0 + r32) * a.hq + h;
+      dst_index = row;
+    }
+  }
+
+  frag_t qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qf[kk] = (row >= 0) ? load8(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+    gf[kk] = (row >= 0) ? load8(dout + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+  }
+  const float lse_l2 = (row >= 0) ? a.lse[row] * kLog2e : 0.f;
+  const float dlt = (row >= 0) ? a.delta[row] : 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  const int nch = (int)((kend - kbeg + BKC - 1) / BKC);
+  const int64_t kstride = (int64_t)a.hkv * D;
+  Stage sk, sv;
+  for (int c = 0; c < nch; ++c) {
+    const int64_t c0 = kbeg + (int64_t)c * BKC;
+    sk.load([&](int r) -> const T* { return (c0 + r < kend) ? k + (c0 + r) * kstride + g * D : nullptr; });
+    sv.load([&](int r) -> const T* { return (c0 + r < kend) ? v + (c0 + r) * kstride + g * D : nullptr; });
+    __syncthreads();                       // the previous chunk is consumed
+    sk.store(k_rows, k_trans);
+    sv.store_rows(v_rows);
+    __syncthreads();
+    const bool needed = (MODE == BWD_SELECTED) || (c0 <= wtok0 + 31);
+    if (!needed) continue;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { s[kt][e] = 0.f; dp[kt][e] = 0.f; }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const frag_t kf = load8(k_rows + (32 * kt + r32) * Stage::LD + 16 * kk + 8 * half);
+        const frag_t vf = load8(v_rows + (32 * kt + r32) * Stage::LD + 16 * kk + 8 * half);
+        s[kt] = mma_k16(kf, qf[kk], s[kt]);
+        dp[kt] = mma_k16(vf, gf[kk], dp[kt]);
+      }
+    }
+    float dsv[2][16];
+    const int64_t tok = wtok0 + r32;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t key = c0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+        const bool masked = (key >= kend) || (MODE == BWD_SELF && key > tok);
+        const float p = masked ? 0.f : fast_exp2(fmaf(s[kt][e], a.scale_log2, -lse_l2));
+        dsv[kt][e] = p * (dp[kt][e] - dlt);
+      }
+    frag_t df[4];
+    df[0] = pack8<T>(&dsv[0][0]);
+    df[1] = pack8<T>(&dsv[0][8]);
+    df[2] = pack8<T>(&dsv[1][0]);
+    df[3] = pack8<T>(&dsv[1][8]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const frag_t kf = load8(k_trans + (32 * dt + r32) * Stage::TLD + 16 * qq + 8 * half);
+        acc[dt] = mma_k16(kf, df[qq], acc[dt]);
+      }
+  }
+
+  // epilogue: lane holds dQ^T[32dt + 8(i/4) + 4half + i%4][row r32]
+  if (dst_index < 0) return;
+  if (MODE == BWD_SELECTED) {
+    float* dst = a.dq_sel + dst_index * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        float4 val = make_float4(acc[dt][4 * aa] * a.scale, acc[dt][4 * aa + 1] * a.scale,
+                                 acc[dt][4 * aa + 2] * a.scale, acc[dt][4 * aa + 3] * a.scale);
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
+      }
+  } else {
+    const int nsel = min(a.ks, blk_i);
+    typedef T vec4_t __attribute__((ext_vector_type(4)));
+    T* dst = (T*)a.dq + dst_index * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        const int d0 = 32 * dt + 8 * aa + 4 * half;
+        float x[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) x[b] = acc[dt][4 * aa + b] * a.scale;
+        for (int sl = 0; sl < nsel; ++sl) {
+          const float4 pt = *reinterpret_cast<const float4*>(
+              a.dq_sel + (dst_index * a.ks + sl) * D + d0);
+          x[0] += pt.x;
+          x[1] += pt.y;
+          x[2] += pt.z;
+          x[3] += pt.w;
+        }
+        vec4_t r;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) r[b] = from_f32<T>(x[b]);
+        *reinterpret_cast<vec4_t*>(dst + d0) = r;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV, key-major. Tile = 128 keys of one block and kv head (4 waves x 32
+// keys). Rows: the block's own rows from the tile's first token on (the G q
+// heads of the group; causal mask), then the rows routed to the block. Per 32-
+// row chunk (Q, dO staged in LDS row-major and transposed, lse and Delta per
+// row) and wave: S = Q K_w^T, dP = dO V_w^T (K_w^T, V_w^T register operands),
+// P = exp2(S c log2e - lse log2e), dS = P (dP - Delta), dV_w^T += dO^T P,
+// dK_w^T += Q^T dS.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+k_bwd_dkdv(BwdArgs a) {
+  typedef typename Frag<T>::type frag_t;
+  typedef RowStage<T, D, BRC, 256> Stage;
+  __shared__ __attribute__((aligned(16))) T smem[2 * BRC * Stage::LD + 2 * D * Stage::TLD];
+  __shared__ float lse_s[BRC], dlt_s[BRC];
+  __shared__ int tok_s[BRC];
+  T* const q_rows = smem;
+  T* const g_rows = smem + BRC * Stage::LD;
+  T* const q_trans = smem + 2 * BRC * Stage::LD;
+  T* const g_trans = q_trans + D * Stage::TLD;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int G = a.hq / a.hkv;
+  // tile -> (global block b, kv head g, key tile kt)
+  const int64_t tile = blockIdx.x;
+  const int kt = (int)(tile % a.kvt);
+  const int g = (int)((tile / a.kvt) % a.hkv);
+  const int64_t b = tile / a.kvt / a.hkv;
+  const int n = a.blk_seq[b], i = a.blk_local[b];
+  const int64_t blk_start = (int64_t)a.cu[n] + (int64_t)i * a.block;
+  const int64_t blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
+  const int64_t t0 = blk_start + (int64_t)kt * (BKV_WAVES * 32);
+  if (t0 >= blk_end) return;
+  const int64_t key = t0 + 32 * w + r32;          // this lane's key (as a B column)
+  const bool key_ok = key < blk_end;
+  const int64_t kstride = (int64_t)a.hkv * D;
+  const T* __restrict__ q = (const T*)a.q;
+  const T* __restrict__ dout = (const T*)a.dout;
+
+  frag_t kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    kf[kk] = key_ok ? load8((const T*)a.k + key * kstride + g * D + 16 * kk + 8 * half)
+                    : zero8<frag_t>();
+    vf[kk] = key_ok ? load8((const T*)a.v + key * kstride + g * D + 16 * kk + 8 * half)
+                    : zero8<frag_t>();
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dk[dt][e] = 0.f; dv[dt][e] = 0.f; }
+
+  // rows: own block tokens t0 .. blk_end-1 (x G heads), then list (b, g) entries
+  const int64_t nself = (blk_end - t0) * G;
+  int64_t e_beg = 0, nsel_rows = 0;
+  if (a.ks > 0 && a.list_offsets) {
+    const int64_t L = b * a.hkv + g;
+    e_beg = a.list_offsets[L];
+    nsel_rows = a.list_offsets[L + 1] - e_beg;
+  }
+  const int64_t nrows = nself + nsel_rows;
+  auto row_of = [&](int64_t rr, int64_t& tokv) -> int64_t {
+    if (rr < nself) {
+      tokv = t0 + rr / G;
+      return tokv * a.hq + g * G + (int)(rr % G);
+    }
+    const int64_t rowid = a.entries[e_beg + (rr - nself)] / a.ks;
+    tokv = rowid / a.hq;
+    return rowid;
+  };
+  Stage sq, sg;
+  for (int64_t c0 = 0; c0 < nrows; c0 += BRC) {
+    sq.load([&](int r) -> const T* {
+      if (c0 + r >= nrows) return nullptr;
+      int64_t tv;
+      return q + row_of(c0 + r, tv) * D;
+    });
+    sg.load([&](int r) -> const T* {
+      if (c0 + r >= nrows) return nullptr;
+      int64_t tv;
+      return dout + row_of(c0 + r, tv) * D;
+    });
+    __syncthreads();
+    sq.store(q_rows, q_trans);
+    sg.store(g_rows, g_trans);
+    if (threadIdx.x < BRC) {
+      const int64_t rr = c0 + threadIdx.x;
+      if (rr < nrows) {
+        int64_t tv;
+        const int64_t rowid = row_of(rr, tv);
+        lse_s[threadIdx.x] = a.lse[rowid] * kLog2e;
+        dlt_s[threadIdx.x] = a.delta[rowid];
+        tok_s[threadIdx.x] = (rr < nself) ? (int)(tv - t0) : -1;   // own-block rows only
+      } else {
+        lse_s[threadIdx.x] = 0.f;
+        dlt_s[threadIdx.x] = 0.f;
+        tok_s[threadIdx.x] = -2;                                   // no row
+      }
+    }
+    __syncthreads();
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const frag_t qa = load8(q_rows + r32 * Stage::LD + 16 * kk + 8 * half);
+      const frag_t ga = load8(g_rows + r32 * Stage::LD + 16 * kk + 8 * half);
+      s = mma_k16(qa, kf[kk], s);
+      dp = mma_k16(ga, vf[kk], dp);
+    }
+    // lane: key column r32 of wave w; items: rows 8(e/4) + 4half + e%4
+    float pv[16], dsv[16];
+    const int keyrel = (int)(key - t0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = 8 * (e >> 2) + 4 * half + (e & 3);
+      const int tr = tok_s[rr];
+      const bool masked = !key_ok || tr == -2 || (tr >= 0 && keyrel > tr);
+      const float p = masked ? 0.f : fast_exp2(fmaf(s[e], a.scale_log2, -lse_s[rr]));
+      pv[e] = p;
+      dsv[e] = p * (dp[e] - dlt_s[rr]);
+    }
+    frag_t pf[2], df[2];
+    pf[0] = pack8<T>(&pv[0]);
+    pf[1] = pack8<T>(&pv[8]);
+    df[0] = pack8<T>(&dsv[0]);
+    df[1] = pack8<T>(&dsv[8]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const frag_t ga = load8(g_trans + (32 * dt + r32) * Stage::TLD + 16 * qq + 8 * half);
+        const frag_t qa = load8(q_trans + (32 * dt + r32) * Stage::TLD + 16 * qq + 8 * half);
+        dv[dt] = mma_k16(ga, pf[qq], dv[dt]);
+        dk[dt] = mma_k16(qa, df[qq], dk[dt]);
+      }
+    __syncthreads();                       // before the next chunk overwrites LDS
+  }
+
+  // epilogue: lane holds d{K,V}^T[32dt + 8(i/4) + 4half + i%4][key]
+  if (!key_ok) return;
+  typedef T vec4_t __attribute__((ext_vector_type(4)));
+  T* dkp = (T*)a.dk + key * kstride + g * D;
+  T* dvp = (T*)a.dv + key * kstride + g * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const int d0 = 32 * dt + 8 * aa + 4 * half;
+      vec4_t rk, rv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rk[e] = from_f32<T>(dk[dt][4 * aa + e] * a.scale);
+        rv[e] = from_f32<T>(dv[dt][4 * aa + e]);
+      }
+      *reinterpret_cast<vec4_t*>(dkp + d0) = rk;
+      *reinterpret_cast<vec4_t*>(dvp + d0) = rv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out,
+                             float* delta, hipStream_t s) {
+  const int64_t rows = p.T * p.hq;
+  {
+    const int rpw = 256 / (D / 8);
+    hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256),
+                       0, s, (const T*)out, (const T*)base.dout, rows, delta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs a = base;
+  if (p.ks > 0 && p.nentries > 0) {
+    a.ntiles = p.max_tiles;
+    a.padded = (p.max_tiles + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELECTED>), dim3((unsigned)a.padded), dim3(512), 0, s,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int tt = 32 * (8 / p.hg);
+    a.nu = (p.block + tt - 1) / tt;
+    a.ntiles = p.nb * a.nu * (p.hq / p.hg);
+    a.padded = (a.ntiles + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELF>), dim3((unsigned)a.padded), dim3(512), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    a.kvt = (p.block + BKV_WAVES * 32 - 1) / (BKV_WAVES * 32);
+    const int64_t tiles = p.nb * p.hkv * a.kvt;
+    hipLaunchKernelGGL((k_bwd_dkdv<T, D>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Plan& p, const void* q, const void* k, const void* v,
+                           const void* out, const float* lse, const void* dout,
+                           const int32_t* cu_dev, const Work& w, float* delta, float* dq_sel,
+                           void* dq, void* dk, void* dv, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  BwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.cu = cu_dev;
+  a.blk_seq = w.blk_seq;
+  a.blk_local = w.blk_local;
+  a.blk_base = w.blk_base;
+  a.list_offsets = (p.ks > 0) ? w.list_offsets : nullptr;
+  a.tile_offsets = (p.ks > 0) ? w.tile_offsets : nullptr;
+  a.entries = (p.ks > 0) ? w.entries : nullptr;
+  a.dq_sel = dq_sel;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.nb = p.nb;
+  a.nlists = p.nlists;
+  a.nseq = p.nseq;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.hg = p.hg;
+  a.block = p.block;
+  a.ks = p.ks;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * kLog2e;
+  if (p.dtype == MOBA_DTYPE_BF16)
+    return p.d == 128 ? bwd_launch<bf16, 128>(a, p, out, delta, s)
+                      : bwd_launch<bf16, 64>(a, p, out, delta, s);
+  return p.d == 128 ? bwd_launch<float, 128>(a, p, out, delta, s)
+                    : bwd_launch<float, 64>(a, p, out, delta, s);
+}
+
+}  // namespace moba

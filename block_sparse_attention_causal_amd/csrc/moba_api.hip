@@ -158,10 +158,11 @@ Work carve(const Plan& p, void* base) {
 // ---------------------------------------------------------------------------
 // Optional per-stage timing.
 enum { ST_POOL = 0, ST_GATE, ST_ROUTE, ST_SELF, ST_SELECTED, ST_MERGE, ST_DENSE, ST_DECODE,
-       ST_KBAR, ST_COUNT };
+       ST_KBAR, ST_BACKWARD, ST_COUNT };
 static const char* kStageNames[ST_COUNT] = {"pool",       "gate",   "route",
                                             "attn_self",  "attn_selected", "merge",
-                                            "attn_dense", "decode", "kbar_append"};
+                                            "attn_dense", "decode", "kbar_append",
+                                            "backward"};
 constexpr int kMaxTimed = 4096;
 
 struct Timing {
@@ -274,6 +275,25 @@ static moba_status_t make_decode_plan(const int32_t* cu_q, const int32_t* cu_k, 
   P.off_part_lse = take(sizeof(float) * items);
   P.total = off;
   return MOBA_OK;
+}
+
+// Backward workspace: the forward's block tables and routing buffers (the
+// lists are rebuilt from the forward's selection), then the selected-block dQ
+// parts in place of the forward's partial outputs (fp32, indexed like them by
+// row * ks + slot) and Delta per row.
+struct BwdLayout {
+  size_t off_delta = 0, off_dq_sel = 0, total = 0;
+};
+
+static BwdLayout backward_layout(const Plan& p) {
+  BwdLayout l;
+  size_t off = p.ks > 0 ? p.off_o_sel : p.total;
+  l.off_dq_sel = off;
+  off = align256(off + sizeof(float) * (size_t)(p.T * p.hq) * p.ks * p.d);
+  l.off_delta = off;
+  off = align256(off + sizeof(float) * (size_t)(p.T * p.hq));
+  l.total = std::max(off, p.total);
+  return l;
 }
 
 }  // namespace moba
@@ -504,6 +524,64 @@ moba_status_t moba_decode_forward(const void* q_new, const void* k_cache, const 
     e = launch_decode(a, shape->head_dim, shape->dtype, s);
   }
   if (e != hipSuccess) return hip_status(e, "decode");
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+size_t moba_backward_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                     const moba_shape_t* shape, int32_t block_size,
+                                     int32_t topk) {
+  Plan p;
+  if (make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0) !=
+      MOBA_OK)
+    return 0;
+  g_err[0] = 0;
+  return backward_layout(p).total;
+}
+
+moba_status_t moba_backward(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, const int32_t* sel,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, const moba_shape_t* shape, int32_t block_size,
+                            int32_t topk, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Plan p;
+  moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (p.T == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !cu_seqlens_dev)
+    return fail(MOBA_ERR_INVALID_ARG, "q, k, v, out, lse, dout, dq, dk, dv and cu_seqlens_dev "
+                "must be non-NULL");
+  if (p.ks > 0 && !sel) return fail(MOBA_ERR_INVALID_ARG, "sel is NULL (topk > 1)");
+  if (!workspace) return fail(MOBA_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const BwdLayout bl = backward_layout(p);
+  if (workspace_bytes < bl.total)
+    return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                bl.total);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  Work w = carve(p, workspace);
+  char* b = (char*)workspace;
+  float* delta = (float*)(b + bl.off_delta);
+  float* dq_sel = (float*)(b + bl.off_dq_sel);
+  hipError_t e = launch_setup(p, cu_seqlens_dev, w, s);
+  if (e != hipSuccess) return hip_status(e, "setup");
+  if (p.ks > 0) {
+    StageScope t(ST_ROUTE, s);
+    e = launch_route(p, sel, cu_seqlens_dev, w, w.list_offsets, w.entries, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "route");
+  {
+    StageScope t(ST_BACKWARD, s);
+    e = launch_backward(p, q, k, v, out, lse, dout, cu_seqlens_dev, w, delta, dq_sel, dq, dk,
+                        dv, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "backward");
   g_err[0] = 0;
   return MOBA_OK;
 }

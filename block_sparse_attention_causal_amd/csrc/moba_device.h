@@ -147,4 +147,30 @@ __device__ __forceinline__ int upper_index(const int32_t* offs, int n, int64_t x
   return lo;
 }
 
+// Eight fp32 values as one MFMA operand fragment of the input type.
+template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
+template <> __device__ __forceinline__ bf16x8 pack8<bf16>(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[e];
+  return r;
+}
+template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+  return r;
+}
+
+// Transposed copies of a matrix whose rows are the k index of an MFMA with a
+// register operand from the 32x32 accumulator layout (P^T, dS^T, P, dS): lane
+// l holds, per 16-row group, rows {4h..4h+3} and {8+4h..8+4h+3} (h = l / 32),
+// and the operand wants k index 8h + e at element e. So inside each group of 16
+// rows the transposed copy stores the four-row groups in the order 0, 2, 1, 3,
+// i.e. bits 2 and 3 of the row index are swapped. Returns the position of the
+// first row of four-row group kg (= row / 4).
+__device__ __forceinline__ int vt_pos_of_group4(int kg) {
+  return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+}
+
 }  // namespace moba

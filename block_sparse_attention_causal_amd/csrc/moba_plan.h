@@ -93,6 +93,12 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
 hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const void* v,
                              const int32_t* cu_dev, void* out, float* lse_out, hipStream_t s);
 
+// ---- backward (NEXT-1) --------------------------------------------------------
+hipError_t launch_backward(const Plan& p, const void* q, const void* k, const void* v,
+                           const void* out, const float* lse, const void* dout,
+                           const int32_t* cu_dev, const Work& w, float* delta, float* dq_sel,
+                           void* dq, void* dk, void* dv, hipStream_t s);
+
 // ---- decoding against a KV cache (NEXT-2) ----------------------------------
 struct DecodeArgs {
   const void* q;            // [Tq, hq, d] new rows

@@ -138,6 +138,32 @@ moba_status_t moba_attention_forward(int32_t mode, const void* q, const void* k,
                                      size_t workspace_bytes, int32_t* sel_out, float* lse_out,
                                      void* stream);
 
+/* ---- Backward ---------------------------------------------------------------
+ * Gradients of moba_forward's out with respect to q, k and v, given the
+ * gradient dout of a loss with respect to out. The forward's selection is
+ * held fixed (top-k is piecewise constant: no gradient reaches the gate;
+ * README, "Trainable Block Sparse Attention"). With p the attention weights of
+ * a row over its attended keys, Delta = dout . out, dS = p (dout . v - Delta):
+ *   dq = scale * sum dS k,  dk = scale * sum_rows dS q,  dv = sum_rows p dout,
+ * dk and dv summed over every row (all q heads of the kv group) that attends
+ * the key. Deterministic (no atomics).
+ *   out, lse:  the forward's out and lse_out ([T, Hq, D] input dtype; fp32
+ *              [T, Hq]) for these q, k, v.
+ *   dout:      [T, Hq, D] input dtype.
+ *   sel:       the forward's sel_out, int32 [T, Hq, topk-1] (unused when topk == 1).
+ *   dq: [T, Hq, D]; dk, dv: [T, Hkv, D] (input dtype), written in full.
+ *   workspace: at least moba_backward_workspace_bytes(...), 256-byte aligned.
+ * Same shapes and limits as moba_forward. */
+size_t moba_backward_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                     const moba_shape_t* shape, int32_t block_size,
+                                     int32_t topk);
+moba_status_t moba_backward(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, const int32_t* sel,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, const moba_shape_t* shape, int32_t block_size,
+                            int32_t topk, void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* ---- Decoding against a KV cache (gated decode / chunked-prefill
  * continuation) ------------------------------------------------------------
  * README FAQ (issue #27, decoding); "Parameter-less Gating Mechanism". New
@@ -234,7 +260,8 @@ moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
  * merges the parts), 4 selected-block attention, 5 merge (no separate launch:
  * always 0 launches; the id is kept so that the others stay fixed), 6 dense
  * causal attention, 7 decode (gate, parts and merge of moba_decode_forward),
- * 8 pooled-key append. Returns the number of stages
+ * 8 pooled-key append, 9 backward (Delta, dq and dk/dv passes; its routing is
+ * timed as stage 2). Returns the number of stages
  * written. At most 4096 event pairs are kept; later ones are not recorded. */
 moba_status_t moba_timing_enable(int32_t enable);
 int32_t moba_timing_read(double* stage_ms, int32_t* stage_launches, int32_t max_stages);

@@ -57,6 +57,9 @@ def _load():
     lib.moba_oracle_backward.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f64, p, p,
                                          p, i32]
     lib.moba_oracle_backward.restype = ctypes.c_int
+    lib.moba_oracle_dq_rows.argtypes = [p, p, p, p, i64, p, p, p, i32, i32, i32, i32, i32, i32,
+                                        f64, p, i32]
+    lib.moba_oracle_dq_rows.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -196,3 +199,23 @@ def backward(q, k, v, dout, cu_seqlens, block: int, topk: int, scale: float = 0.
     if rc != 0:
         raise ValueError("moba_oracle_backward failed with code %d" % rc)
     return {"dq": dq, "dk": dk, "dv": dv}
+
+
+def dq_rows(q, k, v, dout, cu_seqlens, block: int, topk: int, tokens, heads,
+            scale: float = 0.0, k_f32=None, v_f32=None, nthreads: int = 0) -> np.ndarray:
+    """dq of the given (token, head) rows only, exact in fp64 ([n, D]); q and
+    dout are the full [T, Hq, D] tensors (any device), k/v as in rows()."""
+    qr, tokens, heads = _row_queries(q, tokens, heads)
+    gr, _, _ = _row_queries(dout, tokens, heads)
+    kf = _f32(k) if k_f32 is None else k_f32
+    vf = _f32(v) if v_f32 is None else v_f32
+    cu = _i32(cu_seqlens)
+    n = len(tokens)
+    T, hkv, d = kf.shape
+    dq = np.empty((n, d), dtype=np.float64)
+    rc = _load().moba_oracle_dq_rows(_ptr(qr), _ptr(gr), _ptr(tokens), _ptr(heads), n, _ptr(kf),
+                                     _ptr(vf), _ptr(cu), len(cu) - 1, q.shape[1], hkv, d, block,
+                                     topk, float(scale), _ptr(dq), int(nthreads))
+    if rc != 0:
+        raise ValueError("moba_oracle_dq_rows failed with code %d" % rc)
+    return dq

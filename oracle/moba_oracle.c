@@ -368,18 +368,70 @@ int moba_oracle_causal_rows(const float* q_rows, const int32_t* row_tok,
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
-/* Backward of steps 5 for every row of a batch, with the selection of steps
- * 1-4 held fixed (top-k is piecewise constant in its inputs, so no gradient
- * reaches the gate; README, "Trainable Block Sparse Attention": MoBA is trained
- * through its attention). For a row r with attended set A_r, logits
- * l_s = c * q_r . k_s, probabilities p_s = softmax over A_r, output
- * o_r = sum p_s v_s, and the loss gradient dO_r, the chain rule gives
+/* Backward of step 5 for one row, with the selection of steps 1-4 held fixed
+ * (top-k is piecewise constant in its inputs, so no gradient reaches the gate;
+ * README, "Trainable Block Sparse Attention": MoBA is trained through its
+ * attention). For a row r with attended set A_r, logits l_s = c * q_r . k_s,
+ * probabilities p_s = softmax over A_r, output o_r = sum p_s v_s, and the loss
+ * gradient dO_r, the chain rule gives
  *   dP_s = dO_r . v_s,   Delta_r = sum_{s in A_r} p_s dP_s  (= dO_r . o_r),
  *   dS_s = p_s (dP_s - Delta_r),
- *   dq_r = c sum_s dS_s k_s,   dk_s += c dS_s q_r,   dv_s += p_s dO_r,
- * with dk, dv summed over every row (all q heads of the kv group) that attends
- * key s. Work is split over (sequence, kv head) pairs, each owning its keys'
- * gradients, so the sums need no locking.
+ *   dq_r = c sum_s dS_s k_s,   dk_s += c dS_s q_r,   dv_s += p_s dO_r.
+ * qr, dor: the row's query and output gradient; kbar_g as in gate_and_select;
+ * t: the row's position in its sequence (start = first token). dqr is written;
+ * dk, dv ([T, hkv, d]) are accumulated into unless NULL. key, p, dp hold
+ * block * topk entries; sigma, taken, chosen as in gate_and_select. */
+static void row_backward(const float* qr, const float* dor, const float* k, const float* v,
+                         const double* kbar_g, int64_t start, int64_t t, int32_t g,
+                         int32_t hkv, int32_t d, int32_t block, int32_t topk, double scale,
+                         double* dqr, double* dk, double* dv, double* sigma, char* taken,
+                         int32_t* chosen, int64_t* key, double* p, double* dp) {
+  const int64_t tok = start + t, i = t / block;
+  const int64_t nsel = (topk - 1 < i) ? topk - 1 : i;
+  gate_and_select(qr, kbar_g, i, hkv, d, nsel, sigma, taken, chosen);
+  /* the attended keys: own block up to t, then the kept blocks */
+  int64_t na = 0;
+  for (int64_t s = start + i * block; s <= tok; ++s) key[na++] = s;
+  for (int64_t m = 0; m < nsel; ++m)
+    for (int64_t s = start + (int64_t)chosen[m] * block;
+         s < start + ((int64_t)chosen[m] + 1) * block; ++s)
+      key[na++] = s;
+  double mx = -INFINITY;
+  for (int64_t a = 0; a < na; ++a) {
+    p[a] = scale * dot_ff(qr, k + (key[a] * hkv + g) * d, d);
+    if (p[a] > mx) mx = p[a];
+  }
+  double denom = 0.0;
+  for (int64_t a = 0; a < na; ++a) {
+    p[a] = exp(p[a] - mx);
+    denom += p[a];
+  }
+  double delta = 0.0;
+  for (int64_t a = 0; a < na; ++a) {
+    p[a] /= denom;
+    dp[a] = dot_ff(dor, v + (key[a] * hkv + g) * d, d);
+    delta += p[a] * dp[a];
+  }
+  for (int32_t e = 0; e < d; ++e) dqr[e] = 0.0;
+  for (int64_t a = 0; a < na; ++a) {
+    const double ds = p[a] * (dp[a] - delta);
+    const float* ks = k + (key[a] * hkv + g) * d;
+    for (int32_t e = 0; e < d; ++e) dqr[e] += scale * ds * (double)ks[e];
+    if (dk) {
+      double* dks = dk + (key[a] * hkv + g) * d;
+      double* dvs = dv + (key[a] * hkv + g) * d;
+      for (int32_t e = 0; e < d; ++e) {
+        dks[e] += scale * ds * (double)qr[e];
+        dvs[e] += p[a] * (double)dor[e];
+      }
+    }
+  }
+}
+
+/* Backward (row_backward) for every row of a batch: dk and dv summed over
+ * every row (all q heads of the kv group) that attends each key. Work is split
+ * over (sequence, kv head) pairs, each owning its keys' gradients, so the sums
+ * need no locking.
  *
  * q, dout: [T, hq, d] fp32;  k, v: [T, hkv, d] fp32.
  * dq: [T, hq, d] fp64;  dk, dv: [T, hkv, d] fp64 (fully written).
@@ -432,52 +484,86 @@ int moba_oracle_backward(const float* q, const float* k, const float* v, const f
       for (int64_t unit = 0; unit < (int64_t)nseq * hkv; ++unit) {
         const int32_t n = (int32_t)(unit / hkv), g = (int32_t)(unit % hkv);
         const int64_t start = cu_seqlens[n], len = (int64_t)cu_seqlens[n + 1] - start;
-        for (int64_t t = 0; t < len; ++t) {
-          const int64_t tok = start + t, i = t / block;
-          const int64_t nsel = (topk - 1 < i) ? topk - 1 : i;
+        for (int64_t t = 0; t < len; ++t)
           for (int32_t h = g * group; h < (g + 1) * group; ++h) {
-            const float* qr = q + (tok * hq + h) * d;
-            const float* dor = dout + (tok * hq + h) * d;
-            gate_and_select(qr, kbar + (block_base[n] * hkv + g) * d, i, hkv, d, nsel, sigma,
-                            taken, chosen);
-            /* the attended keys: own block up to t, then the kept blocks */
-            int64_t na = 0;
-            for (int64_t s = start + i * block; s <= tok; ++s) key[na++] = s;
-            for (int64_t m = 0; m < nsel; ++m)
-              for (int64_t s = start + (int64_t)chosen[m] * block;
-                   s < start + ((int64_t)chosen[m] + 1) * block; ++s)
-                key[na++] = s;
-            double mx = -INFINITY;
-            for (int64_t a = 0; a < na; ++a) {
-              p[a] = scale * dot_ff(qr, k + (key[a] * hkv + g) * d, d);
-              if (p[a] > mx) mx = p[a];
-            }
-            double denom = 0.0;
-            for (int64_t a = 0; a < na; ++a) {
-              p[a] = exp(p[a] - mx);
-              denom += p[a];
-            }
-            double delta = 0.0;
-            for (int64_t a = 0; a < na; ++a) {
-              p[a] /= denom;
-              dp[a] = dot_ff(dor, v + (key[a] * hkv + g) * d, d);
-              delta += p[a] * dp[a];
-            }
-            double* dqr = dq + (tok * hq + h) * d;
-            for (int32_t e = 0; e < d; ++e) dqr[e] = 0.0;
-            for (int64_t a = 0; a < na; ++a) {
-              const double ds = p[a] * (dp[a] - delta);
-              const float* ks = k + (key[a] * hkv + g) * d;
-              double* dks = dk + (key[a] * hkv + g) * d;
-              double* dvs = dv + (key[a] * hkv + g) * d;
-              for (int32_t e = 0; e < d; ++e) {
-                dqr[e] += scale * ds * (double)ks[e];
-                dks[e] += scale * ds * (double)qr[e];
-                dvs[e] += p[a] * (double)dor[e];
-              }
-            }
+            const int64_t r = (start + t) * hq + h;
+            row_backward(q + r * d, dout + r * d, k, v, kbar + (block_base[n] * hkv + g) * d,
+                         start, t, g, hkv, d, block, topk, scale, dq + r * d, dk, dv, sigma,
+                         taken, chosen, key, p, dp);
           }
-        }
+      }
+    }
+    free(sigma);
+    free(taken);
+    free(chosen);
+    free(key);
+    free(p);
+    free(dp);
+  }
+  free(kbar);
+  free(block_base);
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* dq (row_backward) of a list of rows only, each from its own inputs: for
+ * checks of sampled rows of batches too large for moba_oracle_backward.
+ * q_rows, dout_rows: [nrows, d] fp32, the rows' query and output gradient;
+ * row_tok, row_head as in moba_oracle_rows; dq: [nrows, d] fp64. */
+int moba_oracle_dq_rows(const float* q_rows, const float* dout_rows, const int32_t* row_tok,
+                        const int32_t* row_head, int64_t nrows, const float* k, const float* v,
+                        const int32_t* cu_seqlens, int32_t nseq, int32_t hq, int32_t hkv,
+                        int32_t d, int32_t block, int32_t topk, double scale, double* dq,
+                        int32_t nthreads) {
+  if (!q_rows || !dout_rows || !row_tok || !row_head || !k || !v || !dq || nrows < 0 ||
+      topk < 1 || !check_layout(cu_seqlens, nseq, hq, hkv, d, block))
+    return ORACLE_BAD_ARG;
+  const int64_t T = cu_seqlens[nseq];
+  for (int64_t r = 0; r < nrows; ++r)
+    if (row_tok[r] < 0 || row_tok[r] >= T || row_head[r] < 0 || row_head[r] >= hq)
+      return ORACLE_BAD_ARG;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+  int64_t* block_base = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseq > 0 ? nseq : 1));
+  if (!block_base) return ORACLE_NO_MEMORY;
+  const int64_t nb_total = count_blocks(cu_seqlens, nseq, block, block_base);
+  double* kbar = (double*)malloc(sizeof(double) * (size_t)(nb_total * hkv * d + 1));
+  if (!kbar) { free(block_base); return ORACLE_NO_MEMORY; }
+  moba_oracle_pool(k, cu_seqlens, nseq, hkv, d, block, kbar);
+  int64_t max_blocks = 0;
+  for (int32_t n = 0; n < nseq; ++n) {
+    int64_t nb = num_blocks_of((int64_t)cu_seqlens[n + 1] - cu_seqlens[n], block);
+    if (nb > max_blocks) max_blocks = nb;
+  }
+  const int32_t group = hq / hkv;
+  int failed = 0;
+
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* sigma = (double*)malloc(sizeof(double) * (size_t)(max_blocks + 1));
+    char* taken = (char*)malloc((size_t)(max_blocks + 1));
+    int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)block * (size_t)topk);
+    double* p = (double*)malloc(sizeof(double) * (size_t)block * (size_t)topk);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)block * (size_t)topk);
+    if (!sigma || !taken || !chosen || !key || !p || !dp) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t tok = row_tok[r];
+        const int32_t n = seq_of_token(cu_seqlens, nseq, tok);
+        const int32_t g = row_head[r] / group;
+        row_backward(q_rows + r * d, dout_rows + r * d, k, v,
+                     kbar + (block_base[n] * hkv + g) * d, cu_seqlens[n], tok - cu_seqlens[n],
+                     g, hkv, d, block, topk, scale, dq + r * d, NULL, NULL, sigma, taken,
+                     chosen, key, p, dp);
       }
     }
     free(sigma);

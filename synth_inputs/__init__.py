@@ -162,6 +162,21 @@ def make_inputs(seqlens, hq, hkv, d, block, topk, dtype="bf16", seed=0, device="
                   meta=meta)
 
 
+def make_grad(shape, dtype="bf16", seed=0, device="cpu", mean=0.0,
+              chunk_rows=32768) -> torch.Tensor:
+    """Seeded upstream gradient dO ~ N(mean, 1) of the given [T, H, D] shape."""
+    tdt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev).manual_seed(seed + 7)
+    g = torch.empty(tuple(shape), dtype=tdt, device=dev)
+    for a in range(0, shape[0], chunk_rows):
+        b = min(shape[0], a + chunk_rows)
+        x = torch.randn((b - a,) + tuple(shape[1:]), generator=gen, device=dev,
+                        dtype=torch.float32)
+        g[a:b] = (x + mean).to(tdt)
+    return g
+
+
 def make_config(name: str, seed=0, device="cpu", **over) -> Inputs:
     cfg = dict(CONFIGS[name])
     cfg.update(over)

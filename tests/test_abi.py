@@ -201,3 +201,38 @@ def test_kbar_append_validation(lib):
                               ctypes.c_void_p(ok.data_ptr()), 2, ctypes.byref(_shape()), 2048,
                               3, None, None)
     assert st == moba.MOBA_OK
+
+
+def _bwd(lib, cu, shape, block, topk, ws_bytes=1 << 40, ws=FAKE, sel=FAKE, dq=FAKE):
+    return lib.moba_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, sel, FAKE,
+                             ctypes.c_void_p(cu.data_ptr()), cu.numel() - 1, ctypes.byref(shape),
+                             block, topk, dq, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_backward_validation(lib):
+    cu = _cu([4096, 1000])
+    assert _bwd(lib, cu, _shape(d=96), 2048, 3) == moba.MOBA_ERR_UNSUPPORTED
+    assert _bwd(lib, cu, _shape(), 100, 3) == moba.MOBA_ERR_UNSUPPORTED
+    assert _bwd(lib, cu, _shape(hq=6, hkv=4), 2048, 3) == moba.MOBA_ERR_INVALID_ARG
+    assert _bwd(lib, cu, _shape(), 2048, 3, sel=None) == moba.MOBA_ERR_INVALID_ARG
+    assert _bwd(lib, cu, _shape(), 2048, 3, dq=None) == moba.MOBA_ERR_INVALID_ARG
+    assert _bwd(lib, cu, _shape(), 2048, 3, ws_bytes=1000) == moba.MOBA_ERR_WORKSPACE
+    assert _bwd(lib, cu, _shape(), 2048, 3, ws=ctypes.c_void_p(0x10000010)) == \
+        moba.MOBA_ERR_INVALID_ARG
+    # topk == 1 needs no selection
+    st = _bwd(lib, cu, _shape(), 2048, 1, sel=None, ws_bytes=0, ws=None)
+    assert st == moba.MOBA_ERR_INVALID_ARG and "workspace" in lib.moba_last_error().decode()
+    # an empty batch is a no-op
+    assert _bwd(lib, _cu([0]), _shape(), 2048, 3, ws=None, sel=None) == moba.MOBA_OK
+
+
+def test_backward_workspace_holds_dq_parts_and_delta(lib):
+    shp = _shape()
+    cu = _cu([32768])
+    n = lib.moba_backward_workspace_bytes(ctypes.c_void_p(cu.data_ptr()), 1, ctypes.byref(shp),
+                                          2048, 3)
+    rows = 32768 * 32
+    # fp32 dQ parts for every (row, slot) and Delta per row
+    assert n >= rows * 2 * 128 * 4 + rows * 4
+    assert n >= moba.moba_workspace_bytes([0, 32768], 32, 8, 128, torch.bfloat16, 2048, 3) - \
+        rows * 2 * 128 * 2

@@ -6,6 +6,8 @@ mathematics, not from re-typing the oracle's formula.
   attention (the mask taken from the forward oracle's selection);
 - closed-form identities: per (sequence, kv head) the dV rows sum to the sum
   of the group's dO rows, and the dK rows sum to zero (every row's dS sums to 0).
+The per-row dq entry (dq_rows, for sampled rows of large batches) must give
+the rows of the full backward's dq.
 """
 import numpy as np
 import pytest
@@ -103,3 +105,15 @@ def test_identities(setup):
             do_sum = do[a:b, g * G:(g + 1) * G].sum((0, 1))
             np.testing.assert_allclose(dv_sum, do_sum, atol=1e-9)
             np.testing.assert_allclose(grads["dk"][a:b, g].sum(0), 0.0, atol=1e-9)
+
+
+def test_dq_rows_equals_full_backward(setup):
+    inp, dout, grads = setup
+    c = CASE
+    rng = np.random.default_rng(5)
+    T = sum(c["seqlens"])
+    toks = rng.integers(0, T, 40).astype(np.int32)
+    heads = rng.integers(0, c["hq"], 40).astype(np.int32)
+    dq = oracle.dq_rows(inp.q, inp.k, inp.v, dout, inp.cu_seqlens, c["block"], c["topk"], toks,
+                        heads)
+    np.testing.assert_array_equal(dq, grads["dq"][toks, heads])
