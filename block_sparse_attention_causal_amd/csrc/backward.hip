@@ -468,6 +468,244 @@ k_bwd_dkdv(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV for 16-bit inputs with D = 128: the same products as k_bwd_dkdv, 8
+// waves x 32 keys = 256 keys per tile, with the rows streamed through LDS by
+// direct loads. Per 32-row chunk every wave issues exactly four direct loads:
+// the list entries of chunk c+5 (row ids of the routed rows, 4 bytes a lane),
+// then for chunk c+3 its four rows of Q and of dO (16 bytes a lane, the
+// forward's swizzled row layout) and the chunk's lse and Delta (4 bytes a
+// lane, a private copy per wave). "Chunk c+1 and the entries of chunk c+4 have
+// landed" is then exactly vmcnt(7) at the end of iteration c. Q^T and dO^T
+// fragments come from the row-major copies through ds_read_b64_tr_b16, in the
+// row order of the score accumulators, so no transposed copy is written.
+// Tiles are dealt to the XCDs list by list (all key tiles of one list on one
+// XCD, which then shares the list's rows in its L2; consecutive lists on
+// different XCDs, which spreads the long lists of the much-selected blocks).
+constexpr int DKV_WAVES = 8;
+
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* rows, int r0, int dt, int vrow, int vx0,
+                                          int vx1, int vbyte) {
+  // rows r0 + {4h .. 4h+3} and r0 + 8 + {4h .. 4h+3} of column 32 dt + (lane % 32)
+  const bf16* b = rows + (r0 + vrow) * 128;
+  const bf16* p0 = b + 8 * ((4 * dt) ^ vx0) + vbyte;
+  const bf16* p1 = b + 8 * 128 + 8 * ((4 * dt) ^ vx1) + vbyte;
+  const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r;
+  r[0] = x0[0]; r[1] = x0[1]; r[2] = x0[2]; r[3] = x0[3];
+  r[4] = x1[0]; r[5] = x1[1]; r[6] = x1[2]; r[7] = x1[3];
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__global__ void __launch_bounds__(64 * DKV_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_bwd_dkdv_dma(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 128;
+  constexpr int CH = BRC * D;       // elements of one 32-row block
+  constexpr int RBUF = 2 * CH;      // Q rows then dO rows
+  __shared__ __attribute__((aligned(16))) bf16 rows_lds[4 * RBUF];
+  __shared__ __attribute__((aligned(16))) float meta_lds[4][DKV_WAVES][64];
+  __shared__ __attribute__((aligned(16))) int32_t ent_lds[8][DKV_WAVES][64];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[DKV_WAVES * 32 * D];   // the tile's V rows
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int G = a.hq / a.hkv;
+  // dispatch id -> (list, key tile): list 8 (j / kvt) + xcd, key tile j % kvt
+  const int64_t j = blockIdx.x >> 3;
+  const int64_t L = 8 * (j / a.kvt) + (blockIdx.x & 7);
+  if (L >= a.nb * a.hkv) return;
+  const int kt = (int)(j % a.kvt);
+  const int g = (int)(L % a.hkv);
+  const int64_t b = L / a.hkv;
+  const int n = a.blk_seq[b], i = a.blk_local[b];
+  const int64_t blk_start = (int64_t)a.cu[n] + (int64_t)i * a.block;
+  const int64_t blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
+  const int64_t t0 = blk_start + (int64_t)kt * (DKV_WAVES * 32);
+  if (t0 >= blk_end) return;
+  const int keyrel = 32 * w + r32;
+  const int64_t key = t0 + keyrel;
+  const bool key_ok = key < blk_end;
+  const bool wave_live = t0 + 32 * w < blk_end;
+  const int64_t kstride = (int64_t)a.hkv * D;
+  const bf16* __restrict__ q = (const bf16*)a.q;
+  const bf16* __restrict__ dout = (const bf16*)a.dout;
+
+  // K fragments in registers; the wave's 32 V rows in LDS (swizzled like the
+  // streamed rows), both of keys clamped into the block
+  bf16x8 kf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    kf[kk] = key_ok ? load8((const bf16*)a.k + key * kstride + g * D + 16 * kk + 8 * half)
+                    : zero8<bf16x8>();
+  {
+    const uint32_t vdst = lds_addr(v_lds) + (uint32_t)(32 * w * D * 2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 4 * u + (lane >> 4);
+      const int64_t kv = min(t0 + 32 * w + r, blk_end - 1);
+      dma16((const bf16*)a.v + kv * kstride + g * D + 8 * ((lane & 15) ^ swz(r)),
+            vdst + (uint32_t)(u * 1024));
+    }
+  }
+  const bf16* vw = v_lds + 32 * w * D;
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dk[dt][e] = 0.f; dv[dt][e] = 0.f; }
+
+  // rows: the block's own tokens t0 .. blk_end-1 (G heads each), then the list
+  // (row counts and row ids fit 32 bits: T * hq < 2^31)
+  const int nself = (int)(blk_end - t0) * G;
+  int e_beg = 0, nsel_rows = 0;
+  if (a.ks > 0 && a.list_offsets) {
+    e_beg = a.list_offsets[L];
+    nsel_rows = a.list_offsets[L + 1] - e_beg;
+  }
+  const int nrows = nself + nsel_rows;
+  const int nch = (nrows + BRC - 1) / BRC;
+  const int row0 = (int)t0 * a.hq + g * G;   // row id of own row 0
+
+  const uint32_t rows_base = lds_addr(rows_lds);
+  auto issue_ent = [&](int c) __attribute__((always_inline)) {
+    const int cc = min(c, nch - 1);
+    const int idx = cc * BRC + (lane & 31) - nself;
+    const int32_t* src =
+        (nsel_rows > 0) ? a.entries + e_beg + min(max(idx, 0), nsel_rows - 1) : a.cu;
+    dma4(src, lds_addr(&ent_lds[c & 7][w][0]));
+  };
+  auto rowid_of = [&](int c, int r) __attribute__((always_inline)) -> int {
+    const int rr = min(c, nch - 1) * BRC + r;
+    if (rr < nself) {
+      const int tq = rr / G;
+      return row0 + tq * a.hq + (rr - tq * G);
+    }
+    if (rr < nrows) return ent_lds[c & 7][w][r] / a.ks;
+    return 0;   // padding: any valid row, masked out
+  };
+  const int rA = 4 * w + (lane >> 4);
+  const int offA = 8 * ((lane & 15) ^ swz(rA));
+  auto issue_rows = [&](int c) __attribute__((always_inline)) {
+    const int buf = c & 3;
+    const int ridA = rowid_of(c, rA);
+    const int ridM = rowid_of(c, lane & 31);
+    const uint32_t dst = rows_base + (uint32_t)((buf * RBUF + 4 * w * D) * 2);
+    dma16(q + (int64_t)ridA * D + offA, dst);
+    dma16(dout + (int64_t)ridA * D + offA, dst + (uint32_t)(CH * 2));
+    dma4((lane < 32) ? a.lse + ridM : a.delta + ridM, lds_addr(&meta_lds[buf][w][0]));
+  };
+
+  const int hx = half ^ swz(r32);
+  const int ml = lane & 15;
+  const int vrow = 4 * half + (ml >> 2);
+  const int vp = 2 * ((lane >> 4) & 1) + ((ml & 3) >> 1);
+  const int vx0 = vp ^ swz(vrow), vx1 = vp ^ swz(vrow + 8);
+  const int vbyte = (ml & 1) * 4;
+  const int mask_below = keyrel * G;   // own rows rr < keyrel * G come before the key
+
+  auto compute = [&](int c) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    const int rr0 = c * BRC;
+    // a chunk of own rows whose last token precedes the wave's first key
+    if (rr0 + BRC - 1 < nself && rr0 + BRC - 1 < 32 * w * G) return;
+    const bf16* qb = rows_lds + (c & 3) * RBUF;
+    const bf16* gb = qb + CH;
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 qa = load8(qb + r32 * D + 8 * ((2 * kk) ^ hx));
+      const bf16x8 ga = load8(gb + r32 * D + 8 * ((2 * kk) ^ hx));
+      const bf16x8 vb = load8(vw + r32 * D + 8 * ((2 * kk) ^ hx));
+      s = mma_k16(qa, kf[kk], s);
+      dp = mma_k16(ga, vb, dp);
+    }
+    // lane: key column r32 of wave w; item e: row 8(e/4) + 4half + e%4 of the chunk.
+    // P overwrites s, dS overwrites dp.
+    const float* mt = meta_lds[c & 3][w];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 l4 = *reinterpret_cast<const float4*>(mt + 8 * jj + 4 * half);
+      const float4 d4 = *reinterpret_cast<const float4*>(mt + 32 + 8 * jj + 4 * half);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * jj + u;
+        const int rr = rr0 + 8 * jj + 4 * half + u;
+        const bool masked = rr >= nrows || rr < mask_below;
+        const float p = masked ? 0.f : fast_exp2(fmaf(s[e], a.scale_log2, -lv[u] * kLog2e));
+        s[e] = p;
+        dp[e] = p * (dp[e] - dl[u]);
+      }
+    }
+    bf16x8 pf[2], df[2];
+    {
+      float t[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[e] = s[e];
+      pf[0] = pack8<bf16>(&t[0]);
+      pf[1] = pack8<bf16>(&t[8]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[e] = dp[e];
+      df[0] = pack8<bf16>(&t[0]);
+      df[1] = pack8<bf16>(&t[8]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const bf16x8 ga = tr_frag(gb, 16 * qq, dt, vrow, vx0, vx1, vbyte);
+        dv[dt] = mma_k16(ga, pf[qq], dv[dt]);
+        const bf16x8 qa = tr_frag(qb, 16 * qq, dt, vrow, vx0, vx1, vbyte);
+        dk[dt] = mma_k16(qa, df[qq], dk[dt]);
+      }
+  };
+
+  // the K fragments (compiler-visible loads) and the V rows land first
+  MOBA_WAIT_VM_LGKM0(0);
+  for (int c = 0; c < 5; ++c) issue_ent(c);
+  MOBA_WAIT_VM_LGKM0(0);
+  bare_barrier();
+  issue_rows(0);
+  issue_rows(1);
+  issue_rows(2);
+  MOBA_WAIT_VM_LGKM0(6);
+  bare_barrier();
+  for (int c = 0; c < nch; ++c) {
+    issue_ent(c + 5);
+    issue_rows(c + 3);
+    compute(c);
+    MOBA_WAIT_VM_LGKM0(7);
+    bare_barrier();
+  }
+  MOBA_WAIT_VM_LGKM0(0);
+
+  // epilogue: lane holds d{K,V}^T[32dt + 8(i/4) + 4half + i%4][key]
+  if (!key_ok) return;
+  typedef bf16 vec4_t __attribute__((ext_vector_type(4)));
+  bf16* dkp = (bf16*)a.dk + key * kstride + g * D;
+  bf16* dvp = (bf16*)a.dv + key * kstride + g * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const int d0 = 32 * dt + 8 * aa + 4 * half;
+      vec4_t rk, rv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rk[e] = (bf16)(dk[dt][4 * aa + e] * a.scale);
+        rv[e] = (bf16)dv[dt][4 * aa + e];
+      }
+      *reinterpret_cast<vec4_t*>(dkp + d0) = rk;
+      *reinterpret_cast<vec4_t*>(dvp + d0) = rv;
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out,
                              float* delta, hipStream_t s) {
@@ -497,7 +735,12 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    a.kvt = (p.block + DKV_WAVES * 32 - 1) / (DKV_WAVES * 32);
+    const int64_t lists8 = (p.nb * p.hkv + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_bwd_dkdv_dma, dim3((unsigned)(lists8 * a.kvt)), dim3(64 * DKV_WAVES), 0,
+                       s, a);
+  } else {
     a.kvt = (p.block + BKV_WAVES * 32 - 1) / (BKV_WAVES * 32);
     const int64_t tiles = p.nb * p.hkv * a.kvt;
     hipLaunchKernelGGL((k_bwd_dkdv<T, D>), dim3((unsigned)tiles), dim3(256), 0, s, a);

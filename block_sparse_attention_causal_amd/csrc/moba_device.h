@@ -173,4 +173,67 @@ __device__ __forceinline__ int vt_pos_of_group4(int kg) {
   return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit inputs: K and V chunks go straight from global memory into LDS with
+// gfx950's direct loads (global_load_lds_dwordx4: lane i's 16 bytes land at
+// base + 16 i), so no registers hold chunks in flight and three chunks can be
+// outstanding. Both are stored row-major, 256-byte rows (D = 128) of sixteen
+// 16-byte pieces; piece p of row r sits at position p ^ swz(r). gfx950's LDS
+// has 64 four-byte banks (one 256-byte row) and serves 16 lanes of a 16-byte
+// read, or 32 lanes of an 8-byte read, per clock. The K reads put 16
+// consecutive rows in one clock (swz must be a bijection on 0..15); the V^T
+// reads put four pieces of each of 4 consecutive rows in one clock (the four
+// rows must land in different piece quads). Transposing the row index's two
+// 2-bit halves satisfies both. V^T fragments are
+// read with ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte reads of lanes i/4, i/4+4, i/4+8, i/4+12, so
+// pointing the group at a 4-row x 16-column block of V gives lane i column i of
+// those four rows: four consecutive keys of one head dimension.
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One direct global->LDS load of 16 bytes per lane (lane i's bytes land at
+// lds + 16 i). Issued from inline assembly so that the compiler, unaware of
+// these LDS writes, does not pad every later LDS read with conservative waits;
+// the caller orders them with an explicit vmcnt wait and a barrier. No register
+// receives data, so nothing is left in flight in a register.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_lds_dwordx4 %1, off"
+               :
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
+               : "memory");
+#endif
+}
+
+// A bare s_barrier (the host pass of the compiler sees only an empty body).
+__device__ __forceinline__ void bare_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
+
+// s_waitcnt with vmcnt(n) (n < 64) and lgkmcnt(0), expcnt untouched (gfx9 encoding).
+#define MOBA_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+
+// One direct global->LDS load of 4 bytes per lane (lane i's dword lands at
+// lds + 4 i); same conventions as dma16.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_lds_dword %1, off"
+               :
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
+               : "memory");
+#endif
+}
+
 }  // namespace moba
