@@ -706,6 +706,218 @@ k_bwd_dkdv_dma(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dQ for 16-bit inputs with D = 128: k_bwd_dq's products and tiles, with the
+// forward's key pipeline (64-key chunks of K and V by direct loads into four
+// swizzled LDS buffers, three in flight, vmcnt(8) per iteration). K and V rows
+// are the A operands of S^T and dP^T; K^T fragments for dQ^T come from the same
+// K rows through ds_read_b64_tr_b16 in the key order of the dS^T registers.
+template <int MODE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_bwd_dq_dma(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 128;
+  constexpr int DBUF = 2 * BKC * D;              // K rows then V rows
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * DBUF];
+  const int64_t logical = xcd_logical(blockIdx.x, a.padded);
+  if (logical >= a.ntiles) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int group = a.hq / a.hkv;
+  const bf16* __restrict__ q = (const bf16*)a.q;
+  const bf16* __restrict__ k = (const bf16*)a.k;
+  const bf16* __restrict__ v = (const bf16*)a.v;
+  const bf16* __restrict__ dout = (const bf16*)a.dout;
+
+  int g;
+  int64_t kbeg, kend;
+  int64_t row = -1, dst_index = -1, wtok0 = 0;
+  bool wave_live;
+  int blk_i = 0;
+  if (MODE == BWD_SELECTED) {
+    const int64_t tile = logical;
+    const int32_t* toffs = a.tile_offsets;
+    if (tile >= toffs[a.nlists]) return;
+    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int64_t b = L / a.hkv;
+    g = L % a.hkv;
+    const int n = a.blk_seq[b], j = a.blk_local[b];
+    kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
+    kend = kbeg + a.block;
+    const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kRowsPerTile +
+                       (int64_t)w * kRowsPerWave;
+    const int64_t e1 = a.list_offsets[L + 1];
+    wave_live = e0 < e1;
+    if (e0 + r32 < e1) {
+      const int32_t ev = a.entries[e0 + r32];
+      dst_index = ev;
+      row = ev / a.ks;
+    }
+  } else {
+    const int tt = 32 * (8 / a.hg);
+    const int nhs = a.hq / a.hg;
+    const int u = a.nu - 1 - (int)(logical % a.nu);
+    const int64_t rest = logical / a.nu;
+    const int hs = (int)(rest % nhs);
+    const int64_t b = a.nb - 1 - rest / nhs;
+    const int n = a.blk_seq[b], i = a.blk_local[b];
+    blk_i = i;
+    const int64_t blk_start = (int64_t)a.cu[n] + (int64_t)i * a.block;
+    const int64_t blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
+    const int64_t tok0 = blk_start + (int64_t)u * tt;
+    if (tok0 >= blk_end) return;
+    const int h = hs * a.hg + (w % a.hg);
+    g = h / group;
+    wtok0 = tok0 + (int64_t)(w / a.hg) * 32;
+    wave_live = wtok0 < blk_end;
+    kbeg = blk_start;
+    kend = min(tok0 + tt, blk_end);
+    if (wtok0 + r32 < blk_end) {
+      row = (wtok0 + r32) * a.hq + h;
+      dst_index = row;
+    }
+  }
+
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qf[kk] = (row >= 0) ? load8_stream(q + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
+    gf[kk] = (row >= 0) ? load8_stream(dout + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
+  }
+  const float lse_l2 = (row >= 0) ? a.lse[row] * kLog2e : 0.f;
+  const float dlt = (row >= 0) ? a.delta[row] : 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  const int hx = half ^ swz(r32);
+  const int ml = lane & 15;
+  const int vrow = 4 * half + (ml >> 2);
+  const int vp = 2 * ((lane >> 4) & 1) + ((ml & 3) >> 1);
+  const int vx0 = vp ^ swz(vrow), vx1 = vp ^ swz(vrow + 8);
+  const int vbyte = (ml & 1) * 4;
+
+  auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
+    const bool needed = (MODE == BWD_SELECTED) ? wave_live : (wave_live && c0 <= wtok0 + 31);
+    if (!needed) return;
+    const bf16* kb = smem + buf * DBUF;
+    const bf16* vb = kb + BKC * D;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { s[kt][e] = 0.f; dp[kt][e] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 kf = load8(kb + (32 * kt + r32) * D + 8 * ((2 * kk) ^ hx));
+        s[kt] = mma_k16(kf, qf[kk], s[kt]);
+        const bf16x8 vf = load8(vb + (32 * kt + r32) * D + 8 * ((2 * kk) ^ hx));
+        dp[kt] = mma_k16(vf, gf[kk], dp[kt]);
+      }
+    const int64_t tok = wtok0 + r32;
+    const bool need_mask = (MODE == BWD_SELF && c0 + BKC - 1 > wtok0) || (c0 + BKC > kend);
+    bf16x8 df[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float dsv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t key = c0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+        const bool masked = need_mask && ((key >= kend) || (MODE == BWD_SELF && key > tok));
+        const float p = masked ? 0.f : fast_exp2(fmaf(s[kt][e], a.scale_log2, -lse_l2));
+        dsv[e] = p * (dp[kt][e] - dlt);
+      }
+      df[2 * kt] = pack8<bf16>(&dsv[0]);
+      df[2 * kt + 1] = pack8<bf16>(&dsv[8]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const bf16x8 kt_f = tr_frag(kb, 16 * qq, dt, vrow, vx0, vx1, vbyte);
+        acc[dt] = mma_k16(kt_f, df[qq], acc[dt]);
+      }
+  };
+
+  const int nch = (int)((kend - kbeg + BKC - 1) / BKC);
+  const int row_stride = a.hkv * D;
+  const uint32_t smem_lds = lds_addr(smem);
+  const int rowA = 8 * w + (lane >> 4), rowB = rowA + 4;
+  const int pieceA = (lane & 15) ^ swz(rowA), pieceB = (lane & 15) ^ swz(rowB);
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const int cc = min(c, nch - 1);
+    const int64_t c0 = kbeg + (int64_t)cc * BKC;
+    const int last = (int)min((int64_t)(BKC - 1), kend - 1 - c0);
+    const bf16* kp = k + (c0 * a.hkv + g) * D;
+    const bf16* vp2 = v + (c0 * a.hkv + g) * D;
+    const uint32_t dst = smem_lds + (uint32_t)((c & 3) * DBUF * 2 + 128 * w * 16);
+    const int offA = min(rowA, last) * row_stride + 8 * pieceA;
+    const int offB = min(rowB, last) * row_stride + 8 * pieceB;
+    dma16(kp + offA, dst);
+    dma16(kp + offB, dst + 1024u);
+    dma16(vp2 + offA, dst + (uint32_t)(BKC * D * 2));
+    dma16(vp2 + offB, dst + (uint32_t)(BKC * D * 2) + 1024u);
+  };
+  // the Q and dO fragments (compiler-visible loads) land before any direct load
+  MOBA_WAIT_VM_LGKM0(0);
+  issue(0);
+  issue(1);
+  issue(2);
+  MOBA_WAIT_VM_LGKM0(8);
+  bare_barrier();
+  for (int c = 0; c < nch; ++c) {
+    issue(c + 3);
+    compute(c & 3, kbeg + (int64_t)c * BKC);
+    MOBA_WAIT_VM_LGKM0(8);
+    bare_barrier();
+  }
+  MOBA_WAIT_VM_LGKM0(0);
+
+  // epilogue: lane holds dQ^T[32dt + 8(i/4) + 4half + i%4][row r32]
+  if (dst_index < 0) return;
+  if (MODE == BWD_SELECTED) {
+    float* dst = a.dq_sel + dst_index * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        float4 val = make_float4(acc[dt][4 * aa] * a.scale, acc[dt][4 * aa + 1] * a.scale,
+                                 acc[dt][4 * aa + 2] * a.scale, acc[dt][4 * aa + 3] * a.scale);
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
+      }
+  } else {
+    const int nsel = min(a.ks, blk_i);
+    typedef bf16 vec4_t __attribute__((ext_vector_type(4)));
+    bf16* dst = (bf16*)a.dq + dst_index * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        const int d0 = 32 * dt + 8 * aa + 4 * half;
+        float x[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) x[bb] = acc[dt][4 * aa + bb] * a.scale;
+        for (int sl = 0; sl < nsel; ++sl) {
+          const float4 pt = *reinterpret_cast<const float4*>(
+              a.dq_sel + (dst_index * a.ks + sl) * D + d0);
+          x[0] += pt.x;
+          x[1] += pt.y;
+          x[2] += pt.z;
+          x[3] += pt.w;
+        }
+        vec4_t r;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) r[bb] = (bf16)x[bb];
+        *reinterpret_cast<vec4_t*>(dst + d0) = r;
+      }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out,
                              float* delta, hipStream_t s) {
@@ -721,8 +933,11 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
   if (p.ks > 0 && p.nentries > 0) {
     a.ntiles = p.max_tiles;
     a.padded = (p.max_tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELECTED>), dim3((unsigned)a.padded), dim3(512), 0, s,
-                       a);
+    if constexpr (sizeof(T) == 2 && D == 128)
+      hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELECTED>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELECTED>), dim3((unsigned)a.padded), dim3(512), 0,
+                         s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -731,7 +946,10 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
     a.nu = (p.block + tt - 1) / tt;
     a.ntiles = p.nb * a.nu * (p.hq / p.hg);
     a.padded = (a.ntiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELF>), dim3((unsigned)a.padded), dim3(512), 0, s, a);
+    if constexpr (sizeof(T) == 2 && D == 128)
+      hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELF>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELF>), dim3((unsigned)a.padded), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
