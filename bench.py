@@ -28,7 +28,7 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 MFMA / vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 CONFIG_NAMES = {"tiny": "moba_fwd_tiny_2k_fp32", "llama32k": "moba_fwd_llama8b_32k",
                 "varlen131k": "moba_fwd_varlen_131k", "1m": "moba_fwd_1m",
-                "fine256k": "moba_fwd_fine_blocks_256k"}
+                "fine256k": "moba_fwd_fine_blocks_256k", "10m_shard": "moba_fwd_10m_head_shard"}
 
 
 def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):

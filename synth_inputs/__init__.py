@@ -33,7 +33,8 @@ import torch
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 # The five workloads: tiny fp32 check, a Llama-3.1-8B-shaped layer at 32K, a packed
-# varlen batch, one 1M-token sequence, and fine-grained blocks at 256K.
+# varlen batch, one 1M-token sequence, and fine-grained blocks at 256K; and the
+# per-GPU head shard of a 10M-token sequence.
 CONFIGS = {
     "tiny": dict(seqlens=[2048], hq=1, hkv=1, d=64, block=256, topk=3, dtype="f32"),
     "llama32k": dict(seqlens=[32768], hq=32, hkv=8, d=128, block=2048, topk=3, dtype="bf16"),
@@ -41,6 +42,10 @@ CONFIGS = {
                        topk=3, dtype="bf16"),
     "1m": dict(seqlens=[1048576], hq=32, hkv=8, d=128, block=2048, topk=3, dtype="bf16"),
     "fine256k": dict(seqlens=[262144], hq=32, hkv=8, d=128, block=512, topk=12, dtype="bf16"),
+    # one GPU's share of a 10M-token (10 x 2^20) layer of the same shape split by kv head
+    # over 8 GPUs: 4 q heads and their kv head, 5,120 blocks
+    "10m_shard": dict(seqlens=[10485760], hq=4, hkv=1, d=128, block=2048, topk=3,
+                      dtype="bf16"),
 }
 
 

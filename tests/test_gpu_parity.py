@@ -205,7 +205,7 @@ def test_hybrid_switch_runs_each_path():
 
 # --- full-size workloads, benchmark launch configuration, sampled rows --------
 
-FULL = ["llama32k", "varlen131k", "fine256k", "1m"]
+FULL = ["llama32k", "varlen131k", "fine256k", "1m", "10m_shard"]
 
 
 @pytest.mark.parametrize("name", FULL)
