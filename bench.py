@@ -64,10 +64,14 @@ def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
     }
 
 
+# the sources the attention kernels are built from (their launch code included)
+ATTN_SOURCES = ("attention.hip", "moba_device.h", "moba_plan.h")
+
+
 def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_attention_causal_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ATTN_SOURCES:
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]

@@ -25,9 +25,16 @@ KERNELS = {
     "attn_selected": r"k_attn<[^,]+, \d+, 1>|k_attnI\w+Li1EEEv",
     "attn_self": r"k_attn<[^,]+, \d+, 0>|k_attnI\w+Li0EEEv",
     "attn_dense": r"k_attn<[^,]+, \d+, 2>|k_attnI\w+Li2EEEv",
-    "gate": r"k_gate",
+    "gate": r"k_gate\b|k_gateI",
     "pool": r"k_pool",
-    "merge": r"k_merge",
+    "kbar_append": r"k_kbar_append",
+    "decode_gate": r"k_dec_gate",
+    "decode_part": r"k_dec_part",
+    "decode_merge": r"k_dec_merge",
+    "bwd_delta": r"k_bwd_delta",
+    "bwd_dq_selected": r"k_bwd_dq_dma<1>|k_bwd_dq_dmaILi1E|k_bwd_dq<[^>]*, 1>|k_bwd_dqI\w+Li1EEEv",
+    "bwd_dq_self": r"k_bwd_dq_dma<0>|k_bwd_dq_dmaILi0E|k_bwd_dq<[^>]*, 0>|k_bwd_dqI\w+Li0EEEv",
+    "bwd_dkdv": r"k_bwd_dkdv",
     "route_count": r"k_route_count",
     "route_lists": r"k_route_lists",
     "route_offsets": r"k_route_offsets",
