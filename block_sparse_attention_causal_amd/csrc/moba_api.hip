@@ -116,6 +116,15 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
   P.off_kbar = take(sizeof(float) * P.nb * P.hkv * P.d);
   P.off_kbar_split =
       take(P.dtype == MOBA_DTYPE_BF16 ? sizeof(bf16) * 3 * P.nb * P.hkv * P.d : 0);
+  P.off_kbar_err = take(sizeof(float) * P.nb * P.hkv);
+  P.off_gate_bound = take(sizeof(float) * nseq * P.hkv);
+  {
+    // the gate's tiling: 8 waves x 32 rows, HG heads of one group side by side
+    const int tt = 32 * (8 / P.hg);
+    const int64_t nu = P.block > 0 ? (P.block + tt - 1) / tt : 0;
+    P.gate_tiles = P.nb * nu * (P.hq / P.hg);
+  }
+  P.off_gate_flags = take(P.gate_tiles);
   if (P.ks > 0) {
     P.off_sel = take(sizeof(int32_t) * rows * P.ks);
     P.off_hist = take(sizeof(int32_t) * P.tri);
@@ -141,6 +150,9 @@ Work carve(const Plan& p, void* base) {
   w.blk_local = (int32_t*)(b + p.off_blk_local);
   w.kbar = (float*)(b + p.off_kbar);
   w.kbar_split = (bf16*)(b + p.off_kbar_split);
+  w.kbar_err = (float*)(b + p.off_kbar_err);
+  w.gate_bound = (float*)(b + p.off_gate_bound);
+  w.gate_flags = (uint8_t*)(b + p.off_gate_flags);
   if (p.ks > 0) {
     w.sel = (int32_t*)(b + p.off_sel);
     w.hist = (int32_t*)(b + p.off_hist);

@@ -40,7 +40,9 @@ struct Plan {
   int64_t max_tiles = 0;    // launch bound for the selected-block attention grid
   // workspace offsets (bytes); -1 when not used
   size_t off_blk_base = 0, off_tri_base = 0, off_blk_seq = 0, off_blk_local = 0;
-  size_t off_kbar = 0, off_kbar_split = 0, off_sel = 0;
+  size_t off_kbar = 0, off_kbar_split = 0, off_kbar_err = 0, off_gate_bound = 0;
+  size_t off_gate_flags = 0, off_sel = 0;
+  int64_t gate_tiles = 0;   // tiles of the gate grid (one screening flag each)
   size_t off_hist = 0, off_chunk_off = 0, off_list_count = 0, off_list_offsets = 0;
   size_t off_tile_offsets = 0, off_entries = 0;
   size_t off_o_sel = 0, off_lse_sel = 0;
@@ -61,6 +63,9 @@ struct Work {
   int32_t* blk_local;    // [nb] index of each global block inside its sequence
   float* kbar;           // [nb, hkv, d] pooled keys
   bf16* kbar_split;      // [3, nb, hkv, d] pooled keys as hi + mid + lo bf16 (bf16 inputs)
+  float* kbar_err;       // [nb, hkv] error bound of the hi term of each pooled key (bf16)
+  float* gate_bound;     // [nseq, hkv] max of kbar_err over the sequence's blocks
+  uint8_t* gate_flags;   // [gate_tiles] 1: a row of the tile needs the exact gate
   int32_t* sel;          // [T, hq, ks] selected blocks
   int32_t* hist;         // [tri] per (query block, kv-head) counts per past block
   int32_t* chunk_off;    // [tri] start of each (query block, kv-head) inside each list

@@ -143,8 +143,10 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
                                               const int32_t* __restrict__ blk_seq,
                                               const int32_t* __restrict__ blk_local, int hkv,
                                               int block, int64_t nb, float* __restrict__ kbar,
-                                              bf16* __restrict__ kbar_split) {
+                                              bf16* __restrict__ kbar_split,
+                                              float* __restrict__ kbar_err) {
   __shared__ float red[256 / (D / (16 / sizeof(T)))][D + 1];
+  __shared__ float err_part[2][D / 64];
   const int64_t b = blockIdx.x / hkv;
   const int g = blockIdx.x % hkv;
   const int n = blk_seq[b];
@@ -165,6 +167,29 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ k,
       kbar_split[o] = hi;
       kbar_split[part + o] = mid;
       kbar_split[2 * part + o] = (bf16)r2;
+      // |mean - hi|^2 and |mean|^2 over the head dimension, per wave then
+      // across the D / 64 waves that hold channels
+      float e2 = r1 * r1, m2 = mean * mean;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        e2 += __shfl_xor(e2, off, 64);
+        m2 += __shfl_xor(m2, off, 64);
+      }
+      if ((c & 63) == 0) {
+        err_part[0][c >> 6] = e2;
+        err_part[1][c >> 6] = m2;
+      }
+    }
+  }
+  if (kbar_split) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float e2 = 0.f, m2 = 0.f;
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) { e2 += err_part[0][u]; m2 += err_part[1][u]; }
+      // the hi term's error |mean - hi| plus a bound of the fp32 accumulation
+      // of a D-term product (D 2^-24 relative, covered by 2^-16)
+      kbar_err[b * hkv + g] = sqrtf(e2) * (1.f + 0x1p-10f) + sqrtf(m2) * 0x1p-16f;
     }
   }
 }
@@ -174,20 +199,21 @@ hipError_t launch_pool(const Plan& p, const void* k, const int32_t* cu_dev, cons
   if (p.nb == 0) return hipSuccess;
   dim3 grid((unsigned)(p.nb * p.hkv));
   bf16* split = (p.dtype == MOBA_DTYPE_BF16) ? w.kbar_split : nullptr;
+  float* err = w.kbar_err;
   if (p.dtype == MOBA_DTYPE_BF16) {
     if (p.d == 128)
       hipLaunchKernelGGL((k_pool<bf16, 128>), grid, dim3(256), 0, s, (const bf16*)k, cu_dev,
-                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split, err);
     else
       hipLaunchKernelGGL((k_pool<bf16, 64>), grid, dim3(256), 0, s, (const bf16*)k, cu_dev,
-                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split, err);
   } else {
     if (p.d == 128)
       hipLaunchKernelGGL((k_pool<float, 128>), grid, dim3(256), 0, s, (const float*)k, cu_dev,
-                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split, err);
     else
       hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, s, (const float*)k, cu_dev,
-                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split);
+                         w.blk_seq, w.blk_local, p.hkv, p.block, p.nb, kbar, split, err);
   }
   return hipGetLastError();
 }
@@ -280,7 +306,8 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
                                               const int32_t* __restrict__ blk_local,
                                               const T* __restrict__ kparts, int64_t nb, int hq,
                                               int hkv, int hg, int block, int ks, int64_t ntiles,
-                                              int64_t padded, int32_t* __restrict__ sel) {
+                                              int64_t padded, const uint8_t* __restrict__ flags,
+                                              int32_t* __restrict__ sel) {
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LD = D + PAD;
   constexpr int VEC = 16 / sizeof(T);
@@ -288,6 +315,7 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
 
   const int64_t logical = xcd_logical(blockIdx.x, padded);
   if (logical >= ntiles) return;
+  if (flags && flags[logical] == 0) return;   // the screened selection is already exact
   const int tt = 32 * (8 / hg);                       // tokens per workgroup tile
   const int nu = (block + tt - 1) / tt;
   const int nhs = hq / hg;
@@ -440,20 +468,230 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
     if (p < ks) dst[p] = (sj[p] == kNoBlock) ? -1 : sj[p];
 }
 
+// Screened gate (bf16): one matrix-core pass over the hi term of the pooled
+// keys gives s~_j = q . hi(Kbar_j) with |s_j - s~_j| <= |q| * err_j, err_j the
+// bound the pool kernel stored (|Kbar_j - hi_j| plus the fp32 accumulation
+// term). With E = |q| * max_j err_j over the sequence, if the k-th best and
+// the (k+1)-th best s~ differ by more than 2E, then every kept block's exact
+// score exceeds every other block's, and the kept set is exactly that of the
+// exact scores. Rows where this fails (or where two s~ tie across the cut)
+// flag their tile, and the exact three-pass kernel recomputes flagged tiles
+// only. Tiles, lists and outputs as in k_gate; lists hold ks + 1 entries.
+__global__ void __launch_bounds__(256) k_gate_bound(const int32_t* __restrict__ blk_base,
+                                                    const float* __restrict__ kbar_err, int hkv,
+                                                    float* __restrict__ bound) {
+  __shared__ float red[4];
+  const int n = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  const int b0 = blk_base[n], b1 = blk_base[n + 1];
+  float m = 0.f;
+  for (int b = b0 + (int)threadIdx.x; b < b1; b += 256) m = vmax(m, kbar_err[(int64_t)b * hkv + g]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = vmax(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) bound[blockIdx.x] = vmax(vmax(red[0], red[1]), vmax(red[2], red[3]));
+}
+
+template <int D, int KB>
+__global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
+                                                   const int32_t* __restrict__ cu,
+                                                   const int32_t* __restrict__ blk_base,
+                                                   const int32_t* __restrict__ blk_seq,
+                                                   const int32_t* __restrict__ blk_local,
+                                                   const bf16* __restrict__ khi,
+                                                   const float* __restrict__ bound, int64_t nb,
+                                                   int hq, int hkv, int hg, int block, int ks,
+                                                   int64_t ntiles, int64_t padded,
+                                                   uint8_t* __restrict__ flags,
+                                                   int32_t* __restrict__ sel) {
+  constexpr int PAD = 8;
+  constexpr int LD = D + PAD;
+  constexpr int VEC = 8;
+  __shared__ __attribute__((aligned(16))) bf16 kb[2][32][LD];
+
+  const int64_t logical = xcd_logical(blockIdx.x, padded);
+  if (logical >= ntiles) return;
+  const int tt = 32 * (8 / hg);
+  const int nu = (block + tt - 1) / tt;
+  const int nhs = hq / hg;
+  const int u = (int)(logical % nu);
+  const int64_t rest = logical / nu;
+  const int64_t b = nb - 1 - (rest % nb);
+  const int hs = (int)(rest / nb);
+  const int n = blk_seq[b];
+  const int i = blk_local[b];
+  const int64_t seq0 = cu[n];
+  const int64_t blk_end = min(seq0 + (int64_t)(i + 1) * block, (int64_t)cu[n + 1]);
+  const int64_t tok0 = seq0 + (int64_t)i * block + (int64_t)u * tt;
+  if (tok0 >= blk_end || hs >= nhs) {
+    if (threadIdx.x == 0) flags[logical] = 0;
+    return;
+  }
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int h = hs * hg + (w % hg);
+  const int g = h / (hq / hkv);
+  const int64_t tok = tok0 + (int64_t)(w / hg) * 32 + r32;
+  const bool row_ok = tok < blk_end;
+  const int64_t row = tok * hq + h;
+  const int kl = ks + 1;                 // list length: the kept blocks and the next one
+
+  float bs[KB];
+  int bj[KB];
+#pragma unroll
+  for (int p = 0; p < KB; ++p) { bs[p] = -INFINITY; bj[p] = kNoBlock; }
+  bool unsure = false;
+
+  if (i > 0) {
+    bf16x8 qf[D / 16];
+    float qq = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = row_ok ? load8(q + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qq = fmaf((float)qf[kk][e], (float)qf[kk][e], qq);
+    }
+    const float qnorm = sqrtf(qq + swap_half(qq));
+    const int64_t gbase = blk_base[n];
+    float ws = -INFINITY;
+    constexpr int PIECES = 32 * (D / VEC);
+    constexpr int PPT = (PIECES + 511) / 512;
+    typedef bf16 vec_t __attribute__((ext_vector_type(VEC)));
+    vec_t pre[PPT];
+    auto fetch = [&](int j0) {
+#pragma unroll
+      for (int r = 0; r < PPT; ++r) {
+        const int pc = threadIdx.x + 512 * r;
+        if (PIECES % 512 == 0 || pc < PIECES) {
+          const int rr = pc / (D / VEC);
+          const int col = pc % (D / VEC);
+          const int jj = min(j0 + rr, i - 1);
+          pre[r] = *reinterpret_cast<const vec_t*>(khi + ((gbase + jj) * hkv + g) * D + col * VEC);
+        }
+      }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int r = 0; r < PPT; ++r) {
+        const int pc = threadIdx.x + 512 * r;
+        if (PIECES % 512 == 0 || pc < PIECES) {
+          const int rr = pc / (D / VEC);
+          const int col = pc % (D / VEC);
+          *reinterpret_cast<vec_t*>(&kb[buf][rr][col * VEC]) = pre[r];
+        }
+      }
+    };
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    int buf = 0;
+    for (int j0 = 0; j0 < i; j0 += 32) {
+      if (j0 + 32 < i) fetch(j0 + 32);
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        acc = mma_k16(load8(&kb[buf][r32][16 * kk + 8 * half]), qf[kk], acc);
+      if (j0 + 32 > i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int e = 1; e < 16; e += 2)
+        mx = (e + 1 < 16) ? vmax(vmax(mx, acc[e]), acc[e + 1]) : vmax(mx, acc[e]);
+      if (mx > ws) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (acc[e] > ws) {
+            list_insert<KB>(bs, bj, kl, acc[e], j0 + 8 * (e >> 2) + 4 * half + (e & 3));
+#pragma unroll
+            for (int p = 0; p < KB; ++p)
+              if (p == kl - 1) ws = bs[p];
+          }
+        }
+      }
+      if (j0 + 32 < i) stash(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+    float os[KB];
+    int oj[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) { os[p] = swap_half(bs[p]); oj[p] = swap_half(bj[p]); }
+#pragma unroll
+    for (int p = 0; p < KB; ++p)
+      if (p < kl && oj[p] != kNoBlock) list_insert<KB>(bs, bj, kl, os[p], oj[p]);
+    // the cut: entry ks - 1 (last kept) against entry ks (best left out)
+    if (row_ok && i > ks) {
+      float s_in = 0.f, s_out = 0.f;
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        if (p == ks - 1) s_in = bs[p];
+        if (p == ks) s_out = bs[p];
+      }
+      const float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
+      unsure = !(s_in - s_out > e2);
+    }
+  }
+  const int any = __syncthreads_or(unsure ? 1 : 0);
+  if (threadIdx.x == 0) flags[logical] = any ? 1 : 0;
+  if (!row_ok || half != 0) return;
+  int sj[KB];
+#pragma unroll
+  for (int p = 0; p < KB; ++p) sj[p] = kNoBlock;
+#pragma unroll
+  for (int p = 0; p < KB; ++p) {
+    if (p < ks) {
+      int j = bj[p];
+#pragma unroll
+      for (int r = 0; r < KB; ++r) {
+        if (r < ks) {
+          const bool lt = j < sj[r];
+          const int t = sj[r];
+          sj[r] = lt ? j : t;
+          j = lt ? t : j;
+        }
+      }
+    }
+  }
+  int32_t* dst = sel + row * ks;
+#pragma unroll
+  for (int p = 0; p < KB; ++p)
+    if (p < ks) dst[p] = (sj[p] == kNoBlock) ? -1 : sj[p];
+}
+
 template <typename T, int D, int NP>
 static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const Work& w,
-                             const T* parts, int32_t* sel, hipStream_t s, int64_t ntiles,
-                             int64_t padded) {
+                             const T* parts, const uint8_t* flags, int32_t* sel, hipStream_t s,
+                             int64_t ntiles, int64_t padded) {
   dim3 grid((unsigned)padded), blk(512);
 #define MOBA_GATE(KBV)                                                                        \
   hipLaunchKernelGGL((k_gate<T, D, NP, KBV>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,  \
                      w.blk_local, parts, p.nb, p.hq, p.hkv, p.hg, p.block, p.ks, ntiles,     \
-                     padded, sel)
+                     padded, flags, sel)
   if (p.ks <= 2) MOBA_GATE(2);
   else if (p.ks <= 4) MOBA_GATE(4);
   else if (p.ks <= 8) MOBA_GATE(8);
   else MOBA_GATE(16);
 #undef MOBA_GATE
+}
+
+template <int D>
+static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, const Work& w,
+                               int32_t* sel, hipStream_t s, int64_t ntiles, int64_t padded) {
+  dim3 grid((unsigned)padded), blk(512);
+#define MOBA_GATE_FAST(KBV)                                                                     \
+  hipLaunchKernelGGL((k_gate_fast<D, KBV>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,      \
+                     w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
+                     p.ks, ntiles, padded, w.gate_flags, sel)
+  if (p.ks + 1 <= 4) MOBA_GATE_FAST(4);
+  else if (p.ks + 1 <= 8) MOBA_GATE_FAST(8);
+  else MOBA_GATE_FAST(16);
+#undef MOBA_GATE_FAST
 }
 
 hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, const Work& w,
@@ -464,19 +702,31 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
   const int64_t ntiles = p.nb * nu * (p.hq / p.hg);
   const int64_t padded = (ntiles + 7) / 8 * 8;
   if (p.dtype == MOBA_DTYPE_BF16) {
+    // screened single pass, then the exact three-pass gate on flagged tiles only
+    // (lists of ks + 1 entries hold at most 16)
+    const bool screen = p.ks + 1 <= 16;
+    const uint8_t* flags = screen ? w.gate_flags : nullptr;
+    if (screen) {
+      hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
+                         w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
+      if (p.d == 128)
+        gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+      else
+        gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+    }
     if (p.d == 128)
-      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, sel, s, ntiles,
-                                     padded);
+      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, flags, sel, s,
+                                     ntiles, padded);
     else
-      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, sel, s, ntiles,
-                                    padded);
+      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, flags, sel, s,
+                                    ntiles, padded);
   } else {
     if (p.d == 128)
-      gate_dispatch_kb<float, 128, 1>(p, (const float*)q, cu_dev, w, w.kbar, sel, s, ntiles,
-                                      padded);
+      gate_dispatch_kb<float, 128, 1>(p, (const float*)q, cu_dev, w, w.kbar, nullptr, sel, s,
+                                      ntiles, padded);
     else
-      gate_dispatch_kb<float, 64, 1>(p, (const float*)q, cu_dev, w, w.kbar, sel, s, ntiles,
-                                     padded);
+      gate_dispatch_kb<float, 64, 1>(p, (const float*)q, cu_dev, w, w.kbar, nullptr, sel, s,
+                                     ntiles, padded);
   }
   return hipGetLastError();
 }
