@@ -279,9 +279,11 @@ __device__ __forceinline__ bool better(float s1, int j1, float s2, int j2) {
   return s1 > s2 || (s1 == s2 && j1 < j2);
 }
 
+// Inserts (s, j) into the sorted list of ks entries; returns the score that
+// ends up outside the list (the evicted last entry, or s itself).
 template <int KB>
-__device__ __forceinline__ void list_insert(float (&bs)[KB], int (&bj)[KB], int ks, float s,
-                                            int j) {
+__device__ __forceinline__ float list_insert(float (&bs)[KB], int (&bj)[KB], int ks, float s,
+                                             int j) {
 #pragma unroll
   for (int p = 0; p < KB; ++p) {
     if (p < ks) {
@@ -294,6 +296,7 @@ __device__ __forceinline__ void list_insert(float (&bs)[KB], int (&bj)[KB], int 
       j = b ? tj : j;
     }
   }
+  return s;
 }
 
 constexpr int kNoBlock = 0x7fffffff;
@@ -504,10 +507,15 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
                                                    int64_t ntiles, int64_t padded,
                                                    uint8_t* __restrict__ flags,
                                                    int32_t* __restrict__ sel) {
-  constexpr int PAD = 8;
-  constexpr int LD = D + PAD;
-  constexpr int VEC = 8;
-  __shared__ __attribute__((aligned(16))) bf16 kb[2][32][LD];
+  // Pooled hi keys stream through an LDS ring of GB buffers (32 blocks each,
+  // rows of D bf16 in 16-byte pieces, piece p of row r at p ^ swz(r) as in the
+  // attention kernels) by direct loads, GB - 1 chunks in flight: each thread
+  // issues exactly one 16-byte load per chunk (clamped past the end; with
+  // D = 64 the upper half of a buffer holds unused rows), so "chunk s+1 has
+  // landed" is vmcnt(GB - 2) at the end of iteration s.
+  constexpr int GB = 8;
+  constexpr int KBUF = 512 * 8;                       // bf16 per buffer: 512 16-byte slots
+  __shared__ __attribute__((aligned(16))) bf16 kb[GB][KBUF];
 
   const int64_t logical = xcd_logical(blockIdx.x, padded);
   if (logical >= ntiles) return;
@@ -535,106 +543,111 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
   const int64_t tok = tok0 + (int64_t)(w / hg) * 32 + r32;
   const bool row_ok = tok < blk_end;
   const int64_t row = tok * hq + h;
-  const int kl = ks + 1;                 // list length: the kept blocks and the next one
 
+  // the top-ks list as in k_gate, plus the best score left out of it
   float bs[KB];
   int bj[KB];
 #pragma unroll
   for (int p = 0; p < KB; ++p) { bs[p] = -INFINITY; bj[p] = kNoBlock; }
+  float out_max = -INFINITY;
   bool unsure = false;
 
   if (i > 0) {
     bf16x8 qf[D / 16];
-    float qq = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = row_ok ? load8(q + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qq = fmaf((float)qf[kk][e], (float)qf[kk][e], qq);
-    }
-    const float qnorm = sqrtf(qq + swap_half(qq));
     const int64_t gbase = blk_base[n];
-    float ws = -INFINITY;
-    constexpr int PIECES = 32 * (D / VEC);
-    constexpr int PPT = (PIECES + 511) / 512;
-    typedef bf16 vec_t __attribute__((ext_vector_type(VEC)));
-    vec_t pre[PPT];
-    auto fetch = [&](int j0) {
-#pragma unroll
-      for (int r = 0; r < PPT; ++r) {
-        const int pc = threadIdx.x + 512 * r;
-        if (PIECES % 512 == 0 || pc < PIECES) {
-          const int rr = pc / (D / VEC);
-          const int col = pc % (D / VEC);
-          const int jj = min(j0 + rr, i - 1);
-          pre[r] = *reinterpret_cast<const vec_t*>(khi + ((gbase + jj) * hkv + g) * D + col * VEC);
-        }
-      }
+    const int nsteps = (i + 31) / 32;
+    const uint32_t kb_lds = lds_addr(&kb[0][0]);
+    constexpr int PIECES_ROW = D / 8;
+    const int slot = threadIdx.x;                        // 16-byte slot in a buffer
+    const int srow = slot / PIECES_ROW;
+    const int spiece = (slot % PIECES_ROW) ^ (swz(srow) & (PIECES_ROW - 1));
+    auto issue = [&](int st) __attribute__((always_inline)) {
+      const int jj = min(min(st, nsteps - 1) * 32 + srow, i - 1);
+      dma16(khi + ((gbase + jj) * hkv + g) * D + 8 * spiece,
+            kb_lds + (uint32_t)(((st % GB) * KBUF + 8 * (threadIdx.x - lane)) * 2));
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-      for (int r = 0; r < PPT; ++r) {
-        const int pc = threadIdx.x + 512 * r;
-        if (PIECES % 512 == 0 || pc < PIECES) {
-          const int rr = pc / (D / VEC);
-          const int col = pc % (D / VEC);
-          *reinterpret_cast<vec_t*>(&kb[buf][rr][col * VEC]) = pre[r];
-        }
-      }
-    };
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    int buf = 0;
-    for (int j0 = 0; j0 < i; j0 += 32) {
-      if (j0 + 32 < i) fetch(j0 + 32);
-      f32x16 acc;
+    const int rx = swz(r32) & (PIECES_ROW - 1);
+    // S~^T of chunk st (the LDS buffer holds it), blocks >= i set to -inf
+    auto scores = [&](int st, f32x16& acc) __attribute__((always_inline)) {
+      const bf16* kr = &kb[st % GB][r32 * D];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        acc = mma_k16(load8(&kb[buf][r32][16 * kk + 8 * half]), qf[kk], acc);
+        acc = mma_k16(load8(kr + 8 * (((2 * kk) | half) ^ rx)), qf[kk], acc);
+      const int j0 = st * 32;
       if (j0 + 32 > i) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
       }
-      float mx = acc[0];
+    };
+    auto max16 = [](const f32x16& acc) __attribute__((always_inline)) {
+      float m = acc[0];
 #pragma unroll
       for (int e = 1; e < 16; e += 2)
-        mx = (e + 1 < 16) ? vmax(vmax(mx, acc[e]), acc[e + 1]) : vmax(mx, acc[e]);
+        m = (e + 1 < 16) ? vmax(vmax(m, acc[e]), acc[e + 1]) : vmax(m, acc[e]);
+      return m;
+    };
+    // Every score either enters the list (and whatever it evicts is left out)
+    // or is left out at once, so out_max ends as the best score not kept.
+    float ws = -INFINITY;
+    MOBA_WAIT_VM_LGKM0(0);                 // Q before any direct load
+    for (int st = 0; st < GB - 1; ++st) issue(st);
+    MOBA_WAIT_VM_LGKM0(GB - 2);
+    bare_barrier();
+    for (int st = 0; st < nsteps; ++st) {
+      issue(st + GB - 1);
+      f32x16 acc;
+      scores(st, acc);
+      const float mx = max16(acc);
       if (mx > ws) {
+        const int j0 = st * 32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           if (acc[e] > ws) {
-            list_insert<KB>(bs, bj, kl, acc[e], j0 + 8 * (e >> 2) + 4 * half + (e & 3));
+            out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, acc[e],
+                                                    j0 + 8 * (e >> 2) + 4 * half + (e & 3)));
 #pragma unroll
             for (int p = 0; p < KB; ++p)
-              if (p == kl - 1) ws = bs[p];
+              if (p == ks - 1) ws = bs[p];
+          } else {
+            out_max = vmax(out_max, acc[e]);
           }
         }
+      } else {
+        out_max = vmax(out_max, mx);
       }
-      if (j0 + 32 < i) stash(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
+      MOBA_WAIT_VM_LGKM0(GB - 2);
+      bare_barrier();
     }
+    MOBA_WAIT_VM_LGKM0(0);
     float os[KB];
     int oj[KB];
 #pragma unroll
     for (int p = 0; p < KB; ++p) { os[p] = swap_half(bs[p]); oj[p] = swap_half(bj[p]); }
+    out_max = vmax(out_max, swap_half(out_max));
 #pragma unroll
     for (int p = 0; p < KB; ++p)
-      if (p < kl && oj[p] != kNoBlock) list_insert<KB>(bs, bj, kl, os[p], oj[p]);
-    // the cut: entry ks - 1 (last kept) against entry ks (best left out)
+      if (p < ks && oj[p] != kNoBlock)
+        out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, os[p], oj[p]));
+    // the cut: the last kept entry against the best score left out
     if (row_ok && i > ks) {
-      float s_in = 0.f, s_out = 0.f;
+      float s_in = 0.f;
 #pragma unroll
-      for (int p = 0; p < KB; ++p) {
+      for (int p = 0; p < KB; ++p)
         if (p == ks - 1) s_in = bs[p];
-        if (p == ks) s_out = bs[p];
-      }
+      float qq = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 16; ++e)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) qq = fmaf((float)qf[e][x], (float)qf[e][x], qq);
+      const float qnorm = sqrtf(qq + swap_half(qq));
       const float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
-      unsure = !(s_in - s_out > e2);
+      unsure = !(s_in - out_max > e2);
     }
   }
   const int any = __syncthreads_or(unsure ? 1 : 0);
@@ -688,8 +701,9 @@ static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, 
   hipLaunchKernelGGL((k_gate_fast<D, KBV>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,      \
                      w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
                      p.ks, ntiles, padded, w.gate_flags, sel)
-  if (p.ks + 1 <= 4) MOBA_GATE_FAST(4);
-  else if (p.ks + 1 <= 8) MOBA_GATE_FAST(8);
+  if (p.ks <= 2) MOBA_GATE_FAST(2);
+  else if (p.ks <= 4) MOBA_GATE_FAST(4);
+  else if (p.ks <= 8) MOBA_GATE_FAST(8);
   else MOBA_GATE_FAST(16);
 #undef MOBA_GATE_FAST
 }
@@ -702,24 +716,18 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
   const int64_t ntiles = p.nb * nu * (p.hq / p.hg);
   const int64_t padded = (ntiles + 7) / 8 * 8;
   if (p.dtype == MOBA_DTYPE_BF16) {
-    // screened single pass, then the exact three-pass gate on flagged tiles only
-    // (lists of ks + 1 entries hold at most 16)
-    const bool screen = p.ks + 1 <= 16;
-    const uint8_t* flags = screen ? w.gate_flags : nullptr;
-    if (screen) {
-      hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
-                         w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
-      if (p.d == 128)
-        gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
-      else
-        gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+    // screened single bf16 pass, then the exact three-pass gate on flagged tiles only
+    hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
+                       w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
+    if (p.d == 128) {
+      gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, w.gate_flags,
+                                     sel, s, ntiles, padded);
+    } else {
+      gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, w.gate_flags,
+                                    sel, s, ntiles, padded);
     }
-    if (p.d == 128)
-      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, flags, sel, s,
-                                     ntiles, padded);
-    else
-      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, flags, sel, s,
-                                    ntiles, padded);
   } else {
     if (p.d == 128)
       gate_dispatch_kb<float, 128, 1>(p, (const float*)q, cu_dev, w, w.kbar, nullptr, sel, s,
