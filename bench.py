@@ -319,8 +319,10 @@ def main():
         elif name == "gate":
             gbs = work["gate_bytes"] / (avg * 1e-3) / 1e9
             tf = work["gate_flop"] / (avg * 1e-3) / 1e12
+            # one bf16 matrix-core pass per score (the screened gate; flagged tiles
+            # add three more): both the HBM and the matrix-core fraction
             rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
-                       achieved_tflops=tf)
+                       achieved_tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
         elif name == "pool":
             gbs = work[name + "_bytes"] / (avg * 1e-3) / 1e9
             rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)

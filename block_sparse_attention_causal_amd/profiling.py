@@ -25,6 +25,8 @@ KERNELS = {
     "attn_selected": r"k_attn<[^,]+, \d+, 1>|k_attnI\w+Li1EEEv",
     "attn_self": r"k_attn<[^,]+, \d+, 0>|k_attnI\w+Li0EEEv",
     "attn_dense": r"k_attn<[^,]+, \d+, 2>|k_attnI\w+Li2EEEv",
+    "gate_fast": r"k_gate_fast",
+    "gate_bound": r"k_gate_bound",
     "gate": r"k_gate\b|k_gateI",
     "pool": r"k_pool",
     "kbar_append": r"k_kbar_append",

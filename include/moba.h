@@ -150,7 +150,10 @@ moba_status_t moba_attention_forward(int32_t mode, const void* q, const void* k,
  *   out, lse:  the forward's out and lse_out ([T, Hq, D] input dtype; fp32
  *              [T, Hq]) for these q, k, v.
  *   dout:      [T, Hq, D] input dtype.
- *   sel:       the forward's sel_out, int32 [T, Hq, topk-1] (unused when topk == 1).
+ *   sel:       the forward's sel_out, int32 [T, Hq, topk-1] (unused when topk == 1),
+ *              for the same q, k, block_size and topk. Other contents give
+ *              meaningless gradients (ids outside a row's past blocks are
+ *              ignored, so nothing is accessed out of bounds).
  *   dq: [T, Hq, D]; dk, dv: [T, Hkv, D] (input dtype), written in full.
  *   workspace: at least moba_backward_workspace_bytes(...), 256-byte aligned.
  * Same shapes and limits as moba_forward. */

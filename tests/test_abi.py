@@ -236,3 +236,22 @@ def test_backward_workspace_holds_dq_parts_and_delta(lib):
     assert n >= rows * 2 * 128 * 4 + rows * 4
     assert n >= moba.moba_workspace_bytes([0, 32768], 32, 8, 128, torch.bfloat16, 2048, 3) - \
         rows * 2 * 128 * 2
+
+
+def test_profiling_kernel_keys():
+    from block_sparse_attention_causal_amd.profiling import kernel_key
+    names = {
+        "_ZN4moba6k_attnIDF16bLi128ELi1EEEvNS_8AttnArgsE": "attn_selected",
+        "_ZN4moba6k_attnIDF16bLi128ELi0EEEvNS_8AttnArgsE": "attn_self",
+        "_ZN4moba6k_attnIDF16bLi128ELi2EEEvNS_8AttnArgsE": "attn_dense",
+        "_ZN4moba6k_gateIDF16bLi128ELi3ELi2EEEvPKT_PKiS5_S5_S5_S3_liiiiillPKhPi": "gate",
+        "_ZN4moba11k_gate_fastILi128ELi2EEEvPKDF16bPKiS4_S4_S4_S2_PKfliiiiillPhPi": "gate_fast",
+        "moba::k_gate_bound(int const*, float const*, int, float*)": "gate_bound",
+        "void moba::k_bwd_dq_dma<1>(moba::BwdArgs)": "bwd_dq_selected",
+        "void moba::k_bwd_dq_dma<0>(moba::BwdArgs)": "bwd_dq_self",
+        "moba::k_bwd_dkdv_dma(moba::BwdArgs)": "bwd_dkdv",
+        "_ZN4moba10k_dec_partIDF16bLi128EEEvNS_10DecodeArgsE": "decode_part",
+        "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel": "copy_calibration",
+    }
+    for name, key in names.items():
+        assert kernel_key(name) == key, name
