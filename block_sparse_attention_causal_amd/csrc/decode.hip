@@ -19,6 +19,24 @@ namespace moba {
 
 constexpr int kSeg = 512;   // keys per attention work item
 
+// Sum over aligned groups of LANES (4, 8 or 16) lanes with DPP lane moves on
+// the vector ALU (quad permutations, then the half-row and row mirrors)
+// instead of LDS permutes: every lane of a group ends with the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                CTRL, 0xF, 0xF, true));
+}
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "groups of 4, 8 or 16 lanes");
+  x += dpp_move<0xB1>(x);                        // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_move<0x4E>(x);                        // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LANES >= 8) x += dpp_move<0x141>(x);   // row_half_mirror: the other quad
+  if constexpr (LANES >= 16) x += dpp_move<0x140>(x);  // row_mirror: the other half-row
+  return x;
+}
+
 // Sequence and in-sequence position of new row r.
 __device__ __forceinline__ void decode_row(const DecodeArgs& a, int64_t r, int& n, int64_t& p) {
   n = seq_of_token(a.cu_q, a.nseq, r);
@@ -141,7 +159,7 @@ __global__ void __launch_bounds__(256) k_dec_gate(DecodeArgs a) {
 // over 64-key chunks. Writes the segment's normalised output and its natural
 // log-sum-exp (-inf for an empty segment).
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_dec_part(DecodeArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 3))) k_dec_part(DecodeArgs a) {
   constexpr int LPK = D / 8;      // lanes per key row, 8 values each
   constexpr int KPS = 64 / LPK;   // keys per step
   constexpr int NS = 64 / KPS;    // steps per 64-key chunk
@@ -190,17 +208,26 @@ __global__ void __launch_bounds__(256) k_dec_part(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int64_t c0 = 0; c0 < len; c0 += 64) {
+    // all of the chunk's K and V pieces of this lane in flight at once (keys
+    // past the segment end are clamped, always in range, and masked below)
+    vec8 kx[NS], vx[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int64_t kk = min(c0 + kl + KPS * s, len - 1);
+      kx[s] = *reinterpret_cast<const vec8*>(kbase + kk * stride);
+      vx[s] = *reinterpret_cast<const vec8*>(vbase + kk * stride);
+    }
+    // keep the loads ahead of their uses (16-bit inputs; fp32 pieces are twice
+    // the registers, so there the compiler keeps its own order)
+    if constexpr (sizeof(T) == 2) __builtin_amdgcn_sched_barrier(0);
     float sc[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int64_t key = c0 + kl + KPS * s;
-      const int64_t kk = min(key, len - 1);        // clamped, always in range
-      const vec8 x = *reinterpret_cast<const vec8*>(kbase + kk * stride);
       float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(qv[e], to_f32(x[e]), dot);
-#pragma unroll
-      for (int off = 1; off < LPK; off <<= 1) dot += __shfl_xor(dot, off, 64);
+      for (int e = 0; e < 8; ++e) dot = fmaf(qv[e], to_f32(kx[s][e]), dot);
+      dot = group_sum<LPK>(dot);
       sc[s] = (key < len) ? dot : -INFINITY;
     }
     float cm = sc[0];
@@ -216,13 +243,10 @@ __global__ void __launch_bounds__(256) k_dec_part(DecodeArgs a) {
     m = mn;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int64_t key = c0 + kl + KPS * s;
-      const int64_t kk = min(key, len - 1);
       const float pk = fast_exp2(sc[s] - m);   // 0 for keys past the end
       l += pk;
-      const vec8 x = *reinterpret_cast<const vec8*>(vbase + kk * stride);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pk, to_f32(x[e]), acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pk, to_f32(vx[s][e]), acc[e]);
     }
   }
   // sum over the key groups of the wave (lanes with the same dl)
