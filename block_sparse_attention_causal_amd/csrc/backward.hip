@@ -892,26 +892,60 @@ k_bwd_dq_dma(BwdArgs a) {
     const int nsel = min(a.ks, blk_i);
     typedef bf16 vec4_t __attribute__((ext_vector_type(4)));
     bf16* dst = (bf16*)a.dq + dst_index * D;
+    float x[D / 32][4][4];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) x[dt][aa][bb] = acc[dt][4 * aa + bb] * a.scale;
+    if (a.ks <= 2) {
+      // every part load of the row at once (a missing part reads entry 0, always
+      // allocated, and is dropped), so the epilogue pays one memory latency
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const bool valid = sl < nsel;
+        const int64_t e = valid ? dst_index * a.ks + sl : 0;
+        float4 pt[D / 32][4];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa)
+            pt[dt][aa] = *reinterpret_cast<const float4*>(a.dq_sel + e * D + 32 * dt + 8 * aa +
+                                                          4 * half);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa) {
+            x[dt][aa][0] += valid ? pt[dt][aa].x : 0.f;
+            x[dt][aa][1] += valid ? pt[dt][aa].y : 0.f;
+            x[dt][aa][2] += valid ? pt[dt][aa].z : 0.f;
+            x[dt][aa][3] += valid ? pt[dt][aa].w : 0.f;
+          }
+      }
+    } else {
+      for (int sl = 0; sl < nsel; ++sl) {
+        const float* src = a.dq_sel + (dst_index * a.ks + sl) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa) {
+            const float4 pt = *reinterpret_cast<const float4*>(src + 32 * dt + 8 * aa + 4 * half);
+            x[dt][aa][0] += pt.x;
+            x[dt][aa][1] += pt.y;
+            x[dt][aa][2] += pt.z;
+            x[dt][aa][3] += pt.w;
+          }
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa) {
-        const int d0 = 32 * dt + 8 * aa + 4 * half;
-        float x[4];
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) x[bb] = acc[dt][4 * aa + bb] * a.scale;
-        for (int sl = 0; sl < nsel; ++sl) {
-          const float4 pt = *reinterpret_cast<const float4*>(
-              a.dq_sel + (dst_index * a.ks + sl) * D + d0);
-          x[0] += pt.x;
-          x[1] += pt.y;
-          x[2] += pt.z;
-          x[3] += pt.w;
-        }
         vec4_t r;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) r[bb] = (bf16)x[bb];
-        *reinterpret_cast<vec4_t*>(dst + d0) = r;
+        for (int bb = 0; bb < 4; ++bb) r[bb] = (bf16)x[dt][aa][bb];
+        *reinterpret_cast<vec4_t*>(dst + 32 * dt + 8 * aa + 4 * half) = r;
       }
   }
 #endif
