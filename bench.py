@@ -28,7 +28,8 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 MFMA / vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 CONFIG_NAMES = {"tiny": "moba_fwd_tiny_2k_fp32", "llama32k": "moba_fwd_llama8b_32k",
                 "varlen131k": "moba_fwd_varlen_131k", "1m": "moba_fwd_1m",
-                "fine256k": "moba_fwd_fine_blocks_256k", "10m_shard": "moba_fwd_10m_head_shard"}
+                "fine256k": "moba_fwd_fine_blocks_256k", "10m_shard": "moba_fwd_10m_head_shard",
+                "10m_full": "moba_fwd_10m_full_width_group_major"}
 
 
 def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
@@ -228,12 +229,73 @@ def bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma, steps):
             "algorithmic_flop": flop, "achieved_tflops": tf, "mfma_frac": tf / peak_mfma}
 
 
+def bench_group_major(moba, torch, args):
+    """A full-width 10M-token layer (32 q heads, 8 kv heads) on one GPU: Q, K, V and
+    out held kv-group-major (one contiguous [T, 4, D] / [T, 1, D] slice per kv head),
+    one moba_forward per group in a step, the workspace shared by the groups. Every
+    MoBA step is independent per kv group, so this is the same computation as the
+    [T, 32, D] layout; the layout keeps the workspace at one group's size (Q, K, V
+    and out already take 205 GB)."""
+    from synth_inputs import CONFIGS, make_config
+    cfg = CONFIGS["10m_shard"]
+    groups = 8
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    slices = []
+    for gi in range(groups):
+        print("[bench] building inputs, kv group %d" % gi, file=sys.stderr, flush=True)
+        inp = make_config("10m_shard", seed=args.seed + gi, device=dev)
+        slices.append((inp.q, inp.k, inp.v, torch.empty_like(inp.q)))
+    T, hq, d = slices[0][0].shape
+    cu_host = inp.cu_seqlens
+    cu_dev = cu_host.to(dev)
+    nbytes = moba.moba_workspace_bytes(cu_host, hq, 1, d, slices[0][0].dtype, inp.block,
+                                       inp.topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        for q, k, v, out in slices:
+            moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,
+                              cu_seqlens_dev=cu_dev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print("[bench] %d steps: %.3f ms/step" % (args.steps, ms), file=sys.stderr, flush=True)
+    work = work_counts(inp.seqlens, hq * groups, groups, d, inp.block, inp.topk, 2)
+    attn_flop = work["attn_selected_flop"] + work["attn_self_flop"]
+    line = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V with planted needle blocks",
+        "config": {"workload": CONFIG_NAMES["10m_full"], "seqlens": inp.seqlens, "tokens": T,
+                   "q_heads": hq * groups, "kv_heads": groups, "head_dim": d,
+                   "block_size": inp.block, "topk": inp.topk, "parallelism": "single GPU",
+                   "layout": "kv-group-major, one call per kv group"},
+        "roofline": None, "cpu_baseline": None,
+        "effective_attn_tflops": attn_flop / (ms * 1e-3) / 1e12,
+        "attn_mfma_frac_of_step": attn_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gpu_memory_gb": torch.cuda.max_memory_allocated(dev) / 1e9,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="1m", choices=sorted(CONFIG_NAMES))
+    ap.add_argument("--config", default="1m", choices=sorted(CONFIG_NAMES),
+                    help="10m_full: a full-width 10M-token layer held kv-group-major")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
@@ -254,6 +316,9 @@ def main():
     import block_sparse_attention_causal_amd as moba
     from synth_inputs import CONFIGS, make_config
 
+    if args.config == "10m_full":
+        bench_group_major(moba, torch, args)
+        return
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
