@@ -255,3 +255,30 @@ def test_profiling_kernel_keys():
     }
     for name, key in names.items():
         assert kernel_key(name) == key, name
+
+
+def test_bench_work_counts_closed_forms():
+    """The benchmark's algorithmic work against closed forms for one sequence of
+    nb full blocks: own-block pairs nb*B(B+1)/2, selected pairs
+    B^2 (ks nb - ks(ks+1)/2), gate pairs B nb(nb-1)/2 (per head)."""
+    import bench
+    B, nb, ks, hq, hkv, d = 2048, 512, 2, 32, 8, 128
+    w = bench.work_counts([nb * B], hq, hkv, d, B, ks + 1, 2)
+    self_pairs = nb * B * (B + 1) // 2
+    sel_pairs = B * B * (ks * nb - ks * (ks + 1) // 2)
+    gate_pairs = B * nb * (nb - 1) // 2
+    assert w["attn_self_flop"] == 4.0 * d * hq * self_pairs
+    assert w["attn_selected_flop"] == 4.0 * d * hq * sel_pairs
+    assert w["gate_flop"] == 2.0 * d * hq * gate_pairs
+    # the 1M workload's figures: 17.6 + 70.2 TFLOP of attention, 2.19 TFLOP of gate
+    assert abs(w["attn_self_flop"] / 1e12 - 17.60) < 0.01
+    assert abs(w["attn_selected_flop"] / 1e12 - 70.16) < 0.01
+    assert abs(w["gate_flop"] / 1e12 - 2.19) < 0.01
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys as _sys
+    r = subprocess.run([_sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
