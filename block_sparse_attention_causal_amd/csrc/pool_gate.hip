@@ -702,9 +702,7 @@ static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, 
                      w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
                      p.ks, ntiles, padded, w.gate_flags, sel)
   if (p.ks <= 2) MOBA_GATE_FAST(2);
-  else if (p.ks <= 4) MOBA_GATE_FAST(4);
-  else if (p.ks <= 8) MOBA_GATE_FAST(8);
-  else MOBA_GATE_FAST(16);
+  else MOBA_GATE_FAST(4);
 #undef MOBA_GATE_FAST
 }
 
@@ -716,18 +714,26 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
   const int64_t ntiles = p.nb * nu * (p.hq / p.hg);
   const int64_t padded = (ntiles + 7) / 8 * 8;
   if (p.dtype == MOBA_DTYPE_BF16) {
-    // screened single bf16 pass, then the exact three-pass gate on flagged tiles only
-    hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
-                       w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
-    if (p.d == 128) {
-      gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
-      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, w.gate_flags,
-                                     sel, s, ntiles, padded);
-    } else {
-      gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
-      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, w.gate_flags,
-                                    sel, s, ntiles, padded);
+    // Screened single bf16 pass, then the exact three-pass gate on flagged tiles
+    // only. With many kept blocks the list upkeep dominates either way and the
+    // screen only adds a pass (measured: top-12 at 256K, 10.0 ms screened
+    // against 6.3 exact), so it is used for topk - 1 <= 4.
+    const bool screen = p.ks <= 4;
+    if (screen) {
+      hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
+                         w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
+      if (p.d == 128)
+        gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+      else
+        gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
     }
+    const uint8_t* flags = screen ? w.gate_flags : nullptr;
+    if (p.d == 128)
+      gate_dispatch_kb<bf16, 128, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, flags, sel, s,
+                                     ntiles, padded);
+    else
+      gate_dispatch_kb<bf16, 64, 3>(p, (const bf16*)q, cu_dev, w, w.kbar_split, flags, sel, s,
+                                    ntiles, padded);
   } else {
     if (p.d == 128)
       gate_dispatch_kb<float, 128, 1>(p, (const float*)q, cu_dev, w, w.kbar, nullptr, sel, s,
