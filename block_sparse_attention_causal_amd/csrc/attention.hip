@@ -594,6 +594,167 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// Selected-block attention for 16-bit inputs with D = 128, in 4-wave
+// workgroups: a tile is 128 routed rows (4 waves x 32) of one (block, kv head)
+// list, the block's keys stream through two 32 KB LDS buffers (K then V rows of
+// a 64-key chunk, the same swizzled layout and fragment reads as k_attn's
+// direct-load path), one chunk in flight. With 64 KB of LDS two workgroups
+// share a CU, and one's tile prologue, epilogue and barrier waits overlap the
+// other's products, which matters most when blocks are short (block 512: 8
+// chunks per tile). Every wave issues 8 direct loads per chunk (16 rows of K
+// and of V), so "chunk c+1 landed" is vmcnt(0) at the end of iteration c.
+__global__ void __launch_bounds__(64 * kSelWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_attn_sel4(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef bf16 T;
+  constexpr int D = 128;
+  typedef bf16x8 frag_t;
+  typedef typename PartType<T>::type PT;
+  constexpr int DBUF = 2 * KC * D;                 // K rows then V rows of one chunk
+  static_assert(kSelWaves * 32 * (D + 16 / sizeof(PT)) * sizeof(PT) <= 2 * DBUF * sizeof(T),
+                "output staging must fit in the LDS buffers");
+  __shared__ __attribute__((aligned(16))) T lds[2 * DBUF];
+  const int64_t logical = xcd_logical(blockIdx.x, a.padded);
+  if (logical >= a.ntiles) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const T* __restrict__ q = (const T*)a.q;
+  const T* __restrict__ k = (const T*)a.k;
+  const T* __restrict__ v = (const T*)a.v;
+
+  const int64_t tile = logical;
+  const int32_t* toffs = a.tile_offsets;
+  if (tile >= toffs[a.nlists]) return;
+  const int L = upper_index(toffs, (int)a.nlists, tile);
+  const int64_t b = L / a.hkv;
+  const int g = L % a.hkv;
+  const int n = a.blk_seq[b], j = a.blk_local[b];
+  const int64_t kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
+  const int64_t kend = kbeg + a.block;            // a past block is full
+  const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kSelRowsPerTile +
+                     (int64_t)w * kRowsPerWave;
+  const int64_t e1 = a.list_offsets[L + 1];
+  int64_t row = -1, dst_index = -1;
+  if (e0 + r32 < e1) {
+    const int32_t ev = a.entries[e0 + r32];
+    dst_index = ev;
+    row = ev / a.ks;
+  }
+  frag_t qf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = (row >= 0) ? load8_stream(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int hx = half ^ swz(r32);
+  const int ml = lane & 15;
+  const int vrow = 4 * half + (ml >> 2);
+  const int vp = 2 * ((lane >> 4) & 1) + ((ml & 3) >> 1);
+  const int vx0 = vp ^ swz(vrow), vx1 = vp ^ swz(vrow + 8);
+  const int vbyte = (ml & 1) * 4;
+  auto kfrag = [&](int buf, int kt, int kk) __attribute__((always_inline)) -> frag_t {
+    const T* kb = lds + buf * DBUF + (32 * kt + r32) * D;
+    return load8(kb + 8 * ((2 * kk) ^ hx));
+  };
+  auto vfrag = [&](int buf, int dt, int qq) __attribute__((always_inline)) -> frag_t {
+    // keys 32kt + 16mm + {4h .. 4h+3} and the same + 8; head dim 32dt + r32
+    const int kt = qq >> 1, mm = qq & 1;
+    const T* vb = lds + buf * DBUF + KC * D + (32 * kt + 16 * mm + vrow) * D;
+    const T* p0 = vb + 8 * ((4 * dt) ^ vx0) + vbyte;
+    const T* p1 = vb + 8 * D + 8 * ((4 * dt) ^ vx1) + vbyte;
+    const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 r;
+    r[0] = x0[0]; r[1] = x0[1]; r[2] = x0[2]; r[3] = x0[3];
+    r[4] = x1[0]; r[5] = x1[1]; r[6] = x1[2]; r[7] = x1[3];
+    return __builtin_bit_cast(frag_t, r);
+  };
+  // one staged chunk into the wave's running softmax state (as in k_attn)
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    f32x16 s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s0 = mma_k16(kfrag(buf, 0, kk), qf[kk], s0);
+      s1 = mma_k16(kfrag(buf, 1, kk), qf[kk], s1);
+    }
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
+    mx = vmax(mx, swap_half(mx));
+    const float m_cand = vmax(m_run, mx * a.scale_log2);
+    if (__ballot(m_cand > m_run + 8.f)) {
+      const float alpha = fast_exp2(m_run - m_cand);   // 0 while m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      m_run = m_cand;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float p0[16], p1[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p0[e] = fast_exp2(fmaf(s0[e], a.scale_log2, -m_use));
+      p1[e] = fast_exp2(fmaf(s1[e], a.scale_log2, -m_use));
+      psum += p0[e] + p1[e];
+    }
+    l_run += psum;
+    frag_t pf[4];
+    pf[0] = pack8<T>(&p0[0]);
+    pf[1] = pack8<T>(&p0[8]);
+    pf[2] = pack8<T>(&p1[0]);
+    pf[3] = pack8<T>(&p1[8]);
+#pragma unroll
+    for (int f = 0; f < (D / 32) * 4; ++f)
+      o[f >> 2] = mma_k16(vfrag(buf, f >> 2, f & 3), pf[f & 3], o[f >> 2]);
+  };
+
+  const int nch = (int)((kend - kbeg + KC - 1) / KC);
+  const int row_stride = a.hkv * D;
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const int64_t c0 = kbeg + (int64_t)min(c, nch - 1) * KC;
+    const T* kb = k + (c0 * a.hkv + g) * D;
+    const T* vb = v + (c0 * a.hkv + g) * D;
+    const uint32_t dst = lds0 + (uint32_t)((c & 1) * DBUF * 2 + 16 * w * 256);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * i + (lane >> 4);  // rows 16w .. 16w+15 of the chunk
+      const int off = r * row_stride + 8 * ((lane & 15) ^ swz(r));
+      dma16(kb + off, dst + (uint32_t)(1024 * i));
+      dma16(vb + off, dst + (uint32_t)(KC * D * 2 + 1024 * i));
+    }
+  };
+  // the Q fragments (compiler-visible loads) land before any direct load
+  MOBA_WAIT_VM_LGKM0(0);
+  issue(0);
+  MOBA_WAIT_VM_LGKM0(0);
+  bare_barrier();
+  for (int c = 0; c < nch; ++c) {
+    issue(c + 1);                                  // clamped past the end
+    compute(c & 1);
+    MOBA_WAIT_VM_LGKM0(0);
+    bare_barrier();
+  }
+  const float l_tot = l_run + swap_half(l_run);
+  const float inv = (row >= 0) ? 1.f / l_tot : 0.f;
+  const float lse = (m_run + fast_log2(l_tot)) * kLn2;
+  if (row >= 0 && half == 0) a.lse_part[dst_index] = lse;
+  store_rows<PT, D>((PT*)a.o_part, (char*)lds, o, inv, dst_index, w, lane);
+#endif
+}
+
 template <int MODE>
 static hipError_t attn_dispatch(const Plan& p, const AttnArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.padded), blk(512);
@@ -639,6 +800,10 @@ hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, con
   a.lse_part = w.lse_sel;
   a.ntiles = p.max_tiles;
   a.padded = (p.max_tiles + 7) / 8 * 8;
+  if (p.sel_rows == kSelRowsPerTile) {             // bf16, D = 128
+    hipLaunchKernelGGL(k_attn_sel4, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s, a);
+    return hipGetLastError();
+  }
   return attn_dispatch<MODE_SELECTED>(p, a, s);
 }
 

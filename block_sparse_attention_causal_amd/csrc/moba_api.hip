@@ -100,7 +100,9 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
       return fail(MOBA_ERR_UNSUPPORTED, "routing histogram too large");
   }
   P.nlists = P.nb * P.hkv;
-  P.max_tiles = P.nentries / kRowsPerTile + P.nlists + 1;
+  P.sel_rows = (P.dtype == MOBA_DTYPE_BF16 && P.d == 128) ? kSelRowsPerTile : kRowsPerTile;
+  // a bound for either tile size (surplus workgroups read the device-side count and exit)
+  P.max_tiles = P.nentries / std::min(kSelRowsPerTile, kRowsPerTile) + P.nlists + 1;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -367,7 +369,7 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
     if (e != hipSuccess) return hip_status(e, "gate");
     {
       StageScope t(ST_ROUTE, s);
-      e = launch_route(p, sel, cu_seqlens_dev, w, w.list_offsets, w.entries, s);
+      e = launch_route(p, sel, cu_seqlens_dev, w, p.sel_rows, w.list_offsets, w.entries, s);
     }
     if (e != hipSuccess) return hip_status(e, "route");
     {
@@ -585,7 +587,7 @@ moba_status_t moba_backward(const void* q, const void* k, const void* v, const v
   if (e != hipSuccess) return hip_status(e, "setup");
   if (p.ks > 0) {
     StageScope t(ST_ROUTE, s);
-    e = launch_route(p, sel, cu_seqlens_dev, w, w.list_offsets, w.entries, s);
+    e = launch_route(p, sel, cu_seqlens_dev, w, kRowsPerTile, w.list_offsets, w.entries, s);
   }
   if (e != hipSuccess) return hip_status(e, "route");
   {
@@ -671,7 +673,7 @@ moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
   if (e != hipSuccess) return hip_status(e, "setup");
   {
     StageScope t(ST_ROUTE, s);
-    e = launch_route(p, sel_dev, cu_seqlens_dev, w, list_offsets, entries, s);
+    e = launch_route(p, sel_dev, cu_seqlens_dev, w, p.sel_rows, list_offsets, entries, s);
   }
   if (e != hipSuccess) return hip_status(e, "route");
   g_err[0] = 0;

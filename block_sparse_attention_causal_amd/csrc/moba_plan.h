@@ -17,7 +17,12 @@ constexpr int kGateWaves = 8;              // gate workgroups: 512 threads
 // its own copy of every chunk and only one chunk fits in flight.)
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kRowsPerTile = kRowsPerWave * kAttnWaves;   // routed rows per attention tile
+constexpr int kRowsPerTile = kRowsPerWave * kAttnWaves;   // routed rows per 8-wave tile
+// The selected-block kernel for 16-bit inputs with D = 128 runs 4-wave tiles of
+// 128 routed rows (two workgroups per CU); the other selected-block kernels,
+// and the backward, use 8-wave tiles of kRowsPerTile.
+constexpr int kSelWaves = 4;
+constexpr int kSelRowsPerTile = kRowsPerWave * kSelWaves;
 constexpr int kMaxSelected = 16;           // topk - 1 limit (per-lane register lists)
 constexpr int kMaxBlocksPerSeq = 16384;    // per-sequence block counters live in LDS
 
@@ -38,6 +43,7 @@ struct Plan {
   int64_t nlists = 0;       // nb * hkv
   int64_t nentries = 0;     // routed (row, slot) pairs
   int64_t max_tiles = 0;    // launch bound for the selected-block attention grid
+  int32_t sel_rows = 0;     // routed rows per selected-block tile of the forward
   // workspace offsets (bytes); -1 when not used
   size_t off_blk_base = 0, off_tri_base = 0, off_blk_seq = 0, off_blk_local = 0;
   size_t off_kbar = 0, off_kbar_split = 0, off_kbar_err = 0, off_gate_bound = 0;
@@ -87,6 +93,7 @@ hipError_t launch_pool(const Plan& p, const void* k, const int32_t* cu_dev, cons
 hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, const Work& w,
                        int32_t* sel, hipStream_t s);
 hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev, const Work& w,
+                        int rows_per_tile,
                         int32_t* list_offsets, int32_t* entries, hipStream_t s);
 hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, const void* v,
                                 const int32_t* cu_dev, const Work& w, hipStream_t s);

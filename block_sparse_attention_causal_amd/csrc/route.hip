@@ -184,6 +184,7 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
 }
 
 hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev, const Work& w,
+                        int rows_per_tile,
                         int32_t* list_offsets, int32_t* entries, hipStream_t s) {
   if (p.ks == 0 || p.nb == 0) return hipSuccess;
   const unsigned nchunks = (unsigned)(p.nb * p.hkv);
@@ -194,7 +195,7 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
                      w.hist, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, p.hkv, p.nlists,
                      w.chunk_off, w.list_count);
   hipLaunchKernelGGL(k_route_offsets, dim3(1), dim3(1024), 0, s, w.list_count, p.nlists,
-                     kRowsPerTile, list_offsets, w.tile_offsets);
+                     rows_per_tile, list_offsets, w.tile_offsets);
   hipLaunchKernelGGL(k_route_scatter, dim3(nchunks), dim3(64), lds, s, sel, cu_dev, w.blk_base,
                      w.tri_base, w.blk_seq, w.blk_local, w.chunk_off, list_offsets, p.hq, p.hkv,
                      p.block, p.ks, entries);
