@@ -798,8 +798,8 @@ hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, con
   a.nlists = p.nlists;
   a.o_part = w.o_sel;
   a.lse_part = w.lse_sel;
-  a.ntiles = p.max_tiles;
-  a.padded = (p.max_tiles + 7) / 8 * 8;
+  a.ntiles = tile_bound(p, p.sel_rows);
+  a.padded = (a.ntiles + 7) / 8 * 8;
   if (p.sel_rows == kSelRowsPerTile) {             // bf16, D = 128
     hipLaunchKernelGGL(k_attn_sel4, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s, a);
     return hipGetLastError();

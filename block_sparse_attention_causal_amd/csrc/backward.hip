@@ -965,8 +965,8 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
   }
   BwdArgs a = base;
   if (p.ks > 0 && p.nentries > 0) {
-    a.ntiles = p.max_tiles;
-    a.padded = (p.max_tiles + 7) / 8 * 8;
+    a.ntiles = tile_bound(p, kRowsPerTile);
+    a.padded = (a.ntiles + 7) / 8 * 8;
     if constexpr (sizeof(T) == 2 && D == 128)
       hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELECTED>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
     else

@@ -101,8 +101,6 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
   }
   P.nlists = P.nb * P.hkv;
   P.sel_rows = (P.dtype == MOBA_DTYPE_BF16 && P.d == 128) ? kSelRowsPerTile : kRowsPerTile;
-  // a bound for either tile size (surplus workgroups read the device-side count and exit)
-  P.max_tiles = P.nentries / std::min(kSelRowsPerTile, kRowsPerTile) + P.nlists + 1;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

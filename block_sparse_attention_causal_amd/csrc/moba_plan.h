@@ -42,7 +42,6 @@ struct Plan {
   int64_t tri = 0;          // sum_n Hkv * NB_n * (NB_n - 1) / 2 (route histograms)
   int64_t nlists = 0;       // nb * hkv
   int64_t nentries = 0;     // routed (row, slot) pairs
-  int64_t max_tiles = 0;    // launch bound for the selected-block attention grid
   int32_t sel_rows = 0;     // routed rows per selected-block tile of the forward
   // workspace offsets (bytes); -1 when not used
   size_t off_blk_base = 0, off_tri_base = 0, off_blk_seq = 0, off_blk_local = 0;
@@ -54,6 +53,11 @@ struct Plan {
   size_t off_o_sel = 0, off_lse_sel = 0;
   size_t total = 0;
 };
+
+// Launch bound on the tiles of the routed lists cut into tiles of `rows` rows: each list
+// adds at most one partial tile. A grid sized by the bound of another tile size would
+// leave workgroups idle and, under the XCD mapping, whole XCDs without work.
+inline int64_t tile_bound(const Plan& p, int rows) { return p.nentries / rows + p.nlists + 1; }
 
 // Fills `plan` from validated arguments. Returns MOBA_OK or an error status and
 // writes a message into `err` (size errlen).

@@ -7,8 +7,17 @@
         HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE, then
         WRITE_SIZE), scaled by what the same counters read for a plain copy kernel
         (torch.neg over N MiB of fp32: N MiB read, N MiB written).
+    python -m block_sparse_attention_causal_amd.profiling dram DIR --copy-mib N
+        DRAM bytes read and written per launch of every kernel from one --pmc run of
+        TCC_EA0_RDREQ_DRAM_32B_sum and TCC_EA0_WRREQ_WRITE_DRAM_32B_sum (requests in
+        32-byte units, 64- and 128-byte requests counted 2 and 4 times), checked
+        against the same copy.
     python -m block_sparse_attention_causal_amd.profiling counters DIR
         per-kernel mean of every counter of one --pmc run (one row per kernel)
+
+The calibration copy is summed over all of its dispatches: torch splits an
+elementwise kernel whose byte offsets overflow 32 bits (a 4 GiB copy) into
+several launches.
 """
 from __future__ import annotations
 
@@ -107,13 +116,17 @@ def _counter_per_dispatch(dirpath: str, counter: str) -> dict:
     return {k: sorted(v.values()) for k, v in per.items()}
 
 
+def _copy_total(per: dict) -> float:
+    """Counter total over every dispatch of the calibration copy."""
+    return sum(per.get("copy_calibration", [0.0]))
+
+
 def traffic(fetch_dir: str, write_dir: str, copy_mib: int, kernel: str) -> str:
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
     cal_bytes = copy_mib * 1024.0 * 1024.0
-    # the calibration copy is the largest elementwise dispatch of the run
-    f_copy = max(fetch.get("copy_calibration", [0.0])) * 1024.0
-    w_copy = max(write.get("copy_calibration", [0.0])) * 1024.0
+    f_copy = _copy_total(fetch) * 1024.0
+    w_copy = _copy_total(write) * 1024.0
     f_scale = cal_bytes / f_copy if f_copy > 0 else float("nan")
     w_scale = cal_bytes / w_copy if w_copy > 0 else float("nan")
     fk = fetch.get(kernel, [])
@@ -136,6 +149,34 @@ def traffic(fetch_dir: str, write_dir: str, copy_mib: int, kernel: str) -> str:
         "hbm_bytes_per_launch: %.6g" % (f_mean * f_scale + w_mean * w_scale),
     ]
     return "\n".join(lines)
+
+
+DRAM_READ = "TCC_EA0_RDREQ_DRAM_32B_sum"
+DRAM_WRITE = "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"
+
+
+def dram(dirpath: str, copy_mib: int) -> str:
+    rd = _counter_per_dispatch(dirpath, DRAM_READ)
+    wr = _counter_per_dispatch(dirpath, DRAM_WRITE)
+    cal_bytes = copy_mib * 1024.0 * 1024.0
+    r_copy = _copy_total(rd) * 32.0
+    w_copy = _copy_total(wr) * 32.0
+    out = ["copy_calibration_bytes: %.6g" % cal_bytes,
+           "copy_read_bytes: %.6g (ratio %.4f)" % (r_copy, r_copy / cal_bytes),
+           "copy_write_bytes: %.6g (ratio %.4f)" % (w_copy, w_copy / cal_bytes),
+           "",
+           "| kernel | launches | GB read / launch | GB written / launch |",
+           "|---|---|---|---|"]
+    keys = sorted(set(rd) | set(wr), key=lambda k: -(sum(rd.get(k, [0])) + sum(wr.get(k, [0]))))
+    for k in keys:
+        if k == "copy_calibration":
+            continue
+        r, w = rd.get(k, []), wr.get(k, [])
+        n = max(len(r), len(w))
+        out.append("| %s | %d | %.4f | %.4f |" % (
+            k, n, (sum(r) / len(r) * 32e-9) if r else float("nan"),
+            (sum(w) / len(w) * 32e-9) if w else float("nan")))
+    return "\n".join(out)
 
 
 def counters(dirpath: str) -> str:
@@ -176,9 +217,14 @@ def main(argv=None):
     t.add_argument("--kernel", default="attn_selected")
     c = sub.add_parser("counters")
     c.add_argument("dir")
+    m = sub.add_parser("dram")
+    m.add_argument("dir")
+    m.add_argument("--copy-mib", type=int, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.dir))
+    elif a.cmd == "dram":
+        print(dram(a.dir, a.copy_mib))
     elif a.cmd == "counters":
         print(counters(a.dir))
     else:

@@ -282,3 +282,40 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([_sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _write_counter_csv(path, rows):
+    import csv
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_profiling_copy_calibration_sums_split_launches(tmp_path):
+    """torch runs a copy whose byte offsets overflow 32 bits as several launches: the
+    calibration must total them, else the scale factors come out twice too large."""
+    from block_sparse_attention_causal_amd import profiling
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda"
+    sel = "moba::k_attn_sel4(moba::AttnArgs)"
+    gib = 1 << 30
+    fdir, wdir = str(tmp_path / "f"), str(tmp_path / "w")
+    # a 4 GiB copy in two launches; FETCH_SIZE reads half the bytes, WRITE_SIZE all (KiB)
+    _write_counter_csv(fdir, [(1, neg, "FETCH_SIZE", gib / 1024), (2, neg, "FETCH_SIZE", gib / 1024),
+                              (3, sel, "FETCH_SIZE", 3 * gib / 1024)])
+    _write_counter_csv(wdir, [(1, neg, "WRITE_SIZE", 2 * gib / 1024),
+                              (2, neg, "WRITE_SIZE", 2 * gib / 1024),
+                              (3, sel, "WRITE_SIZE", 5 * gib / 1024)])
+    out = dict(l.split(": ", 1) for l in profiling.traffic(fdir, wdir, 4096, "attn_selected")
+               .splitlines())
+    assert float(out["fetch_scale"]) == 2.0 and float(out["write_scale"]) == 1.0
+    assert abs(float(out["hbm_bytes_per_launch"]) / ((6 + 5) * gib) - 1) < 1e-5
+    ddir = str(tmp_path / "d")
+    _write_counter_csv(ddir, [(1, neg, profiling.DRAM_READ, gib / 16), (2, neg, profiling.DRAM_READ, gib / 16),
+                              (1, neg, profiling.DRAM_WRITE, gib / 16), (2, neg, profiling.DRAM_WRITE, gib / 16),
+                              (3, sel, profiling.DRAM_READ, 1e9 / 32), (3, sel, profiling.DRAM_WRITE, 2e9 / 32)])
+    txt = profiling.dram(ddir, 4096)
+    assert "copy_read_bytes: 4.29497e+09 (ratio 1.0000)" in txt
+    assert "| attn_selected | 1 | 1.0000 | 2.0000 |" in txt
