@@ -481,6 +481,11 @@ k_bwd_dkdv(BwdArgs a) {
 // Tiles are dealt to the XCDs list by list (all key tiles of one list on one
 // XCD, which then shares the list's rows in its L2; consecutive lists on
 // different XCDs, which spreads the long lists of the much-selected blocks).
+// For that sharing the key tiles of a list stream the same rows in the same
+// order at the same time: first the routed rows, then the block's own rows from
+// its last token down, each tile stopping below its first key. (Own rows first,
+// from each tile's first key up, would start the tiles thousands of rows apart
+// and every tile would fetch every row from HBM.)
 constexpr int DKV_WAVES = 8;
 
 __device__ __forceinline__ bf16x8 tr_frag(const bf16* rows, int r0, int dt, int vrow, int vx0,
@@ -555,33 +560,33 @@ k_bwd_dkdv_dma(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dk[dt][e] = 0.f; dv[dt][e] = 0.f; }
 
-  // rows: the block's own tokens t0 .. blk_end-1 (G heads each), then the list
-  // (row counts and row ids fit 32 bits: T * hq < 2^31)
+  // rows: the list's routed rows, then the block's own tokens blk_end-1 down to t0
+  // (G heads each); row counts and row ids fit 32 bits: T * hq < 2^31
   const int nself = (int)(blk_end - t0) * G;
   int e_beg = 0, nsel_rows = 0;
   if (a.ks > 0 && a.list_offsets) {
     e_beg = a.list_offsets[L];
     nsel_rows = a.list_offsets[L + 1] - e_beg;
   }
-  const int nrows = nself + nsel_rows;
+  const int nrows = nsel_rows + nself;
   const int nch = (nrows + BRC - 1) / BRC;
-  const int row0 = (int)t0 * a.hq + g * G;   // row id of own row 0
+  const int rowl = (int)(blk_end - 1) * a.hq + g * G;   // row id of own row 0 (last token)
 
   const uint32_t rows_base = lds_addr(rows_lds);
   auto issue_ent = [&](int c) __attribute__((always_inline)) {
     const int cc = min(c, nch - 1);
-    const int idx = cc * BRC + (lane & 31) - nself;
+    const int idx = cc * BRC + (lane & 31);
     const int32_t* src =
         (nsel_rows > 0) ? a.entries + e_beg + min(max(idx, 0), nsel_rows - 1) : a.cu;
     dma4(src, lds_addr(&ent_lds[c & 7][w][0]));
   };
   auto rowid_of = [&](int c, int r) __attribute__((always_inline)) -> int {
     const int rr = min(c, nch - 1) * BRC + r;
-    if (rr < nself) {
-      const int tq = rr / G;
-      return row0 + tq * a.hq + (rr - tq * G);
+    if (rr < nsel_rows) return ent_lds[c & 7][w][r] / a.ks;
+    if (rr < nrows) {
+      const int o = rr - nsel_rows, tb = o / G;
+      return rowl - tb * a.hq + (o - tb * G);
     }
-    if (rr < nrows) return ent_lds[c & 7][w][r] / a.ks;
     return 0;   // padding: any valid row, masked out
   };
   const int rA = 4 * w + (lane >> 4);
@@ -602,13 +607,15 @@ k_bwd_dkdv_dma(BwdArgs a) {
   const int vp = 2 * ((lane >> 4) & 1) + ((ml & 3) >> 1);
   const int vx0 = vp ^ swz(vrow), vx1 = vp ^ swz(vrow + 8);
   const int vbyte = (ml & 1) * 4;
-  const int mask_below = keyrel * G;   // own rows rr < keyrel * G come before the key
+  // own rows from rr = lim on come before the key (and rr >= nrows is padding)
+  const int lim = nsel_rows + (int)(blk_end - key) * G;
+  const int lim_wave = nsel_rows + (int)(blk_end - t0 - 32 * w) * G;   // of the wave's first key
 
   auto compute = [&](int c) __attribute__((always_inline)) {
     if (!wave_live) return;
     const int rr0 = c * BRC;
-    // a chunk of own rows whose last token precedes the wave's first key
-    if (rr0 + BRC - 1 < nself && rr0 + BRC - 1 < 32 * w * G) return;
+    // a chunk of own rows whose tokens all precede the wave's first key
+    if (rr0 >= lim_wave) return;
     const bf16* qb = rows_lds + (c & 3) * RBUF;
     const bf16* gb = qb + CH;
     f32x16 s, dp;
@@ -635,7 +642,7 @@ k_bwd_dkdv_dma(BwdArgs a) {
       for (int u = 0; u < 4; ++u) {
         const int e = 4 * jj + u;
         const int rr = rr0 + 8 * jj + 4 * half + u;
-        const bool masked = rr >= nrows || rr < mask_below;
+        const bool masked = rr >= lim;
         const float p = masked ? 0.f : fast_exp2(fmaf(s[e], a.scale_log2, -lv[u] * kLog2e));
         s[e] = p;
         dp[e] = p * (dp[e] - dl[u]);
