@@ -158,6 +158,12 @@ __global__ void __launch_bounds__(256) k_dec_gate(DecodeArgs a) {
 // in the log2 domain (q pre-scaled by scale * log2 e) with an online softmax
 // over 64-key chunks. Writes the segment's normalised output and its natural
 // log-sum-exp (-inf for an empty segment).
+// Items run in (row, head, part, segment) order, and each XCD takes one
+// contiguous range of them (the grid is a multiple of 8 workgroups): the q heads
+// of one kv group, which read the same own block and often the same selected
+// blocks, then run at the same time on one XCD and fetch those keys and values
+// from HBM once, through its L2. Dealt round-robin over the XCDs, each head
+// fetched its blocks again.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 3))) k_dec_part(DecodeArgs a) {
   constexpr int LPK = D / 8;      // lanes per key row, 8 values each
@@ -166,7 +172,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 3))
   typedef T vec8 __attribute__((ext_vector_type(8)));
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nparts = a.ks + 1;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t item = xcd_logical(blockIdx.x, gridDim.x) * 4 + wv;
   if (item >= a.rows * nparts * a.nseg) return;
   const int sg = (int)(item % a.nseg);
   const int t = (int)((item / a.nseg) % nparts);
@@ -315,7 +321,8 @@ static hipError_t decode_launch(const DecodeArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_dec_part<T, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+  const int64_t part_wgs = ((items + 3) / 4 + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_dec_part<T, D>), dim3((unsigned)part_wgs), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_dec_merge<T, D>), dim3(g_rows), dim3(256), 0, s, a);
