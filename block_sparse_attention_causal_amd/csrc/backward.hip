@@ -784,11 +784,14 @@ k_bwd_dq_dma(BwdArgs a) {
     }
   }
 
+  // cached loads: each instruction takes 32 bytes of every row, and the row's
+  // other pieces, read by the next instructions, must still be in L2 (with
+  // non-temporal loads the kernel read 1.5x the Q and dO bytes from DRAM)
   bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    qf[kk] = (row >= 0) ? load8_stream(q + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
-    gf[kk] = (row >= 0) ? load8_stream(dout + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
+    qf[kk] = (row >= 0) ? load8(q + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
+    gf[kk] = (row >= 0) ? load8(dout + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
   }
   const float lse_l2 = (row >= 0) ? a.lse[row] * kLog2e : 0.f;
   const float dlt = (row >= 0) ? a.delta[row] : 0.f;
@@ -884,18 +887,36 @@ k_bwd_dq_dma(BwdArgs a) {
   MOBA_WAIT_VM_LGKM0(0);
 
   // epilogue: lane holds dQ^T[32dt + 8(i/4) + 4half + i%4][row r32]
-  if (dst_index < 0) return;
   if (MODE == BWD_SELECTED) {
-    float* dst = a.dq_sel + dst_index * D;
+    // fp32 parts through LDS, half a row (64 values) at a time, so that every
+    // store instruction writes whole 256-byte half rows: written 32 bytes per
+    // row at a time, the parts cost as many DRAM bytes again in reads
+    constexpr int SLD = 64 + 4;                    // padded staging row (floats)
+    float* stage = reinterpret_cast<float*>(smem) + w * 32 * SLD;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int hh = 0; hh < 2; ++hh) {
+      __syncthreads();   // every wave's direct loads have landed and its products are done
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        float4 val = make_float4(acc[dt][4 * aa] * a.scale, acc[dt][4 * aa + 1] * a.scale,
-                                 acc[dt][4 * aa + 2] * a.scale, acc[dt][4 * aa + 3] * a.scale);
-        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * aa + 4 * half) = val;
+      for (int dt = 2 * hh; dt < 2 * hh + 2; ++dt)
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa)
+          *reinterpret_cast<float4*>(stage + r32 * SLD + 32 * (dt - 2 * hh) + 8 * aa + 4 * half) =
+              make_float4(acc[dt][4 * aa] * a.scale, acc[dt][4 * aa + 1] * a.scale,
+                          acc[dt][4 * aa + 2] * a.scale, acc[dt][4 * aa + 3] * a.scale);
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rr = 4 * it + (lane >> 4), pc = lane & 15;
+        const int64_t di = __shfl(dst_index, rr, 64);
+        if (di >= 0)
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + rr * SLD + 4 * pc),
+                                      reinterpret_cast<f32x4*>(a.dq_sel + di * D + 64 * hh + 4 * pc));
       }
-  } else {
+    }
+    return;
+  }
+  if (dst_index < 0) return;
+  {
     const int nsel = min(a.ks, blk_i);
     typedef bf16 vec4_t __attribute__((ext_vector_type(4)));
     bf16* dst = (bf16*)a.dq + dst_index * D;
