@@ -258,7 +258,61 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, char* smem,
       }
       finish(it, m, den, acc);
     }
+  } else if constexpr (NIT <= 8) {
+    // More parts (16-bit partials): part by part, two at a time, each step
+    // loading those parts for all of the lane's rows at once, so that it pays
+    // one memory latency for NIT rows. First the maximum LSE of every row, then
+    // the weighted sum.
+    float m[NIT], den[NIT], acc[NIT][V];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) m[it] = ls[it];
+    for (int sl = 0; sl < nsel; ++sl) {
+      float l[NIT];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it)
+        l[it] = (di[it] >= 0) ? a.sel_lse[di[it] * a.ks + sl] : -INFINITY;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) m[it] = fmaxf(m[it], l[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const float wgt = fast_exp2((ls[it] - m[it]) * kLog2e);
+      den[it] = wgt;
+      own_part(it, wgt, acc[it]);
+    }
+    for (int sl = 0; sl < nsel; sl += 2) {
+      const bool two = sl + 1 < nsel;
+      float l[NIT][2];
+      pvec_t x[NIT][2];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          l[it][j] = -INFINITY;
+          x[it][j] = pvec_t{};
+          if (di[it] >= 0 && (j == 0 || two)) {
+            const int64_t e = di[it] * a.ks + sl + j;
+            l[it][j] = a.sel_lse[e];
+            x[it][j] = __builtin_nontemporal_load(
+                reinterpret_cast<const pvec_t*>(o_sel + e * D + pc * V));
+          }
+        }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (j == 1 && !two) break;
+          const float wgt = fast_exp2((l[it][j] - m[it]) * kLog2e);
+          den[it] += wgt;
+#pragma unroll
+          for (int b = 0; b < V; ++b) acc[it][b] += to_f32(x[it][j][b]) * wgt;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      if (di[it] >= 0) finish(it, m[it], den[it], acc[it]);
   } else {
+    // fp32 partials (twice the registers per piece): row by row
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       if (di[it] < 0) continue;
@@ -595,24 +649,34 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------
-// Selected-block attention for 16-bit inputs with D = 128, in 4-wave
-// workgroups: a tile is 128 routed rows (4 waves x 32) of one (block, kv head)
-// list, the block's keys stream through two 32 KB LDS buffers (K then V rows of
-// a 64-key chunk, the same swizzled layout and fragment reads as k_attn's
-// direct-load path), one chunk in flight. With 64 KB of LDS two workgroups
-// share a CU, and one's tile prologue, epilogue and barrier waits overlap the
-// other's products, which matters most when blocks are short (block 512: 8
-// chunks per tile). Every wave issues 8 direct loads per chunk (16 rows of K
-// and of V), so "chunk c+1 landed" is vmcnt(0) at the end of iteration c.
+// Selected-block and own-block attention for 16-bit inputs with D = 128, in
+// 4-wave workgroups. The keys stream through two 32 KB LDS buffers (K then V
+// rows of a 64-key chunk, the same swizzled layout and fragment reads as
+// k_attn's direct-load path), one chunk in flight. With 64 KB of LDS two
+// workgroups share a CU, and one's tile prologue, epilogue and barrier waits
+// overlap the other's products, which matters most when tiles are short
+// (block 512: 8 chunks per selected tile; the own-block tiles of the causal
+// triangle: 1 to B/64 chunks). Every wave issues 8 direct loads per chunk (16
+// rows of K and of V), so "chunk c+1 landed" is vmcnt(0) at the end of
+// iteration c.
+//   SELECTED: a tile is 128 routed rows (4 waves x 32) of one (block, kv head)
+//     list over the block's B keys; writes fp16 parts and their LSE.
+//   SELF: a tile is 4 / hw groups of 32 consecutive tokens of one block for hw
+//     q heads of one kv group (hw = gcd(G, 4), one wave per head and token
+//     group, the heads sharing the K/V chunks), over the block's keys up to the
+//     tile's last token with the causal mask; the epilogue merges the row's
+//     selected parts (or, with no selection, writes the output).
+template <int MODE>
 __global__ void __launch_bounds__(64 * kSelWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-k_attn_sel4(AttnArgs a) {
+k_attn4(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef bf16 T;
   constexpr int D = 128;
   typedef bf16x8 frag_t;
   typedef typename PartType<T>::type PT;
   constexpr int DBUF = 2 * KC * D;                 // K rows then V rows of one chunk
-  static_assert(kSelWaves * 32 * (D + 16 / sizeof(PT)) * sizeof(PT) <= 2 * DBUF * sizeof(T),
+  static_assert(kSelWaves * 32 * (D + 16 / sizeof(PT)) * sizeof(PT) <= 2 * DBUF * sizeof(T) &&
+                    kSelWaves * 32 * (D + 16 / sizeof(T)) * sizeof(T) <= 2 * DBUF * sizeof(T),
                 "output staging must fit in the LDS buffers");
   __shared__ __attribute__((aligned(16))) T lds[2 * DBUF];
   const int64_t logical = xcd_logical(blockIdx.x, a.padded);
@@ -623,23 +687,54 @@ k_attn_sel4(AttnArgs a) {
   const T* __restrict__ k = (const T*)a.k;
   const T* __restrict__ v = (const T*)a.v;
 
-  const int64_t tile = logical;
-  const int32_t* toffs = a.tile_offsets;
-  if (tile >= toffs[a.nlists]) return;
-  const int L = upper_index(toffs, (int)a.nlists, tile);
-  const int64_t b = L / a.hkv;
-  const int g = L % a.hkv;
-  const int n = a.blk_seq[b], j = a.blk_local[b];
-  const int64_t kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
-  const int64_t kend = kbeg + a.block;            // a past block is full
-  const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kSelRowsPerTile +
-                     (int64_t)w * kRowsPerWave;
-  const int64_t e1 = a.list_offsets[L + 1];
-  int64_t row = -1, dst_index = -1;
-  if (e0 + r32 < e1) {
-    const int32_t ev = a.entries[e0 + r32];
-    dst_index = ev;
-    row = ev / a.ks;
+  int g;
+  int64_t kbeg, kend, row = -1, dst_index = -1;
+  int64_t wtok0 = 0;          // SELF: the wave's first token
+  bool wave_live = true;      // SELF: the wave has rows
+  int blk_i = 0;              // SELF: the tile's block index in its sequence
+  if constexpr (MODE == MODE_SELECTED) {
+    const int64_t tile = logical;
+    const int32_t* toffs = a.tile_offsets;
+    if (tile >= toffs[a.nlists]) return;
+    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int64_t b = L / a.hkv;
+    g = L % a.hkv;
+    const int n = a.blk_seq[b], j = a.blk_local[b];
+    kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
+    kend = kbeg + a.block;                         // a past block is full
+    const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kSelRowsPerTile +
+                       (int64_t)w * kRowsPerWave;
+    const int64_t e1 = a.list_offsets[L + 1];
+    if (e0 + r32 < e1) {
+      const int32_t ev = a.entries[e0 + r32];
+      dst_index = ev;
+      row = ev / a.ks;
+    }
+  } else {
+    const int group = a.hq / a.hkv;
+    const int hw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+    const int tt = 32 * (kSelWaves / hw);
+    const int u = a.nu - 1 - (int)(logical % a.nu);
+    const int64_t rest = logical / a.nu;
+    const int nhs = a.hq / hw;
+    const int hs = (int)(rest % nhs);
+    const int64_t b = a.nb - 1 - rest / nhs;
+    const int n = a.blk_seq[b];
+    blk_i = a.blk_local[b];
+    const int64_t blk_start = (int64_t)a.cu[n] + (int64_t)blk_i * a.block;
+    const int64_t blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
+    const int64_t tok0 = blk_start + (int64_t)u * tt;
+    if (tok0 >= blk_end) return;
+    const int h = hs * hw + (w % hw);
+    g = h / group;
+    wtok0 = tok0 + (int64_t)(w / hw) * 32;
+    wave_live = wtok0 < blk_end;
+    kbeg = blk_start;
+    kend = min(tok0 + tt, blk_end);
+    if (wtok0 + r32 < blk_end) {
+      row = (wtok0 + r32) * a.hq + h;
+      dst_index = row;
+    }
   }
   frag_t qf[D / 16];
 #pragma unroll
@@ -676,8 +771,12 @@ k_attn_sel4(AttnArgs a) {
     r[4] = x1[0]; r[5] = x1[1]; r[6] = x1[2]; r[7] = x1[3];
     return __builtin_bit_cast(frag_t, r);
   };
-  // one staged chunk into the wave's running softmax state (as in k_attn)
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+  // one staged chunk (keys c0 .. c0+63) into the wave's running softmax state
+  // (as in k_attn)
+  auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
+    if constexpr (MODE == MODE_SELF) {
+      if (!wave_live || c0 > wtok0 + 31) return;   // every key after every row
+    }
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
@@ -685,6 +784,17 @@ k_attn_sel4(AttnArgs a) {
     for (int kk = 0; kk < D / 16; ++kk) {
       s0 = mma_k16(kfrag(buf, 0, kk), qf[kk], s0);
       s1 = mma_k16(kfrag(buf, 1, kk), qf[kk], s1);
+    }
+    if constexpr (MODE == MODE_SELF) {
+      if (c0 + KC - 1 > wtok0) {                    // some key after some row
+        const int64_t tok = wtok0 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t key = c0 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (key > tok) s0[e] = -INFINITY;
+          if (key + 32 > tok) s1[e] = -INFINITY;
+        }
+      }
     }
     float mx = vmax(s0[0], s1[0]);
 #pragma unroll
@@ -727,11 +837,16 @@ k_attn_sel4(AttnArgs a) {
     const int64_t c0 = kbeg + (int64_t)min(c, nch - 1) * KC;
     const T* kb = k + (c0 * a.hkv + g) * D;
     const T* vb = v + (c0 * a.hkv + g) * D;
+    // SELF: keys past the tile's range (the last chunk of a causal tile) read
+    // the range's last key: in bounds, and masked. (A selected block is whole
+    // chunks: the block size is a multiple of 64.)
+    const int last = (MODE == MODE_SELF) ? (int)min((int64_t)(KC - 1), kend - 1 - c0) : KC - 1;
     const uint32_t dst = lds0 + (uint32_t)((c & 1) * DBUF * 2 + 16 * w * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * i + (lane >> 4);  // rows 16w .. 16w+15 of the chunk
-      const int off = r * row_stride + 8 * ((lane & 15) ^ swz(r));
+      const int off = ((MODE == MODE_SELF) ? min(r, last) : r) * row_stride +
+                      8 * ((lane & 15) ^ swz(r));
       dma16(kb + off, dst + (uint32_t)(1024 * i));
       dma16(vb + off, dst + (uint32_t)(KC * D * 2 + 1024 * i));
     }
@@ -743,15 +858,24 @@ k_attn_sel4(AttnArgs a) {
   bare_barrier();
   for (int c = 0; c < nch; ++c) {
     issue(c + 1);                                  // clamped past the end
-    compute(c & 1);
+    compute(c & 1, kbeg + (int64_t)c * KC);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }
   const float l_tot = l_run + swap_half(l_run);
   const float inv = (row >= 0) ? 1.f / l_tot : 0.f;
   const float lse = (m_run + fast_log2(l_tot)) * kLn2;
-  if (row >= 0 && half == 0) a.lse_part[dst_index] = lse;
-  store_rows<PT, D>((PT*)a.o_part, (char*)lds, o, inv, dst_index, w, lane);
+  if constexpr (MODE == MODE_SELECTED) {
+    if (row >= 0 && half == 0) a.lse_part[dst_index] = lse;
+    store_rows<PT, D>((PT*)a.o_part, (char*)lds, o, inv, dst_index, w, lane);
+  } else {
+    if (a.ks > 0) {
+      merge_rows<T, D>(a, (char*)lds, o, inv, lse, dst_index, min(a.ks, blk_i), w, lane);
+    } else {
+      if (row >= 0 && half == 0 && a.lse_out) a.lse_out[dst_index] = lse;
+      store_rows<T, D>((T*)a.out, (char*)lds, o, inv, dst_index, w, lane);
+    }
+  }
 #endif
 }
 
@@ -801,7 +925,8 @@ hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, con
   a.ntiles = tile_bound(p, p.sel_rows);
   a.padded = (a.ntiles + 7) / 8 * 8;
   if (p.sel_rows == kSelRowsPerTile) {             // bf16, D = 128
-    hipLaunchKernelGGL(k_attn_sel4, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s, a);
+    hipLaunchKernelGGL(k_attn4<MODE_SELECTED>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0,
+                       s, a);
     return hipGetLastError();
   }
   return attn_dispatch<MODE_SELECTED>(p, a, s);
@@ -818,6 +943,17 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
   a.sel_lse = w.lse_sel;
   a.out = out;
   a.lse_out = lse_out;
+  if (p.dtype == MOBA_DTYPE_BF16 && p.d == 128) {
+    // 4-wave tiles: hw = gcd(G, 4) heads x 4 / hw groups of 32 tokens
+    const int hw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
+    const int tt = 32 * (kSelWaves / hw);
+    a.nu = (p.block + tt - 1) / tt;
+    a.ntiles = p.nb * a.nu * (p.hq / hw);
+    a.padded = (a.ntiles + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_attn4<MODE_SELF>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s,
+                       a);
+    return hipGetLastError();
+  }
   const int tt = 32 * (8 / p.hg);
   a.nu = (p.block + tt - 1) / tt;
   a.ntiles = p.nb * a.nu * (p.hq / p.hg);

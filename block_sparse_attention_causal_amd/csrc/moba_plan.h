@@ -12,15 +12,15 @@ namespace moba {
 
 constexpr int kRowsPerWave = 32;           // one 32-row MFMA tile per wave
 constexpr int kGateWaves = 8;              // gate workgroups: 512 threads
-// Attention workgroups: 8 waves (512 threads), one per CU; all eight share each
-// staged K/V chunk. (Two 4-wave workgroups per CU measured slower: each stages
-// its own copy of every chunk and only one chunk fits in flight.)
+// Attention workgroups of the general kernels (fp32, or D = 64): 8 waves (512
+// threads), one per CU; all eight share each staged K/V chunk. The backward uses
+// 8-wave tiles too.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kRowsPerTile = kRowsPerWave * kAttnWaves;   // routed rows per 8-wave tile
-// The selected-block kernel for 16-bit inputs with D = 128 runs 4-wave tiles of
-// 128 routed rows (two workgroups per CU); the other selected-block kernels,
-// and the backward, use 8-wave tiles of kRowsPerTile.
+// The forward attention kernels for 16-bit inputs with D = 128 run 4-wave
+// workgroups, two per CU: selected-block tiles of 128 routed rows, own-block
+// tiles of 128 rows (heads x tokens).
 constexpr int kSelWaves = 4;
 constexpr int kSelRowsPerTile = kRowsPerWave * kSelWaves;
 constexpr int kMaxSelected = 16;           // topk - 1 limit (per-lane register lists)

@@ -250,6 +250,10 @@ def test_profiling_kernel_keys():
         "void moba::k_bwd_dq_dma<1>(moba::BwdArgs)": "bwd_dq_selected",
         "void moba::k_bwd_dq_dma<0>(moba::BwdArgs)": "bwd_dq_self",
         "moba::k_bwd_dkdv_dma(moba::BwdArgs)": "bwd_dkdv",
+        "_ZN4moba7k_attn4ILi1EEEvNS_8AttnArgsE": "attn_selected",
+        "_ZN4moba7k_attn4ILi0EEEvNS_8AttnArgsE": "attn_self",
+        "void moba::k_attn4<1>(moba::AttnArgs)": "attn_selected",
+        "void moba::k_attn4<0>(moba::AttnArgs)": "attn_self",
         "_ZN4moba10k_dec_partIDF16bLi128EEEvNS_10DecodeArgsE": "decode_part",
         "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel": "copy_calibration",
     }
@@ -299,7 +303,7 @@ def test_profiling_copy_calibration_sums_split_launches(tmp_path):
     calibration must total them, else the scale factors come out twice too large."""
     from block_sparse_attention_causal_amd import profiling
     neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda"
-    sel = "moba::k_attn_sel4(moba::AttnArgs)"
+    sel = "void moba::k_attn4<1>(moba::AttnArgs)"
     gib = 1 << 30
     fdir, wdir = str(tmp_path / "f"), str(tmp_path / "w")
     # a 4 GiB copy in two launches; FETCH_SIZE reads half the bytes, WRITE_SIZE all (KiB)
