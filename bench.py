@@ -192,6 +192,52 @@ def bench_decode(moba, torch, q, k, v, block, topk, steps, nseq=16):
             "dense_decode_bytes": nseq * hkv * L * d * 2 * elem}
 
 
+def measure_achievable(torch, dev, dtype):
+    """What this machine reaches with library code, beside the datasheet peaks: dense
+    matrix products (torch.mm in the workload's dtype, 8192^3 and 16384 x 16384 x
+    4096, the faster counts) for the matrix cores, and a device-to-device copy of
+    2 GiB (2 GiB read + 2 GiB written) for HBM. Best of several timed repetitions."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mm_tflops, mm_shape = 0.0, None
+    for m, n, kk in ((8192, 8192, 8192), (16384, 16384, 4096)):
+        a = torch.randn(m, kk, device=dev, dtype=torch.float32).to(dtype)
+        b = torch.randn(kk, n, device=dev, dtype=torch.float32).to(dtype)
+        c = torch.empty(m, n, device=dev, dtype=dtype)
+        for _ in range(3):
+            torch.mm(a, b, out=c)
+        best = float("inf")
+        for _ in range(5):
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                torch.mm(a, b, out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 10)
+        tf = 2.0 * m * n * kk / (best * 1e-3) / 1e12
+        if tf > mm_tflops:
+            mm_tflops, mm_shape = tf, "%dx%dx%d" % (m, n, kk)
+        del a, b, c
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 4, device=dev, dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(5):
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 5)
+    copy_gbs = 2.0 * nbytes / (best * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_tflops": mm_tflops,
+            "mfma_source": "torch.mm %s %s" % (str(dtype).replace("torch.", ""), mm_shape),
+            "hbm_gbs": copy_gbs, "hbm_source": "device copy of 2 GiB (read + write)"}
+
+
 def bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma, steps):
     """Backward (dq, dk, dv with the selection held fixed) after one forward that
     keeps sel and lse; inputs and the upstream gradient resident in HBM.
@@ -304,6 +350,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the library GEMM and copy that measure the box's reachable rates")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -420,6 +468,14 @@ def main():
                  "mfma_frac": work["dense_flop"] / (dms * 1e-3) / 1e12 / peak_mfma}
         del dout
 
+    achievable = None
+    if not args.no_achievable:
+        print("[bench] achievable rates (library GEMM, device copy)", file=sys.stderr, flush=True)
+        achievable = measure_achievable(torch, dev, q.dtype)
+        if roofline is not None:
+            roofline["frac_of_achievable"] = round(roofline["achieved"] /
+                                                   achievable["mfma_tflops"], 4)
+
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -436,6 +492,12 @@ def main():
         backward = bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma,
                                   steps=max(1, min(args.steps, 5)))
 
+    if achievable is not None:
+        if decode is not None:
+            decode["hbm_frac_of_achievable"] = decode["achieved_gbs"] / achievable["hbm_gbs"]
+        if backward is not None:
+            backward["mfma_frac_of_achievable"] = (backward["achieved_tflops"] /
+                                                   achievable["mfma_tflops"])
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -454,6 +516,7 @@ def main():
                    "block_size": inp.block, "topk": inp.topk, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "achievable": achievable,
         "effective_attn_tflops": attn_flop / (ms * 1e-3) / 1e12,
         "attn_mfma_frac_of_step": attn_flop / (ms * 1e-3) / 1e12 / peak_mfma,
         "speedup_vs_dense": (dense["ms"] / ms) if dense else None,
