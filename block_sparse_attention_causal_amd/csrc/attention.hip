@@ -799,7 +799,7 @@ k_attn4(AttnArgs a) {
     float mx = vmax(s0[0], s1[0]);
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
-    mx = vmax(mx, swap_half(mx));
+    mx = vmax(mx, swap_half_valu(mx, lane));
     const float m_cand = vmax(m_run, mx * a.scale_log2);
     if (__ballot(m_cand > m_run + 8.f)) {
       const float alpha = fast_exp2(m_run - m_cand);   // 0 while m_run = -inf
@@ -833,7 +833,10 @@ k_attn4(AttnArgs a) {
   const int nch = (int)((kend - kbeg + KC - 1) / KC);
   const int row_stride = a.hkv * D;
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int c) __attribute__((always_inline)) {
+  // chunk c into LDS buffer `buf` (the loop passes both as known constants
+  // parities, so every LDS address of a chunk is a loop-invariant register plus
+  // an immediate offset)
+  auto issue = [&](int c, int buf) __attribute__((always_inline)) {
     const int64_t c0 = kbeg + (int64_t)min(c, nch - 1) * KC;
     const T* kb = k + (c0 * a.hkv + g) * D;
     const T* vb = v + (c0 * a.hkv + g) * D;
@@ -841,24 +844,38 @@ k_attn4(AttnArgs a) {
     // the range's last key: in bounds, and masked. (A selected block is whole
     // chunks: the block size is a multiple of 64.)
     const int last = (MODE == MODE_SELF) ? (int)min((int64_t)(KC - 1), kend - 1 - c0) : KC - 1;
-    const uint32_t dst = lds0 + (uint32_t)((c & 1) * DBUF * 2 + 16 * w * 256);
+    const uint32_t dst = lds0 + (uint32_t)(buf * DBUF * 2 + 16 * w * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * i + (lane >> 4);  // rows 16w .. 16w+15 of the chunk
       const int off = ((MODE == MODE_SELF) ? min(r, last) : r) * row_stride +
                       8 * ((lane & 15) ^ swz(r));
-      dma16(kb + off, dst + (uint32_t)(1024 * i));
-      dma16(vb + off, dst + (uint32_t)(KC * D * 2 + 1024 * i));
+      dma16s(kb, (uint32_t)off * 2u, dst + (uint32_t)(1024 * i));
+      dma16s(vb, (uint32_t)off * 2u, dst + (uint32_t)(KC * D * 2 + 1024 * i));
     }
   };
   // the Q fragments (compiler-visible loads) land before any direct load
   MOBA_WAIT_VM_LGKM0(0);
-  issue(0);
+  issue(0, 0);
   MOBA_WAIT_VM_LGKM0(0);
   bare_barrier();
-  for (int c = 0; c < nch; ++c) {
-    issue(c + 1);                                  // clamped past the end
-    compute(c & 1, kbeg + (int64_t)c * KC);
+  // two chunks per trip, buffers 0 then 1, and an odd last chunk after the loop
+  // (no exit in the middle of a trip: the compiler then keeps one register
+  // assignment for the running state)
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    issue(c + 1, 1);
+    compute(0, kbeg + (int64_t)c * KC);
+    MOBA_WAIT_VM_LGKM0(0);
+    bare_barrier();
+    issue(c + 2, 0);                               // clamped past the end
+    compute(1, kbeg + (int64_t)(c + 1) * KC);
+    MOBA_WAIT_VM_LGKM0(0);
+    bare_barrier();
+  }
+  if (c < nch) {
+    issue(c + 1, 1);                               // clamped: the last chunk again
+    compute(0, kbeg + (int64_t)c * KC);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }

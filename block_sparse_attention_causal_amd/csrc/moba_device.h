@@ -215,6 +215,30 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 #endif
 }
 
+// The same direct load with the address split into a wave-uniform 64-bit base
+// (read into SGPRs: it must be the same in every lane of the wave) and a 32-bit
+// per-lane byte offset: a loop whose offsets are invariant then spends no vector
+// instruction on addresses.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t b = (uint64_t)base;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("global_load_lds_dwordx4 %1, %2"
+               :
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
+               : "memory");
+#endif
+}
+
+// Lane i gets x of lane i ^ 32 (the other half of the wave), by the gfx950
+// cross-half swap on the vector ALU rather than an LDS permute.
+__device__ __forceinline__ float swap_half_valu(float x, int lane) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (lane < 32) ? r[1] : r[0]);
+}
+
 // A bare s_barrier (the host pass of the compiler sees only an empty body).
 __device__ __forceinline__ void bare_barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
