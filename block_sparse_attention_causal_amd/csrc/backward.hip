@@ -125,6 +125,7 @@ struct BwdArgs {
   int64_t nb, nlists, ntiles, padded;
   int nseq, hq, hkv, hg, block, ks, nu, kvt;   // kvt = key tiles per block
   float scale, scale_log2;
+  FastDiv div_ks, div_g;   // entry value -> row (/ ks), own row -> token (/ G)
 };
 
 // ---------------------------------------------------------------------------
@@ -580,14 +581,15 @@ k_bwd_dkdv_dma(BwdArgs a) {
         (nsel_rows > 0) ? a.entries + e_beg + min(max(idx, 0), nsel_rows - 1) : a.cu;
     dma4(src, lds_addr(&ent_lds[c & 7][w][0]));
   };
+  // branch-free: both candidates, then a select (entries past the list are
+  // clamped copies of valid ones, so the unused candidate is harmless)
   auto rowid_of = [&](int c, int r) __attribute__((always_inline)) -> int {
     const int rr = min(c, nch - 1) * BRC + r;
-    if (rr < nsel_rows) return ent_lds[c & 7][w][r] / a.ks;
-    if (rr < nrows) {
-      const int o = rr - nsel_rows, tb = o / G;
-      return rowl - tb * a.hq + (o - tb * G);
-    }
-    return 0;   // padding: any valid row, masked out
+    const int sel = (int)fdiv((uint32_t)ent_lds[c & 7][w][r], a.div_ks);
+    const uint32_t o = (uint32_t)max(rr - nsel_rows, 0);
+    const uint32_t tb = fdiv(o, a.div_g);
+    const int own = rowl - (int)tb * a.hq + (int)(o - tb * (uint32_t)G);
+    return (rr < nsel_rows) ? sel : (rr < nrows) ? own : 0;   // padding: any valid row
   };
   const int rA = 4 * w + (lane >> 4);
   const int offA = 8 * ((lane & 15) ^ swz(rA));
@@ -642,8 +644,9 @@ k_bwd_dkdv_dma(BwdArgs a) {
       for (int u = 0; u < 4; ++u) {
         const int e = 4 * jj + u;
         const int rr = rr0 + 8 * jj + 4 * half + u;
-        const bool masked = rr >= lim;
-        const float p = masked ? 0.f : fast_exp2(fmaf(s[e], a.scale_log2, -lv[u] * kLog2e));
+        // masked: exp2(-inf) = 0, no branch around the exponential
+        const float x = fmaf(s[e], a.scale_log2, -lv[u] * kLog2e);
+        const float p = fast_exp2((rr >= lim) ? -INFINITY : x);
         s[e] = p;
         dp[e] = p * (dp[e] - dl[u]);
       }
@@ -757,7 +760,7 @@ k_bwd_dq_dma(BwdArgs a) {
     if (e0 + r32 < e1) {
       const int32_t ev = a.entries[e0 + r32];
       dst_index = ev;
-      row = ev / a.ks;
+      row = fdiv((uint32_t)ev, a.div_ks);
     }
   } else {
     const int tt = 32 * (8 / a.hg);
@@ -827,17 +830,21 @@ k_bwd_dq_dma(BwdArgs a) {
         const bf16x8 vf = load8(vb + (32 * kt + r32) * D + 8 * ((2 * kk) ^ hx));
         dp[kt] = mma_k16(vf, gf[kk], dp[kt]);
       }
-    const int64_t tok = wtok0 + r32;
-    const bool need_mask = (MODE == BWD_SELF && c0 + BKC - 1 > wtok0) || (c0 + BKC > kend);
+    // SELECTED: a past block is whole 64-key chunks (the block size is a
+    // multiple of 64), nothing to mask. SELF: keys after the row's token (this
+    // covers the clamped keys past the tile's range, which follow every row of
+    // the tile); masked scores become -inf, so exp2 gives 0 without a branch.
+    const bool need_mask = (MODE == BWD_SELF) && (c0 + BKC - 1 > wtok0);
+    const int krel0 = (int)(c0 - wtok0) - r32 + 4 * half;   // key - token at e = 0, kt = 0
     bf16x8 df[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       float dsv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t key = c0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
-        const bool masked = need_mask && ((key >= kend) || (MODE == BWD_SELF && key > tok));
-        const float p = masked ? 0.f : fast_exp2(fmaf(s[kt][e], a.scale_log2, -lse_l2));
+        const float x = fmaf(s[kt][e], a.scale_log2, -lse_l2);
+        const bool masked = need_mask && (krel0 + 32 * kt + 8 * (e >> 2) + (e & 3) > 0);
+        const float p = fast_exp2(masked ? -INFINITY : x);
         dsv[e] = p * (dp[kt][e] - dlt);
       }
       df[2 * kt] = pack8<bf16>(&dsv[0]);
@@ -864,12 +871,13 @@ k_bwd_dq_dma(BwdArgs a) {
     const bf16* kp = k + (c0 * a.hkv + g) * D;
     const bf16* vp2 = v + (c0 * a.hkv + g) * D;
     const uint32_t dst = smem_lds + (uint32_t)((c & 3) * DBUF * 2 + 128 * w * 16);
-    const int offA = min(rowA, last) * row_stride + 8 * pieceA;
-    const int offB = min(rowB, last) * row_stride + 8 * pieceB;
-    dma16(kp + offA, dst);
-    dma16(kp + offB, dst + 1024u);
-    dma16(vp2 + offA, dst + (uint32_t)(BKC * D * 2));
-    dma16(vp2 + offB, dst + (uint32_t)(BKC * D * 2) + 1024u);
+    // byte offsets from the chunk's (wave-uniform) first key
+    const uint32_t offA = (uint32_t)(min(rowA, last) * row_stride + 8 * pieceA) * 2u;
+    const uint32_t offB = (uint32_t)(min(rowB, last) * row_stride + 8 * pieceB) * 2u;
+    dma16s(kp, offA, dst);
+    dma16s(kp, offB, dst + 1024u);
+    dma16s(vp2, offA, dst + (uint32_t)(BKC * D * 2));
+    dma16s(vp2, offB, dst + (uint32_t)(BKC * D * 2) + 1024u);
   };
   // the Q and dO fragments (compiler-visible loads) land before any direct load
   MOBA_WAIT_VM_LGKM0(0);
@@ -1061,6 +1069,8 @@ hipError_t launch_backward(const Plan& p, const void* q, const void* k, const vo
   a.ks = p.ks;
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
+  a.div_ks = make_fastdiv((uint32_t)(p.ks > 0 ? p.ks : 1));
+  a.div_g = make_fastdiv((uint32_t)(p.hq / p.hkv));
   if (p.dtype == MOBA_DTYPE_BF16)
     return p.d == 128 ? bwd_launch<bf16, 128>(a, p, out, delta, s)
                       : bwd_launch<bf16, 64>(a, p, out, delta, s);

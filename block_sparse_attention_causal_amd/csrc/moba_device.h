@@ -219,12 +219,18 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 // (read into SGPRs: it must be the same in every lane of the wave) and a 32-bit
 // per-lane byte offset: a loop whose offsets are invariant then spends no vector
 // instruction on addresses.
+// When the base is held in VGPRs (it depends on the wave index) the compiler
+// moves it to SGPRs with v_readfirstlane, a vector-ALU write of SGPRs, and a
+// memory instruction may read such SGPRs only five wait states later. The
+// compiler inserts those states before its own memory instructions but cannot
+// see into this asm, so the asm keeps them itself (s_nop 4): read sooner, the
+// load took a stale base and faulted.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint64_t b = (uint64_t)base;
   const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("global_load_lds_dwordx4 %1, %2"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
                : "memory");
@@ -237,6 +243,27 @@ __device__ __forceinline__ float swap_half_valu(float x, int lane) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __builtin_bit_cast(float, (lane < 32) ? r[1] : r[0]);
+}
+
+// Division of n in [0, 2^31) by a divisor d >= 1 fixed for a launch, as a
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994: the round-up multiplier with
+// s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1; t + n cannot overflow
+// because n < 2^31). Built on the host by make_fastdiv.
+struct FastDiv {
+  uint32_t m = 1, s = 0;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  if (d <= 1) return f;                            // m = 1, s = 0: n itself
+  uint32_t sh = 0;
+  while ((1ull << sh) < d) ++sh;
+  f.s = sh;
+  f.m = (uint32_t)((((1ull << sh) - d) << 32) / d + 1);
+  return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
 }
 
 // A bare s_barrier (the host pass of the compiler sees only an empty body).
