@@ -850,8 +850,13 @@ k_attn4(AttnArgs a) {
       const int r = 16 * w + 4 * i + (lane >> 4);  // rows 16w .. 16w+15 of the chunk
       const int off = ((MODE == MODE_SELF) ? min(r, last) : r) * row_stride +
                       8 * ((lane & 15) ^ swz(r));
-      dma16s(kb, (uint32_t)off * 2u, dst + (uint32_t)(1024 * i));
-      dma16s(vb, (uint32_t)off * 2u, dst + (uint32_t)(KC * D * 2 + 1024 * i));
+      if (i == 0) {                                // first loads from the chunk's bases
+        dma16s<true>(kb, (uint32_t)off * 2u, dst);
+        dma16s<true>(vb, (uint32_t)off * 2u, dst + (uint32_t)(KC * D * 2));
+      } else {
+        dma16s<false>(kb, (uint32_t)off * 2u, dst + (uint32_t)(1024 * i));
+        dma16s<false>(vb, (uint32_t)off * 2u, dst + (uint32_t)(KC * D * 2 + 1024 * i));
+      }
     }
   };
   // the Q fragments (compiler-visible loads) land before any direct load

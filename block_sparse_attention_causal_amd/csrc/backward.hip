@@ -874,10 +874,10 @@ k_bwd_dq_dma(BwdArgs a) {
     // byte offsets from the chunk's (wave-uniform) first key
     const uint32_t offA = (uint32_t)(min(rowA, last) * row_stride + 8 * pieceA) * 2u;
     const uint32_t offB = (uint32_t)(min(rowB, last) * row_stride + 8 * pieceB) * 2u;
-    dma16s(kp, offA, dst);
-    dma16s(kp, offB, dst + 1024u);
-    dma16s(vp2, offA, dst + (uint32_t)(BKC * D * 2));
-    dma16s(vp2, offB, dst + (uint32_t)(BKC * D * 2) + 1024u);
+    dma16s<true>(kp, offA, dst);                  // first loads from the chunk's bases
+    dma16s<false>(kp, offB, dst + 1024u);
+    dma16s<true>(vp2, offA, dst + (uint32_t)(BKC * D * 2));
+    dma16s<false>(vp2, offB, dst + (uint32_t)(BKC * D * 2) + 1024u);
   };
   // the Q and dO fragments (compiler-visible loads) land before any direct load
   MOBA_WAIT_VM_LGKM0(0);

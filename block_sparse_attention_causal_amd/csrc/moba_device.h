@@ -222,18 +222,27 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 // When the base is held in VGPRs (it depends on the wave index) the compiler
 // moves it to SGPRs with v_readfirstlane, a vector-ALU write of SGPRs, and a
 // memory instruction may read such SGPRs only five wait states later. The
-// compiler inserts those states before its own memory instructions but cannot
-// see into this asm, so the asm keeps them itself (s_nop 4): read sooner, the
-// load took a stale base and faulted.
+// compiler keeps that distance before its own memory instructions but cannot
+// see into this asm (read sooner, the load took a stale base and faulted), so
+// the first load from a newly formed base waits itself (kWait: s_nop 4); the
+// following loads from the same base come after it. A host test compiles the
+// kernels and checks that every such load has its five states.
+template <bool kWait>
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint64_t b = (uint64_t)base;
   const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
-               : "memory");
+  if constexpr (kWait)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
+                 : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %1, %2"
+                 :
+                 : "{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
+                 : "memory");
 #endif
 }
 
