@@ -20,6 +20,8 @@
 // same data to eight 32x32x2 MFMAs): a register operand from the accumulator
 // layout (dS^T, P, dS) pairs with an LDS operand transposed with the row order
 // of vt_pos_of_group4.
+#include <type_traits>
+
 #include "moba_plan.h"
 
 namespace moba {
@@ -35,7 +37,9 @@ constexpr int BKV_WAVES = 4;  // dK/dV pass: 4 waves x 32 keys = 128 keys per ti
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_bwd_delta(const T* __restrict__ out,
                                                    const T* __restrict__ dout, int64_t rows,
-                                                   float* __restrict__ delta) {
+                                                   const float* __restrict__ lse,
+                                                   float* __restrict__ delta,
+                                                   float* __restrict__ lse2) {
   constexpr int TPR = D / 8;
   const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
@@ -48,7 +52,10 @@ __global__ void __launch_bounds__(256) k_bwd_delta(const T* __restrict__ out,
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && c == 0) delta[row] = acc;
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;   // the dK/dV pass's exponent offset, in the log2 domain
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -111,6 +118,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;       // forward log-sum-exp per row (natural log)
   const float* delta;     // [T * hq]
+  const float* lse2;      // [T * hq] lse * log2(e)
   const int32_t* cu;
   const int32_t* blk_seq;
   const int32_t* blk_local;
@@ -600,7 +608,7 @@ k_bwd_dkdv_dma(BwdArgs a) {
     const uint32_t dst = rows_base + (uint32_t)((buf * RBUF + 4 * w * D) * 2);
     dma16(q + (int64_t)ridA * D + offA, dst);
     dma16(dout + (int64_t)ridA * D + offA, dst + (uint32_t)(CH * 2));
-    dma4((lane < 32) ? a.lse + ridM : a.delta + ridM, lds_addr(&meta_lds[buf][w][0]));
+    dma4((lane < 32) ? a.lse2 + ridM : a.delta + ridM, lds_addr(&meta_lds[buf][w][0]));
   };
 
   const int hx = half ^ swz(r32);
@@ -645,7 +653,7 @@ k_bwd_dkdv_dma(BwdArgs a) {
         const int e = 4 * jj + u;
         const int rr = rr0 + 8 * jj + 4 * half + u;
         // masked: exp2(-inf) = 0, no branch around the exponential
-        const float x = fmaf(s[e], a.scale_log2, -lv[u] * kLog2e);
+        const float x = fmaf(s[e], a.scale_log2, -lv[u]);
         const float p = fast_exp2((rr >= lim) ? -INFINITY : x);
         s[e] = p;
         dp[e] = p * (dp[e] - dl[u]);
@@ -837,19 +845,26 @@ k_bwd_dq_dma(BwdArgs a) {
     const bool need_mask = (MODE == BWD_SELF) && (c0 + BKC - 1 > wtok0);
     const int krel0 = (int)(c0 - wtok0) - r32 + 4 * half;   // key - token at e = 0, kt = 0
     bf16x8 df[4];
+    auto grads = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float dsv[16];
+      for (int kt = 0; kt < 2; ++kt) {
+        float dsv[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float x = fmaf(s[kt][e], a.scale_log2, -lse_l2);
-        const bool masked = need_mask && (krel0 + 32 * kt + 8 * (e >> 2) + (e & 3) > 0);
-        const float p = fast_exp2(masked ? -INFINITY : x);
-        dsv[e] = p * (dp[kt][e] - dlt);
+        for (int e = 0; e < 16; ++e) {
+          float x = fmaf(s[kt][e], a.scale_log2, -lse_l2);
+          if constexpr (decltype(masked)::value)
+            x = (krel0 + 32 * kt + 8 * (e >> 2) + (e & 3) > 0) ? -INFINITY : x;
+          const float p = fast_exp2(x);
+          dsv[e] = p * (dp[kt][e] - dlt);
+        }
+        df[2 * kt] = pack8<bf16>(&dsv[0]);
+        df[2 * kt + 1] = pack8<bf16>(&dsv[8]);
       }
-      df[2 * kt] = pack8<bf16>(&dsv[0]);
-      df[2 * kt + 1] = pack8<bf16>(&dsv[8]);
-    }
+    };
+    if (need_mask)
+      grads(std::true_type{});
+    else
+      grads(std::false_type{});
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -990,12 +1005,12 @@ k_bwd_dq_dma(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out,
-                             float* delta, hipStream_t s) {
+                             float* delta, float* lse2, hipStream_t s) {
   const int64_t rows = p.T * p.hq;
   {
     const int rpw = 256 / (D / 8);
     hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256),
-                       0, s, (const T*)out, (const T*)base.dout, rows, delta);
+                       0, s, (const T*)out, (const T*)base.dout, rows, base.lse, delta, lse2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1038,7 +1053,8 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
 
 hipError_t launch_backward(const Plan& p, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const void* dout,
-                           const int32_t* cu_dev, const Work& w, float* delta, float* dq_sel,
+                           const int32_t* cu_dev, const Work& w, float* delta, float* lse2,
+                           float* dq_sel,
                            void* dq, void* dk, void* dv, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   BwdArgs a = {};
@@ -1048,6 +1064,7 @@ hipError_t launch_backward(const Plan& p, const void* q, const void* k, const vo
   a.dout = dout;
   a.lse = lse;
   a.delta = delta;
+  a.lse2 = lse2;
   a.cu = cu_dev;
   a.blk_seq = w.blk_seq;
   a.blk_local = w.blk_local;
@@ -1072,10 +1089,10 @@ hipError_t launch_backward(const Plan& p, const void* q, const void* k, const vo
   a.div_ks = make_fastdiv((uint32_t)(p.ks > 0 ? p.ks : 1));
   a.div_g = make_fastdiv((uint32_t)(p.hq / p.hkv));
   if (p.dtype == MOBA_DTYPE_BF16)
-    return p.d == 128 ? bwd_launch<bf16, 128>(a, p, out, delta, s)
-                      : bwd_launch<bf16, 64>(a, p, out, delta, s);
-  return p.d == 128 ? bwd_launch<float, 128>(a, p, out, delta, s)
-                    : bwd_launch<float, 64>(a, p, out, delta, s);
+    return p.d == 128 ? bwd_launch<bf16, 128>(a, p, out, delta, lse2, s)
+                      : bwd_launch<bf16, 64>(a, p, out, delta, lse2, s);
+  return p.d == 128 ? bwd_launch<float, 128>(a, p, out, delta, lse2, s)
+                    : bwd_launch<float, 64>(a, p, out, delta, lse2, s);
 }
 
 }  // namespace moba

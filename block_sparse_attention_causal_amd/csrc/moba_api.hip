@@ -294,7 +294,7 @@ static moba_status_t make_decode_plan(const int32_t* cu_q, const int32_t* cu_k, 
 // parts in place of the forward's partial outputs (fp32, indexed like them by
 // row * ks + slot) and Delta per row.
 struct BwdLayout {
-  size_t off_delta = 0, off_dq_sel = 0, total = 0;
+  size_t off_delta = 0, off_lse2 = 0, off_dq_sel = 0, total = 0;
 };
 
 static BwdLayout backward_layout(const Plan& p) {
@@ -303,6 +303,8 @@ static BwdLayout backward_layout(const Plan& p) {
   l.off_dq_sel = off;
   off = align256(off + sizeof(float) * (size_t)(p.T * p.hq) * p.ks * p.d);
   l.off_delta = off;
+  off = align256(off + sizeof(float) * (size_t)(p.T * p.hq));
+  l.off_lse2 = off;                                // the forward's LSE times log2(e)
   off = align256(off + sizeof(float) * (size_t)(p.T * p.hq));
   l.total = std::max(off, p.total);
   return l;
@@ -580,6 +582,7 @@ moba_status_t moba_backward(const void* q, const void* k, const void* v, const v
   Work w = carve(p, workspace);
   char* b = (char*)workspace;
   float* delta = (float*)(b + bl.off_delta);
+  float* lse2 = (float*)(b + bl.off_lse2);
   float* dq_sel = (float*)(b + bl.off_dq_sel);
   hipError_t e = launch_setup(p, cu_seqlens_dev, w, s);
   if (e != hipSuccess) return hip_status(e, "setup");
@@ -590,8 +593,8 @@ moba_status_t moba_backward(const void* q, const void* k, const void* v, const v
   if (e != hipSuccess) return hip_status(e, "route");
   {
     StageScope t(ST_BACKWARD, s);
-    e = launch_backward(p, q, k, v, out, lse, dout, cu_seqlens_dev, w, delta, dq_sel, dq, dk,
-                        dv, s);
+    e = launch_backward(p, q, k, v, out, lse, dout, cu_seqlens_dev, w, delta, lse2, dq_sel, dq,
+                        dk, dv, s);
   }
   if (e != hipSuccess) return hip_status(e, "backward");
   g_err[0] = 0;

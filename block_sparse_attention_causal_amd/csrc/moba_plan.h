@@ -112,8 +112,8 @@ hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const 
 // ---- backward (NEXT-1) --------------------------------------------------------
 hipError_t launch_backward(const Plan& p, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const void* dout,
-                           const int32_t* cu_dev, const Work& w, float* delta, float* dq_sel,
-                           void* dq, void* dk, void* dv, hipStream_t s);
+                           const int32_t* cu_dev, const Work& w, float* delta, float* lse2,
+                           float* dq_sel, void* dq, void* dk, void* dv, hipStream_t s);
 
 // ---- decoding against a KV cache (NEXT-2) ----------------------------------
 struct DecodeArgs {
