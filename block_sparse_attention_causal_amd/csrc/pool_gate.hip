@@ -603,24 +603,28 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
       issue(st + GB - 1);
       f32x16 acc;
       scores(st, acc);
-      const float mx = max16(acc);
-      if (mx > ws) {
-        const int j0 = st * 32;
+      // Insert the lane's scores above the cut best first, one per trip (a lane
+      // rarely has more than one): the element equal to the maximum with the
+      // lowest block, then its score is taken out and the maximum recomputed.
+      // Scores of one chunk follow every listed block, so a score equal to the
+      // cut loses the tie and need not be tried; the list's order is total, so
+      // the order of insertion does not change what it keeps.
+      float mx = max16(acc);
+      const int j0 = st * 32;
+      while (mx > ws) {
+        int eb = 15;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (acc[e] > ws) {
-            out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, acc[e],
-                                                    j0 + 8 * (e >> 2) + 4 * half + (e & 3)));
+        for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
+        out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, mx,
+                                                j0 + 8 * (eb >> 2) + 4 * half + (eb & 3)));
 #pragma unroll
-            for (int p = 0; p < KB; ++p)
-              if (p == ks - 1) ws = bs[p];
-          } else {
-            out_max = vmax(out_max, acc[e]);
-          }
-        }
-      } else {
-        out_max = vmax(out_max, mx);
+        for (int p = 0; p < KB; ++p)
+          if (p == ks - 1) ws = bs[p];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
+        mx = max16(acc);
       }
+      out_max = vmax(out_max, mx);   // the best of the scores left out
       MOBA_WAIT_VM_LGKM0(GB - 2);
       bare_barrier();
     }
