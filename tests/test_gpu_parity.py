@@ -123,6 +123,42 @@ def test_gate_near_ties_match_oracle():
     assert err <= 2e-2, err
 
 
+@pytest.mark.parametrize("topk", [3, 6])
+def test_gate_exact_ties_pick_lowest_blocks(topk):
+    """Every block of every sequence has the same keys, so every past block scores
+    the same for a row: the tie rule alone decides, and each row must keep its
+    min(topk-1, i) lowest past blocks (the oracle's selection), on the screened
+    path (topk 3) and on the exact gate (topk 6)."""
+    _say("gate exact ties bf16 [1000, 650] hq=4 hkv=2 d=128 block=64 topk=%d" % topk)
+    seqlens, block, d = [1000, 650], 64, 128
+    inp = make_inputs(seqlens, 4, 2, d, block, topk, dtype="bf16", seed=12, plant=False)
+    g = torch.Generator().manual_seed(13)
+    base = torch.randn(block, 2, d, generator=g)
+    k = []
+    for s in seqlens:
+        for j in range((s + block - 1) // block):
+            k.append(base[:min(block, s - j * block)])
+    inp.k = torch.cat(k).to(torch.bfloat16).contiguous()
+    inp = _to_gpu(inp)
+    out, sel, lse = _run(inp)
+    ref = oracle.all_rows(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.block, inp.topk)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    # the rule by itself: ascending lowest blocks, -1 padded
+    sel_np = sel.cpu().numpy()
+    start = 0
+    for s in seqlens:
+        tok = np.arange(s)
+        i = tok // block
+        want = np.full((s, topk - 1), -1, dtype=np.int32)
+        for c in range(topk - 1):
+            want[:, c] = np.where(c < i, c, -1)
+        for h in range(4):
+            np.testing.assert_array_equal(sel_np[start:start + s, h], want)
+        start += s
+    err = np.abs(out.float().cpu().numpy() - ref["out"]).max()
+    assert err <= 2e-2, err
+
+
 def test_pool_matches_oracle():
     for seqlens, hkv, d, block, dt in (([2048], 1, 64, 256, "f32"), ([1000, 0, 2300, 129], 2,
                                                                        128, 256, "bf16"),
