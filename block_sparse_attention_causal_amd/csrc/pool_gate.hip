@@ -416,20 +416,28 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
         for (int e = 0; e < 16; ++e)
           if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
       }
-      float mx = acc[0];
+      // best first, one score per trip (as in k_gate_fast): the wave runs as
+      // many trips as its busiest lane needs, rather than one insertion for
+      // every position at which any lane has a candidate
+      auto max16 = [&]() __attribute__((always_inline)) {
+        float m = acc[0];
 #pragma unroll
-      for (int e = 1; e < 16; e += 2)
-        mx = (e + 1 < 16) ? vmax(vmax(mx, acc[e]), acc[e + 1]) : vmax(mx, acc[e]);
-      if (mx > ws) {
+        for (int e = 1; e < 16; e += 2)
+          m = (e + 1 < 16) ? vmax(vmax(m, acc[e]), acc[e + 1]) : vmax(m, acc[e]);
+        return m;
+      };
+      float mx = max16();
+      while (mx > ws) {
+        int eb = 15;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (acc[e] > ws) {
-            list_insert<KB>(bs, bj, ks, acc[e], j0 + 8 * (e >> 2) + 4 * half + (e & 3));
+        for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
+        list_insert<KB>(bs, bj, ks, mx, j0 + 8 * (eb >> 2) + 4 * half + (eb & 3));
 #pragma unroll
-            for (int p = 0; p < KB; ++p)
-              if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
-          }
-        }
+        for (int p = 0; p < KB; ++p)
+          if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
+        mx = max16();
       }
       if (j0 + 32 < i) stash(buf ^ 1);
       __syncthreads();
