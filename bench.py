@@ -62,6 +62,10 @@ def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
         "pool_bytes": elem_bytes * T * hkv * d + 4.0 * nb_total * hkv * d,
         "gate_bytes": elem_bytes * T * hq * d + 4.0 * T * hq * ks,
         "merge_bytes": hq * sel_parts * (part_bytes * d + 4.0) + elem_bytes * T * hq * d,
+        # route: the counting sort reads the selection (4 B per (row, slot)) for
+        # the histograms and again for the scatter, and writes one 4-byte entry
+        # per routed (row, slot)
+        "route_bytes": 12.0 * hq * sel_parts,
     }
 
 
@@ -429,6 +433,7 @@ def main():
             if name == "attn_self":
                 # its epilogue also streams the merge's bytes
                 rep["merge_gbs"] = work["merge_bytes"] / (avg * 1e-3) / 1e9
+                rep["merge_hbm_frac"] = rep["merge_gbs"] / PEAK_HBM_GBS
         elif name == "gate":
             gbs = work["gate_bytes"] / (avg * 1e-3) / 1e9
             tf = work["gate_flop"] / (avg * 1e-3) / 1e12
@@ -436,7 +441,7 @@ def main():
             # add three more): both the HBM and the matrix-core fraction
             rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
                        achieved_tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
-        elif name == "pool":
+        elif name in ("pool", "route"):
             gbs = work[name + "_bytes"] / (avg * 1e-3) / 1e9
             rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)
         stage_rep[name] = rep

@@ -278,6 +278,9 @@ def test_bench_work_counts_closed_forms():
     assert abs(w["attn_self_flop"] / 1e12 - 17.60) < 0.01
     assert abs(w["attn_selected_flop"] / 1e12 - 70.16) < 0.01
     assert abs(w["gate_flop"] / 1e12 - 2.19) < 0.01
+    # route bytes: 12 per routed (row, slot); 1M: 0.803 GB
+    assert w["route_bytes"] == 12.0 * hq * B * (ks * nb - ks * (ks + 1) // 2)
+    assert abs(w["route_bytes"] / 1e9 - 0.803) < 0.001
 
 
 def test_bench_refuses_several_gpus():
