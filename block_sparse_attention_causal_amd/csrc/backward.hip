@@ -126,7 +126,8 @@ struct BwdArgs {
   const int32_t* list_offsets;
   const int32_t* tile_offsets;
   const int32_t* entries;
-  float* dq_sel;          // [T * hq * ks, D] selected-block dQ parts (scaled), by entry value
+  float* dq_sel;          // [T * hq * ks, D] selected-block dQ parts (scaled), by entry value:
+                          // fp32, or bf16 (the first half of the buffer) for 16-bit D = 128
   void* dq;               // [T, hq, D]
   void* dk;               // [T, hkv, D]
   void* dv;
@@ -911,30 +912,33 @@ k_bwd_dq_dma(BwdArgs a) {
 
   // epilogue: lane holds dQ^T[32dt + 8(i/4) + 4half + i%4][row r32]
   if (MODE == BWD_SELECTED) {
-    // fp32 parts through LDS, half a row (64 values) at a time, so that every
-    // store instruction writes whole 256-byte half rows: written 32 bytes per
-    // row at a time, the parts cost as many DRAM bytes again in reads
-    constexpr int SLD = 64 + 4;                    // padded staging row (floats)
-    float* stage = reinterpret_cast<float*>(smem) + w * 32 * SLD;
+    // bf16 parts (half the bytes of fp32 each way, and within the gradients'
+    // 2e-2 bar: a part is rounded once, relative 2^-9) through LDS, so every
+    // store writes whole 256-byte rows (written 8 bytes per row at a time, the
+    // parts had cost as many DRAM bytes again in reads)
+    typedef bf16 b4 __attribute__((ext_vector_type(4)));
+    typedef bf16 b8 __attribute__((ext_vector_type(8)));
+    constexpr int SLD = D + 8;                     // padded staging row (bf16)
+    bf16* stage = reinterpret_cast<bf16*>(smem) + w * 32 * SLD;
+    bf16* parts = reinterpret_cast<bf16*>(a.dq_sel);
+    __syncthreads();     // every wave's direct loads have landed and its products are done
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      __syncthreads();   // every wave's direct loads have landed and its products are done
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int dt = 2 * hh; dt < 2 * hh + 2; ++dt)
+      for (int aa = 0; aa < 4; ++aa) {
+        b4 v;
 #pragma unroll
-        for (int aa = 0; aa < 4; ++aa)
-          *reinterpret_cast<float4*>(stage + r32 * SLD + 32 * (dt - 2 * hh) + 8 * aa + 4 * half) =
-              make_float4(acc[dt][4 * aa] * a.scale, acc[dt][4 * aa + 1] * a.scale,
-                          acc[dt][4 * aa + 2] * a.scale, acc[dt][4 * aa + 3] * a.scale);
-      __syncthreads();
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int rr = 4 * it + (lane >> 4), pc = lane & 15;
-        const int64_t di = __shfl(dst_index, rr, 64);
-        if (di >= 0)
-          __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + rr * SLD + 4 * pc),
-                                      reinterpret_cast<f32x4*>(a.dq_sel + di * D + 64 * hh + 4 * pc));
+        for (int bb = 0; bb < 4; ++bb) v[bb] = (bf16)(acc[dt][4 * aa + bb] * a.scale);
+        *reinterpret_cast<b4*>(stage + r32 * SLD + 32 * dt + 8 * aa + 4 * half) = v;
       }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rr = 4 * it + (lane >> 4), pc = lane & 15;
+      const int64_t di = __shfl(dst_index, rr, 64);
+      if (di >= 0)
+        __builtin_nontemporal_store(*reinterpret_cast<const b8*>(stage + rr * SLD + 8 * pc),
+                                    reinterpret_cast<b8*>(parts + di * D + 8 * pc));
     }
     return;
   }
@@ -950,6 +954,9 @@ k_bwd_dq_dma(BwdArgs a) {
       for (int aa = 0; aa < 4; ++aa)
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) x[dt][aa][bb] = acc[dt][4 * aa + bb] * a.scale;
+    // the selected pass's bf16 parts of this row
+    typedef bf16 b4 __attribute__((ext_vector_type(4)));
+    const bf16* parts = reinterpret_cast<const bf16*>(a.dq_sel);
     if (a.ks <= 2) {
       // every part load of the row at once (a missing part reads entry 0, always
       // allocated, and is dropped), so the epilogue pays one memory latency
@@ -957,35 +964,29 @@ k_bwd_dq_dma(BwdArgs a) {
       for (int sl = 0; sl < 2; ++sl) {
         const bool valid = sl < nsel;
         const int64_t e = valid ? dst_index * a.ks + sl : 0;
-        float4 pt[D / 32][4];
+        b4 pt[D / 32][4];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int aa = 0; aa < 4; ++aa)
-            pt[dt][aa] = *reinterpret_cast<const float4*>(a.dq_sel + e * D + 32 * dt + 8 * aa +
-                                                          4 * half);
+            pt[dt][aa] = *reinterpret_cast<const b4*>(parts + e * D + 32 * dt + 8 * aa + 4 * half);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int aa = 0; aa < 4; ++aa) {
-            x[dt][aa][0] += valid ? pt[dt][aa].x : 0.f;
-            x[dt][aa][1] += valid ? pt[dt][aa].y : 0.f;
-            x[dt][aa][2] += valid ? pt[dt][aa].z : 0.f;
-            x[dt][aa][3] += valid ? pt[dt][aa].w : 0.f;
-          }
+          for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) x[dt][aa][bb] += valid ? (float)pt[dt][aa][bb] : 0.f;
       }
     } else {
       for (int sl = 0; sl < nsel; ++sl) {
-        const float* src = a.dq_sel + (dst_index * a.ks + sl) * D;
+        const bf16* src = parts + (dst_index * a.ks + sl) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int aa = 0; aa < 4; ++aa) {
-            const float4 pt = *reinterpret_cast<const float4*>(src + 32 * dt + 8 * aa + 4 * half);
-            x[dt][aa][0] += pt.x;
-            x[dt][aa][1] += pt.y;
-            x[dt][aa][2] += pt.z;
-            x[dt][aa][3] += pt.w;
+            const b4 pt = *reinterpret_cast<const b4*>(src + 32 * dt + 8 * aa + 4 * half);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) x[dt][aa][bb] += (float)pt[bb];
           }
       }
     }
