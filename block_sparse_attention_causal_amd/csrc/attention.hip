@@ -692,6 +692,8 @@ k_attn4(AttnArgs a) {
   int64_t wtok0 = 0;          // SELF: the wave's first token
   bool wave_live = true;      // SELF: the wave has rows
   int blk_i = 0;              // SELF: the tile's block index in its sequence
+  int64_t wrow0 = 0;          // SELF: output row of the wave's first token
+  int wrows = 0;              // SELF: rows of the wave inside the block (0 .. 32)
   if constexpr (MODE == MODE_SELECTED) {
     const int64_t tile = logical;
     const int32_t* toffs = a.tile_offsets;
@@ -729,6 +731,8 @@ k_attn4(AttnArgs a) {
     g = h / group;
     wtok0 = tok0 + (int64_t)(w / hw) * 32;
     wave_live = wtok0 < blk_end;
+    wrow0 = wtok0 * a.hq + h;
+    wrows = (int)max((int64_t)0, min((int64_t)32, blk_end - wtok0));
     kbeg = blk_start;
     kend = min(tok0 + tt, blk_end);
     if (wtok0 + r32 < blk_end) {
@@ -740,6 +744,16 @@ k_attn4(AttnArgs a) {
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     qf[kk] = (row >= 0) ? load8_stream(q + row * D + 16 * kk + 8 * half) : zero8<frag_t>();
+  // SELF with selected blocks: the epilogue merges the row's parts from LDS.
+  // Part 0 is loaded during the last chunk into the buffer that chunk leaves
+  // free, the others after the loop; the LSE of parts 0 and 1 come with Q.
+  const int nsel = (MODE == MODE_SELF) ? min(a.ks, blk_i) : 0;
+  const bool pref = MODE == MODE_SELF && nsel > 0;
+  float lsel0 = -INFINITY, lsel1 = -INFINITY;
+  if (pref && row >= 0) {
+    lsel0 = a.sel_lse[dst_index * a.ks];
+    if (nsel > 1) lsel1 = a.sel_lse[dst_index * a.ks + 1];
+  }
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -859,6 +873,24 @@ k_attn4(AttnArgs a) {
       }
     }
   };
+  // Part `part` of the wave's 32 rows into LDS buffer `buf`: the wave's 8 KB
+  // quarter, row r at 256 r, piece p of the row at position p ^ swz(r) (the
+  // 16-byte pieces of a row spread over the banks, so that the epilogue's reads
+  // of one piece of 16 rows hit distinct banks). Rows past the block repeat its
+  // last row; a wave without rows loads nothing.
+  auto issue_part = [&](int part, int buf) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    const char* pb = (const char*)a.sel_o + (((wrow0 * a.ks) + part) << 8);
+    const uint32_t rbytes = (uint32_t)(a.hq * a.ks) << 8;   // one token to the next
+    const uint32_t dst = lds0 + (uint32_t)(buf * DBUF * 2 + w * 8192);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint32_t off = (uint32_t)min(r, wrows - 1) * rbytes + 16u * ((lane & 15) ^ swz(r));
+      if (i == 0) dma16s<true>(pb, off, dst);
+      else dma16s<false>(pb, off, dst + (uint32_t)(1024 * i));
+    }
+  };
   // the Q fragments (compiler-visible loads) land before any direct load
   MOBA_WAIT_VM_LGKM0(0);
   issue(0, 0);
@@ -873,13 +905,15 @@ k_attn4(AttnArgs a) {
     compute(0, kbeg + (int64_t)c * KC);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
-    issue(c + 2, 0);                               // clamped past the end
+    if (pref && c + 2 >= nch) issue_part(0, 0);    // the last chunk: part 0
+    else issue(c + 2, 0);                          // (clamped past the end)
     compute(1, kbeg + (int64_t)(c + 1) * KC);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }
   if (c < nch) {
-    issue(c + 1, 1);                               // clamped: the last chunk again
+    if (pref) issue_part(0, 1);
+    else issue(c + 1, 1);                          // clamped: the last chunk again
     compute(0, kbeg + (int64_t)c * KC);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
@@ -891,8 +925,52 @@ k_attn4(AttnArgs a) {
     if (row >= 0 && half == 0) a.lse_part[dst_index] = lse;
     store_rows<PT, D>((PT*)a.o_part, (char*)lds, o, inv, dst_index, w, lane);
   } else {
-    if (a.ks > 0) {
-      merge_rows<T, D>(a, (char*)lds, o, inv, lse, dst_index, min(a.ks, blk_i), w, lane);
+    if (pref) {
+      // Kimi发布MoBA突破性实现无限上下文, "PyTorch实现关键要点": the parts (own
+      // block and the selected blocks, disjoint key sets) combine with the
+      // online-softmax rule, out = sum_p e^(lse_p - m) o_p / sum_p e^(lse_p - m)
+      // with m the largest lse_p. Each lane combines its own accumulator slivers
+      // with the same slivers of the parts, read from LDS, two parts at a time
+      // (one per buffer), rescaling what it holds when the maximum grows. Every
+      // wave reads only the quarter of each buffer that it loaded itself.
+      const int pb0 = nch & 1;                     // buffer holding part 0
+      typedef PT pvec4_t __attribute__((ext_vector_type(4)));
+      const char* rp = (const char*)lds + w * 8192 + r32 * 256 + 8 * half;
+      float m = lse, den = 1.f, sc = inv;
+      for (int sl = 0; sl < nsel; sl += 2) {
+        const bool two = sl + 1 < nsel;
+        float la = lsel0, lb = lsel1;
+        if (sl > 0) {
+          issue_part(sl, pb0);
+          la = (row >= 0) ? a.sel_lse[dst_index * a.ks + sl] : -INFINITY;
+          lb = (row >= 0 && two) ? a.sel_lse[dst_index * a.ks + sl + 1] : -INFINITY;
+        }
+        if (two) issue_part(sl + 1, pb0 ^ 1);      // (part 1: the last chunk's buffer)
+        MOBA_WAIT_VM_LGKM0(0);
+        bare_barrier();
+        const float mn = fmaxf(fmaxf(m, la), lb);
+        const float alpha = fast_exp2((m - mn) * kLog2e);
+        const float wa = fast_exp2((la - mn) * kLog2e);
+        const float wb = two ? fast_exp2((lb - mn) * kLog2e) : 0.f;
+        den = den * alpha + wa + wb;
+        const float so = sc * alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa) {
+            const int pos = 16 * ((4 * dt + aa) ^ swz(r32));
+            const pvec4_t xa = *(const pvec4_t*)(rp + pb0 * DBUF * 2 + pos);
+            pvec4_t xb = pvec4_t{};
+            if (two) xb = *(const pvec4_t*)(rp + (pb0 ^ 1) * DBUF * 2 + pos);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[dt][4 * aa + e] = o[dt][4 * aa + e] * so + to_f32(xa[e]) * wa + to_f32(xb[e]) * wb;
+          }
+        m = mn;
+        sc = 1.f;
+      }
+      if (row >= 0 && half == 0 && a.lse_out) a.lse_out[dst_index] = m + fast_log2(den) * kLn2;
+      store_rows<T, D>((T*)a.out, (char*)lds, o, 1.f / den, dst_index, w, lane);
     } else {
       if (row >= 0 && half == 0 && a.lse_out) a.lse_out[dst_index] = lse;
       store_rows<T, D>((T*)a.out, (char*)lds, o, inv, dst_index, w, lane);
