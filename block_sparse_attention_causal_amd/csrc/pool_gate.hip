@@ -503,7 +503,7 @@ __global__ void __launch_bounds__(256) k_gate_bound(const int32_t* __restrict__ 
   if (threadIdx.x == 0) bound[blockIdx.x] = vmax(vmax(red[0], red[1]), vmax(red[2], red[3]));
 }
 
-template <int D, int KB>
+template <int D, int KB, bool CHAIN>
 __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ blk_base,
@@ -611,32 +611,80 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
       issue(st + GB - 1);
       f32x16 acc;
       scores(st, acc);
-      // Insert the lane's scores above the cut best first, one per trip (a lane
-      // rarely has more than one): the element equal to the maximum with the
-      // lowest block, then its score is taken out and the maximum recomputed.
-      // Scores of one chunk follow every listed block, so a score equal to the
-      // cut loses the tie and need not be tried; the list's order is total, so
-      // the order of insertion does not change what it keeps.
-      float mx = max16(acc);
-      const int j0 = st * 32;
-      while (mx > ws) {
-        int eb = 15;
+      if constexpr (CHAIN) {
+        // Few chunks (sequences of up to 512 blocks), where many scores still
+        // enter: every score passes through the lane's list without a branch,
+        // in ascending block order. With the scores t sorted descending,
+        // admitting s gives t'_0 = max(t_0, s) and t'_p = med3(t_{p-1}, t_p, s);
+        // an entry's block moves down one place where s beats the entry above
+        // it, and s takes the first place whose entry it beats (strictly: an
+        // equal score from a later block ranks after). The score that falls off
+        // the end, min(t_last, s), is left out; since nothing left out exceeds
+        // t_last, the best of them updates as med3(out, t_last, s). The list
+        // holds all KB >= ks entries. A block is kept as its position e in its
+        // chunk minus 16 for every chunk since (e is then an instruction
+        // constant), decoded after the loop; an entry whose score is still -inf
+        // never held a block.
 #pragma unroll
-        for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
-        out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, mx,
-                                                j0 + 8 * (eb >> 2) + 4 * half + (eb & 3)));
+        for (int p = 0; p < KB; ++p) bj[p] -= 16;
 #pragma unroll
-        for (int p = 0; p < KB; ++p)
-          if (p == ks - 1) ws = bs[p];
+        for (int e = 0; e < 16; ++e) {
+          const float sc = acc[e];
+          bool c[KB];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
-        mx = max16(acc);
+          for (int p = 0; p < KB; ++p) c[p] = sc > bs[p];
+          out_max = __builtin_amdgcn_fmed3f(out_max, bs[KB - 1], sc);
+#pragma unroll
+          for (int p = KB - 1; p > 0; --p) {
+            bj[p] = c[p - 1] ? bj[p - 1] : (c[p] ? e : bj[p]);
+            bs[p] = __builtin_amdgcn_fmed3f(bs[p - 1], bs[p], sc);
+          }
+          bj[0] = c[0] ? e : bj[0];
+          bs[0] = vmax(bs[0], sc);
+        }
+      } else {
+        // Insert the lane's scores above the cut best first, one per trip (a lane
+        // rarely has more than one): the element equal to the maximum with the
+        // lowest block, then its score is taken out and the maximum recomputed.
+        // Scores of one chunk follow every listed block, so a score equal to the
+        // cut loses the tie and need not be tried; the list's order is total, so
+        // the order of insertion does not change what it keeps.
+        float mx = max16(acc);
+        const int j0 = st * 32;
+        while (mx > ws) {
+          int eb = 15;
+#pragma unroll
+          for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
+          out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, mx,
+                                                  j0 + 8 * (eb >> 2) + 4 * half + (eb & 3)));
+#pragma unroll
+          for (int p = 0; p < KB; ++p)
+            if (p == ks - 1) ws = bs[p];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
+          mx = max16(acc);
+        }
+        out_max = vmax(out_max, mx);   // the best of the scores left out
       }
-      out_max = vmax(out_max, mx);   // the best of the scores left out
       MOBA_WAIT_VM_LGKM0(GB - 2);
       bare_barrier();
     }
     MOBA_WAIT_VM_LGKM0(0);
+    if constexpr (CHAIN) {
+      // positions to blocks; entries past ks are left out too
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        const int cd = bj[p] + 16 * (nsteps - 1);  // 16 st + e
+        bj[p] = (bs[p] == -INFINITY)
+                    ? kNoBlock
+                    : 32 * (cd >> 4) + 8 * ((cd & 15) >> 2) + 4 * half + (cd & 3);
+        if (p >= ks) {
+          out_max = vmax(out_max, bs[p]);
+          bs[p] = -INFINITY;
+          bj[p] = kNoBlock;
+        }
+      }
+    }
     float os[KB];
     int oj[KB];
 #pragma unroll
@@ -709,12 +757,19 @@ template <int D>
 static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, const Work& w,
                                int32_t* sel, hipStream_t s, int64_t ntiles, int64_t padded) {
   dim3 grid((unsigned)padded), blk(512);
-#define MOBA_GATE_FAST(KBV)                                                                     \
-  hipLaunchKernelGGL((k_gate_fast<D, KBV>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,      \
+#define MOBA_GATE_FAST(KBV, CH)                                                                 \
+  hipLaunchKernelGGL((k_gate_fast<D, KBV, CH>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,  \
                      w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
                      p.ks, ntiles, padded, w.gate_flags, sel)
-  if (p.ks <= 2) MOBA_GATE_FAST(2);
-  else MOBA_GATE_FAST(4);
+  // branch-free list updates pay while a row has at most 16 chunks of 32 blocks
+  const bool chain = p.max_nb <= 512;
+  if (p.ks <= 2) {
+    if (chain) MOBA_GATE_FAST(2, true);
+    else MOBA_GATE_FAST(2, false);
+  } else {
+    if (chain) MOBA_GATE_FAST(4, true);
+    else MOBA_GATE_FAST(4, false);
+  }
 #undef MOBA_GATE_FAST
 }
 
