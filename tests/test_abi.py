@@ -246,6 +246,7 @@ def test_profiling_kernel_keys():
         "_ZN4moba6k_attnIDF16bLi128ELi2EEEvNS_8AttnArgsE": "attn_dense",
         "_ZN4moba6k_gateIDF16bLi128ELi3ELi2EEEvPKT_PKiS5_S5_S5_S3_liiiiillPKhPi": "gate",
         "_ZN4moba11k_gate_fastILi128ELi2EEEvPKDF16bPKiS4_S4_S4_S2_PKfliiiiillPhPi": "gate_fast",
+        "_ZN4moba11k_gate_fastILi128ELi2ELb1EEEvPKDF16bPKiS4_S4_S4_S2_PKfliiiiillPhPi": "gate_fast",
         "moba::k_gate_bound(int const*, float const*, int, float*)": "gate_bound",
         "void moba::k_bwd_dq_dma<1>(moba::BwdArgs)": "bwd_dq_selected",
         "void moba::k_bwd_dq_dma<0>(moba::BwdArgs)": "bwd_dq_self",
