@@ -8,8 +8,9 @@
 // Counting sort without global atomics:
 //   1. count:   per "chunk" (query block i, kv-head g) an LDS histogram over the
 //               chunk's candidate blocks j < i;
-//   2. lists:   per list (j, g) an exclusive scan over the chunks i > j that can
-//               feed it -> each chunk's start inside the list, and the list size;
+//   2. lists:   per list (j, g), one wave: an exclusive scan over the chunks
+//               i > j that can feed it -> each chunk's start inside the list,
+//               and the list size;
 //   3. offsets: one exclusive scan over list sizes (and over tiles of 256 rows);
 //   4. scatter: per chunk, one wave walks its entries in row order and ranks
 //               equal block ids with ballots, so rows ascend inside every list.
@@ -44,12 +45,12 @@ __global__ void __launch_bounds__(256) k_route_count(const int32_t* __restrict__
   const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
   const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
   const int per_tok = group * ks;
-  const int64_t total = len * per_tok;
+  const int total = (int)len * per_tok;            // below T * hq * ks < 2^31
   const int nvalid = min(ks, i);
   const int32_t* base = sel + (s0 * hq + (int64_t)g * group) * ks;
-  for (int64_t e = threadIdx.x; e < total; e += 256) {
-    const int64_t t = e / per_tok;
-    const int r = (int)(e % per_tok);
+  for (int e = threadIdx.x; e < total; e += 256) {
+    const int t = e / per_tok;
+    const int r = e % per_tok;
     const int j = base[t * hq * ks + r];
     // only ids a row can hold: at most min(ks, i) valid slots, each in [0, i)
     if (j >= 0 && j < i && (r % ks) < nvalid) atomicAdd(&cnt[j], 1);
@@ -60,6 +61,9 @@ __global__ void __launch_bounds__(256) k_route_count(const int32_t* __restrict__
   for (int j = threadIdx.x; j < i; j += 256) hist[dst + j] = cnt[j];
 }
 
+// One wave per list (j, g): the lanes take 64 consecutive feeding chunks i at a
+// time (independent loads), and a wave-wide inclusive scan turns their counts
+// into each chunk's start inside the list.
 __global__ void __launch_bounds__(256) k_route_lists(const int32_t* __restrict__ hist,
                                                      const int32_t* __restrict__ blk_base,
                                                      const int32_t* __restrict__ tri_base,
@@ -68,19 +72,32 @@ __global__ void __launch_bounds__(256) k_route_lists(const int32_t* __restrict__
                                                      int hkv, int64_t nlists,
                                                      int32_t* __restrict__ chunk_off,
                                                      int32_t* __restrict__ list_count) {
-  const int64_t L = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t L = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (L >= nlists) return;
+  const int lane = threadIdx.x & 63;
   const int64_t b = L / hkv;
   const int g = (int)(L % hkv);
   const int n = blk_seq[b], j = blk_local[b];
   const int nbn = blk_base[n + 1] - blk_base[n];
   int32_t run = 0;
-  for (int i = j + 1; i < nbn; ++i) {
-    const int64_t idx = tri_index(tri_base, n, nbn, g, i, j);
-    chunk_off[idx] = run;
-    run += hist[idx];
+  for (int i0 = j + 1; i0 < nbn; i0 += 64) {
+    const int i = i0 + lane;
+    int64_t idx = 0;
+    int32_t h = 0;
+    if (i < nbn) {
+      idx = tri_index(tri_base, n, nbn, g, i, j);
+      h = hist[idx];
+    }
+    int32_t x = h;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (i < nbn) chunk_off[idx] = run + x - h;
+    run += __shfl(x, 63, 64);
   }
-  list_count[L] = run;
+  if (lane == 0) list_count[L] = run;
 }
 
 // One workgroup of 1024 threads: exclusive scans of list sizes and tile counts.
@@ -149,18 +166,18 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
   const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
   const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
   const int per_tok = group * ks;
-  const int64_t total = len * per_tok;
+  const int total = (int)len * per_tok;            // below T * hq * ks < 2^31
   const int nbits = (i <= 1) ? 0 : 32 - __clz(i - 1);
   const int nvalid = min(ks, i);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t e0 = 0; e0 < total; e0 += 64) {
-    const int64_t e = e0 + lane;
+  for (int e0 = 0; e0 < total; e0 += 64) {
+    const int e = e0 + lane;
     int j = -1;
     int64_t row = 0;
     int slot = 0;
     if (e < total) {
-      const int64_t t = e / per_tok;
-      const int r = (int)(e % per_tok);
+      const int t = e / per_tok;
+      const int r = e % per_tok;
       const int hh = r / ks;
       slot = r % ks;
       row = (s0 + t) * hq + (int64_t)g * group + hh;
@@ -191,7 +208,7 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
   const size_t lds = (size_t)p.max_nb * sizeof(int32_t);
   hipLaunchKernelGGL(k_route_count, dim3(nchunks), dim3(256), lds, s, sel, cu_dev, w.blk_base,
                      w.tri_base, w.blk_seq, w.blk_local, p.hq, p.hkv, p.block, p.ks, w.hist);
-  hipLaunchKernelGGL(k_route_lists, dim3((unsigned)((p.nlists + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(k_route_lists, dim3((unsigned)((p.nlists + 3) / 4)), dim3(256), 0, s,
                      w.hist, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, p.hkv, p.nlists,
                      w.chunk_off, w.list_count);
   hipLaunchKernelGGL(k_route_offsets, dim3(1), dim3(1024), 0, s, w.list_count, p.nlists,
