@@ -170,19 +170,28 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
   const int nbits = (i <= 1) ? 0 : 32 - __clz(i - 1);
   const int nvalid = min(ks, i);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // entry e of the chunk: its row, slot and block id (-1 past the end)
+  auto fetch = [&](int e, int64_t& row, int& slot) __attribute__((always_inline)) -> int {
+    row = 0;
+    slot = 0;
+    if (e >= total) return -1;
+    const int t = e / per_tok;
+    const int r = e % per_tok;
+    slot = r % ks;
+    row = (s0 + t) * hq + (int64_t)g * group + r / ks;
+    return sel[row * ks + slot];
+  };
+  int64_t row_n;
+  int slot_n;
+  int j_n = fetch(lane, row_n, slot_n);
+  // The workgroup is one wave: its LDS accesses take effect in program order,
+  // so the counters need no barrier between steps (only the compiler must keep
+  // the order), and the next step's ids are loaded before this step ranks.
   for (int e0 = 0; e0 < total; e0 += 64) {
-    const int e = e0 + lane;
-    int j = -1;
-    int64_t row = 0;
-    int slot = 0;
-    if (e < total) {
-      const int t = e / per_tok;
-      const int r = e % per_tok;
-      const int hh = r / ks;
-      slot = r % ks;
-      row = (s0 + t) * hq + (int64_t)g * group + hh;
-      j = sel[row * ks + slot];
-    }
+    const int j = j_n;
+    const int64_t row = row_n;
+    const int slot = slot_n;
+    j_n = fetch(e0 + 64 + lane, row_n, slot_n);
     const bool act = j >= 0 && j < i && slot < nvalid;
     uint64_t peers = __ballot(act);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -196,7 +205,7 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
       entries[base + rank] = (int32_t)(row * ks + slot);
       if ((peers & below) == 0) next[j] = base + __popcll(peers);
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");
   }
 }
 
