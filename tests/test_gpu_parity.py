@@ -65,6 +65,9 @@ SMALL = [
     # more than 512 blocks in a sequence: the screened gate's best-first lists
     ("many-blocks-k3-bf16", [40000, 900], 2, 1, 64, 64, 3, "bf16"),
     ("many-blocks-k5-bf16", [36000], 4, 2, 128, 64, 5, "bf16"),
+    # three q heads per kv head with 16-bit D = 128: own-block tiles of one head,
+    # three selected parts merged two and then one at a time
+    ("g3-heads-k4-bf16", [1500, 700, 97], 6, 2, 128, 128, 4, "bf16"),
 ]
 
 
