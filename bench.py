@@ -7,8 +7,10 @@ One step = one moba_forward call over the whole batch (pool, gate, route,
 selected-block attention, self-block attention with the merge of the parts in
 its epilogue), inputs resident in HBM.
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed live
-with HIP events on the launch stream), the dense causal comparison from the same
-library, and the CPU oracle timed on a bounded sample of the same workload.
+with HIP events on the launch stream, and from the committed kernel trace), the
+dense causal comparison from the same library, the CPU oracle timed on a bounded
+sample of the same workload, and (for the 1M workload) the metric's 128K point,
+the packed varlen batch, timed the same way in the same run.
 """
 from __future__ import annotations
 
@@ -82,16 +84,23 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key):
-    """HBM bytes per launch from the committed counter summary, if it still applies."""
-    path = os.path.join(ROOT, "profiles", "traffic_attn_selected_1m.txt")
-    if not os.path.exists(path):
-        return None
+def _profile_values(path):
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
+    return vals
+
+
+def load_traffic(kernel_key, config):
+    """HBM bytes per launch of `kernel_key` on workload `config` from the committed
+    counter summary profiles/traffic_<kernel>_<config>.txt; None when there is no
+    summary for this workload or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel_key, config))
+    if not os.path.exists(path):
+        return None
+    vals = _profile_values(path)
     if vals.get("source_digest") != source_digest() or vals.get("kernel") != kernel_key:
         return None
     try:
@@ -100,13 +109,51 @@ def load_traffic(kernel_key):
         return None
 
 
+def load_trace_avg(kernel_key, config):
+    """Average launch duration (ms) of `kernel_key` in the committed rocprofv3 kernel
+    trace summary profiles/kernels_<workload>.md; None when there is none for this
+    workload or it was taken on other attention sources."""
+    path = os.path.join(ROOT, "profiles", "kernels_%s.md" % CONFIG_NAMES[config])
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if "digest: %s" % source_digest() not in text:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and cells[0] == kernel_key:
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def nproc():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(inp, hq, budget_s, seed):
     """The oracle, untuned, on a bounded sample of the workload's rows."""
     import numpy as np
     import oracle
     from synth_inputs import sample_tokens
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-    threads = min(threads, 16)
+    # every core this process may run on, unless OMP_NUM_THREADS sets the CPU share
+    # (a GPU box gives each GPU a share of its cores through it)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or nproc()
     kf = oracle._f32(inp.k)
     vf = oracle._f32(inp.v)
 
@@ -125,9 +172,15 @@ def cpu_baseline(inp, hq, budget_s, seed):
     per_tok = max(t1 - t0, 1e-6) / max(n1 - n0, 1)
     ntok = int(max(8, min(8192, (budget_s - t0) / per_tok)))
     n, t = run(ntok, seed + 200)
+    T = int(sum(inp.seqlens))
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d sampled tokens x %d q-heads of the workload (oracle fp64, pools every "
-                      "block, then gate + select + attend per row); %.1f s wall" % (n, hq, t)}
+                      "block, then gate + select + attend per row); %.1f s wall" % (n, hq, t),
+            "nproc": nproc(), "cpu_model": cpu_model(),
+            "full_sequence_s_extrapolated": T / (n / t),
+            "extrapolation": "all %d tokens at the sampled rate (linear in tokens; the "
+                             "sample's rows attend as many keys on average as the workload's)"
+                             % T}
 
 
 def bench_decode(moba, torch, q, k, v, block, topk, steps, nseq=16):
@@ -339,6 +392,112 @@ def bench_group_major(moba, torch, args):
     print(json.dumps(line), flush=True)
 
 
+def stage_report(stages, work, peak_mfma):
+    """Per-stage HIP-event averages with their rates against the roofline that
+    bounds each stage."""
+    rep_all = {}
+    for name, (tot_ms, n) in stages.items():
+        if n == 0:
+            continue
+        avg = tot_ms / n
+        rep = {"avg_ms": avg, "launches": n}
+        if name in ("attn_selected", "attn_self"):
+            tf = work[name + "_flop"] / (avg * 1e-3) / 1e12
+            rep.update(bound="mfma", achieved_tflops=tf, frac=tf / peak_mfma)
+        elif name == "gate":
+            gbs = work["gate_bytes"] / (avg * 1e-3) / 1e9
+            tf = work["gate_flop"] / (avg * 1e-3) / 1e12
+            # one bf16 matrix-core pass per score (the screened gate; flagged tiles
+            # add three more): both the HBM and the matrix-core fraction
+            rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
+                       achieved_tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        elif name in ("pool", "route"):
+            gbs = work[name + "_bytes"] / (avg * 1e-3) / 1e9
+            rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)
+        rep_all[name] = rep
+    return rep_all
+
+
+def time_forward(moba, torch, inp, cu_dev, steps, warmup, timing=True):
+    """Time `steps` moba_forward calls over the batch (after `warmup` untimed ones),
+    inputs, output and workspace resident in HBM; with `timing`, also every stage's
+    launches through the library's HIP events."""
+    q, k, v = inp.q, inp.k, inp.v
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    dev = q.device
+    cu_host = inp.cu_seqlens
+    nbytes = moba.moba_workspace_bytes(cu_host, hq, hkv, d, q.dtype, inp.block, inp.topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    work = work_counts(inp.seqlens, hq, hkv, d, inp.block, inp.topk, q.element_size())
+
+    def step():
+        moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,
+                          cu_seqlens_dev=cu_dev)
+
+    print("[bench] warmup %d" % warmup, file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if timing:
+        moba.moba_timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stages = moba.moba_timing_read() if timing else {}
+    moba.moba_timing_enable(False)
+    print("[bench] %d steps: %.3f ms/step" % (steps, ms), file=sys.stderr, flush=True)
+    del ws, out
+    peak = PEAK_BF16_TFLOPS if q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+    return {"ms": ms, "work": work, "stages": stage_report(stages, work, peak)}
+
+
+def bench_second_workload(moba, torch, name, steps, warmup, seed, dense_steps):
+    """The metric's second point (S = 128K: the packed varlen batch of 134,144
+    tokens), timed like the headline workload in the same run: tokens/s, every
+    stage's rate and the dense causal comparison from the same library."""
+    from synth_inputs import make_config
+    dev = torch.device("cuda:0")
+    print("[bench] second workload %s" % name, file=sys.stderr, flush=True)
+    inp = make_config(name, seed=seed, device=dev)
+    cu_dev = inp.cu_seqlens.to(dev)
+    fwd = time_forward(moba, torch, inp, cu_dev, steps, warmup, True)
+    ms, work = fwd["ms"], fwd["work"]
+    T = inp.q.shape[0]
+    out = torch.empty_like(inp.q)
+    moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, out=out,
+                                   cu_seqlens_dev=cu_dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(dense_steps):
+        moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, out=out,
+                                       cu_seqlens_dev=cu_dev)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / dense_steps
+    attn_flop = work["attn_selected_flop"] + work["attn_self_flop"]
+    sel = fwd["stages"].get("attn_selected", {})
+    res = {"workload": CONFIG_NAMES[name], "seqlens": inp.seqlens, "tokens": T,
+           "steps": steps, "warmup": warmup, "ms_per_step": ms,
+           "tokens_per_s": T / (ms * 1e-3),
+           "effective_attn_tflops": attn_flop / (ms * 1e-3) / 1e12,
+           "attn_selected_mfma_frac": sel.get("frac"),
+           "dense_causal_ms": dms, "speedup_vs_dense": dms / ms,
+           "stages": fwd["stages"]}
+    del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,6 +511,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the gated-decode measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-second", action="store_true",
+                    help="skip the metric's 128K point (varlen 131K) timed after the 1M one")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
     ap.add_argument("--no-achievable", action="store_true",
@@ -381,11 +542,6 @@ def main():
     hkv = k.shape[1]
     cu_host = inp.cu_seqlens
     cu_dev = cu_host.to(dev)
-    nbytes = moba.moba_workspace_bytes(cu_host, hq, hkv, d, q.dtype, inp.block, inp.topk)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    elem = q.element_size()
-    work = work_counts(inp.seqlens, hq, hkv, d, inp.block, inp.topk, elem)
 
     if args.copy_calibration_mib > 0:
         # one plain streaming kernel of known size: reads and writes N MiB of fp32
@@ -396,65 +552,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,
-                          cu_seqlens_dev=cu_dev)
-
-    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    if not args.no_timing:
-        moba.moba_timing_enable(True)
+    fwd = time_forward(moba, torch, inp, cu_dev, args.steps, args.warmup, not args.no_timing)
+    ms, work, stage_rep = fwd["ms"], fwd["work"], fwd["stages"]
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    stages = moba.moba_timing_read() if not args.no_timing else {}
-    moba.moba_timing_enable(False)
-    print("[bench] %d steps: %.3f ms/step" % (args.steps, ms), file=sys.stderr, flush=True)
-
-    # per-stage averages and rooflines
+    out = torch.empty_like(q)
     peak_mfma = PEAK_BF16_TFLOPS if q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
-    stage_rep = {}
-    for name, (tot_ms, n) in stages.items():
-        if n == 0:
-            continue
-        avg = tot_ms / n
-        rep = {"avg_ms": avg, "launches": n}
-        if name in ("attn_selected", "attn_self"):
-            tf = work[name + "_flop"] / (avg * 1e-3) / 1e12
-            rep.update(bound="mfma", achieved_tflops=tf, frac=tf / peak_mfma)
-            if name == "attn_self":
-                # its epilogue also streams the merge's bytes
-                rep["merge_gbs"] = work["merge_bytes"] / (avg * 1e-3) / 1e9
-                rep["merge_hbm_frac"] = rep["merge_gbs"] / PEAK_HBM_GBS
-        elif name == "gate":
-            gbs = work["gate_bytes"] / (avg * 1e-3) / 1e9
-            tf = work["gate_flop"] / (avg * 1e-3) / 1e12
-            # one bf16 matrix-core pass per score (the screened gate; flagged tiles
-            # add three more): both the HBM and the matrix-core fraction
-            rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS,
-                       achieved_tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
-        elif name in ("pool", "route"):
-            gbs = work[name + "_bytes"] / (avg * 1e-3) / 1e9
-            rep.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)
-        stage_rep[name] = rep
     roofline = None
     if "attn_selected" in stage_rep:
-        s = stage_rep["attn_selected"]
-        traffic = load_traffic("attn_selected")
+        st = stage_rep["attn_selected"]
+        traffic = load_traffic("attn_selected", args.config)
+        trace_ms = load_trace_avg("attn_selected", args.config)
         roofline = {"kernel": "attn_selected", "bound": "mfma",
-                    "achieved": round(s["achieved_tflops"], 2), "peak": peak_mfma,
-                    "unit": "TFLOP/s", "frac": round(s["frac"], 4),
+                    "achieved": round(st["achieved_tflops"], 2), "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": round(st["frac"], 4),
                     "traffic": traffic,
-                    "avg_launch_ms": round(s["avg_ms"], 4),
-                    "algorithmic_flop_per_launch": work["attn_selected_flop"]}
+                    "avg_launch_ms": round(st["avg_ms"], 4),
+                    "avg_launch_source": "HIP events on the launch stream, %d timed launches"
+                                         % st["launches"],
+                    "algorithmic_flop_per_launch": work["attn_selected_flop"],
+                    "trace_avg_launch_ms": trace_ms,
+                    "frac_from_trace": (round(work["attn_selected_flop"] / (trace_ms * 1e-3)
+                                              / 1e12 / peak_mfma, 4) if trace_ms else None),
+                    "trace_source": ("profiles/kernels_%s.md" % CONFIG_NAMES[args.config])
+                                    if trace_ms else None}
     attn_flop = work["attn_selected_flop"] + work["attn_self_flop"]
 
     dense = None
@@ -497,6 +618,12 @@ def main():
         backward = bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma,
                                   steps=max(1, min(args.steps, 5)))
 
+    second = None
+    if not args.no_second and args.config == "1m":
+        second = bench_second_workload(moba, torch, "varlen131k", steps=max(args.steps, 10),
+                                       warmup=max(args.warmup, 3), seed=args.seed,
+                                       dense_steps=max(args.dense_steps, 3))
+
     if achievable is not None:
         if decode is not None:
             decode["hbm_frac_of_achievable"] = decode["achieved_gbs"] / achievable["hbm_gbs"]
@@ -529,6 +656,7 @@ def main():
         "decode": decode,
         "backward": backward,
         "stages": stage_rep,
+        "workload_128k": second,
     }
     print(json.dumps(line), flush=True)
 

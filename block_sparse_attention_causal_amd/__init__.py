@@ -17,7 +17,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoba.so")
+# MOBA_LIB selects another build of the same sources (the host-sanitizer test's)
+LIB_PATH = os.environ.get("MOBA_LIB") or os.path.join(_PKG, "libmoba.so")
 
 MOBA_OK, MOBA_ERR_INVALID_ARG, MOBA_ERR_UNSUPPORTED, MOBA_ERR_WORKSPACE, MOBA_ERR_HIP = range(5)
 MOBA_DTYPE_F32, MOBA_DTYPE_BF16 = 0, 1
@@ -86,8 +87,8 @@ def exported_symbols():
     """Names the binding resolves in libmoba.so (loading fails if any is missing)."""
     _load()
     return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
-            "moba_dense_causal_forward", "moba_attention_forward", "moba_block_pool",
-            "moba_kbar_append", "moba_decode_workspace_bytes", "moba_decode_forward",
+            "moba_dense_causal_forward", "moba_attention_forward",
+            "moba_block_pool", "moba_kbar_append", "moba_decode_workspace_bytes", "moba_decode_forward",
             "moba_backward_workspace_bytes", "moba_backward", "moba_route_sizes", "moba_route",
             "moba_timing_enable", "moba_timing_read", "moba_stage_name"]
 
@@ -123,6 +124,49 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_cu_total(host, T, name="cu_seqlens"):
+    """The library reads T = cu_seqlens[-1] tokens of every tensor; a tensor with fewer
+    rows would be read and written out of bounds, so refuse the mismatch here."""
+    if host.dim() != 1 or host.numel() < 1:
+        raise ValueError("%s must be a 1-D list of num_seqs + 1 offsets" % name)
+    if int(host[-1]) != int(T):
+        raise ValueError("%s[-1] = %d but the tensors hold %d tokens" % (name, int(host[-1]),
+                                                                          int(T)))
+
+
+def _check_like(name, t, ref):
+    """A caller-supplied output must be a contiguous tensor shaped, typed and placed
+    like the tensor it mirrors (the library writes it in full)."""
+    if t is None:
+        return
+    if (t.device != ref.device or t.dtype != ref.dtype or tuple(t.shape) != tuple(ref.shape)
+            or not t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s tensor %s on %s, got %s %s on %s"
+                         % (name, ref.dtype, tuple(ref.shape), ref.device, t.dtype,
+                            tuple(t.shape), t.device))
+
+
+def _check_kv_cache(cache, cu_host, name):
+    """A KV cache must hold at least cu_k[-1] token rows (the kernels read that many)."""
+    if cache.shape[0] < int(cu_host[-1]):
+        raise ValueError("%s holds %d token rows, but cu_k[-1] = %d" % (name, cache.shape[0],
+                                                                        int(cu_host[-1])))
+
+
+def _check_kbar_cache(kbar_cache, k_cache, nseq, max_blocks):
+    """The pooled-key cache: fp32, contiguous, on the cache's device, with room for
+    num_seqs * max_blocks blocks of [Hkv, D]."""
+    if kbar_cache is None:
+        raise ValueError("kbar_cache is required")
+    need = int(nseq) * int(max_blocks) * k_cache.shape[1] * k_cache.shape[2]
+    if (kbar_cache.dtype != torch.float32 or kbar_cache.device != k_cache.device
+            or not kbar_cache.is_contiguous()):
+        raise ValueError("kbar_cache must be a contiguous fp32 tensor on %s" % k_cache.device)
+    if kbar_cache.numel() < need:
+        raise ValueError("kbar_cache holds %d values, needs num_seqs * max_blocks * Hkv * D = %d"
+                         % (kbar_cache.numel(), need))
+
+
 def _check_qkv(q, k, v, same_len=True):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -148,6 +192,17 @@ def moba_workspace_bytes(cu_seqlens, num_q_heads, num_kv_heads, head_dim, dtype,
     return int(n)
 
 
+def _check_workspace(ws, ref, nbytes):
+    """A caller-supplied workspace: a contiguous GPU byte buffer on the tensors' device,
+    at least nbytes long (the library also checks the size it is told)."""
+    if ws is None:
+        return
+    if ws.device != ref.device or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % ref.device)
+    if ws.numel() < nbytes:
+        raise ValueError("workspace holds %d bytes, needs %d" % (ws.numel(), nbytes))
+
+
 def _workspace(nbytes, device):
     # 256-byte aligned device buffer (the caching allocator returns 512-byte aligned blocks)
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -165,12 +220,15 @@ def moba_forward(q, k, v, cu_seqlens, block_size, topk, *, out=None, workspace=N
     T, hq, d = q.shape
     hkv = k.shape[1]
     host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
+    _check_cu_total(host, T)
+    _check_like("out", out, q)
     shape = _shape(hq, hkv, d, q.dtype, softmax_scale)
     lib = _load()
     nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
                                       int(block_size), int(topk))
     if nbytes == 0 and moba_last_error():
         raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    _check_workspace(workspace, q, nbytes)
     if workspace is None:
         workspace = _workspace(nbytes, dev)
     if out is None:
@@ -197,6 +255,8 @@ def moba_dense_causal_forward(q, k, v, cu_seqlens, *, out=None, return_lse=False
     dev = q.device
     T, hq, d = q.shape
     host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
+    _check_cu_total(host, T)
+    _check_like("out", out, q)
     shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
     if out is None:
         out = torch.empty_like(q)
@@ -225,23 +285,32 @@ def moba_backward(q, k, v, out, lse, dout, sel, cu_seqlens, block_size, topk, *,
     fixed (both from moba_forward with return_sel / return_lse)."""
     _check_qkv(q, k, v)
     for name, t in (("out", out), ("dout", dout)):
-        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("%s must be a contiguous GPU tensor shaped and typed like q" % name)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != q.shape[:2]:
-        raise ValueError("lse must be a contiguous fp32 tensor [T, Hq]")
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _check_like(name, t, q)
+    if (lse is None or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or tuple(lse.shape) != tuple(q.shape[:2]) or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 tensor [T, Hq] on q's device")
     if topk > 1 and (sel is None or sel.dtype != torch.int32 or not sel.is_contiguous()
-                     or tuple(sel.shape) != (q.shape[0], q.shape[1], topk - 1)):
-        raise ValueError("sel must be the forward's int32 selection [T, Hq, topk-1]")
+                     or tuple(sel.shape) != (q.shape[0], q.shape[1], topk - 1)
+                     or sel.device != q.device):
+        raise ValueError("sel must be the forward's int32 selection [T, Hq, topk-1] on q's "
+                         "device")
     dev = q.device
     T, hq, d = q.shape
     host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
+    _check_cu_total(host, T)
+    _check_like("dq", dq, q)
+    _check_like("dk", dk, k)
+    _check_like("dv", dv, v)
     shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
     lib = _load()
+    nbytes = lib.moba_backward_workspace_bytes(_ptr(host), host.numel() - 1,
+                                               ctypes.byref(shape), int(block_size), int(topk))
+    if nbytes == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    _check_workspace(workspace, q, nbytes)
     if workspace is None:
-        nbytes = lib.moba_backward_workspace_bytes(_ptr(host), host.numel() - 1,
-                                                   ctypes.byref(shape), int(block_size), int(topk))
-        if nbytes == 0 and moba_last_error():
-            raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
         workspace = _workspace(nbytes, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -266,15 +335,19 @@ def moba_attention(q, k, v, cu_seqlens, block_size, topk, *, full=False, out=Non
     dev = q.device
     T, hq, d = q.shape
     host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
+    _check_cu_total(host, T)
+    _check_like("out", out, q)
     shape = _shape(hq, k.shape[1], d, q.dtype, softmax_scale)
     lib = _load()
     mode = MOBA_MODE_FULL if full else MOBA_MODE_SPARSE
-    if not full and workspace is None:
+    if not full:
         nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
                                           int(block_size), int(topk))
         if nbytes == 0 and moba_last_error():
             raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
-        workspace = _workspace(nbytes, dev)
+        _check_workspace(workspace, q, nbytes)
+        if workspace is None:
+            workspace = _workspace(nbytes, dev)
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty(T, hq, dtype=torch.float32, device=dev) if return_lse else None
@@ -299,8 +372,8 @@ def moba_kbar_append(k_cache, cu_k, prev_len, block_size, max_blocks, kbar_cache
     prev_d = prev_h.to(dev)
     if prev_h.numel() != host.numel() - 1:
         raise ValueError("prev_len needs one entry per sequence")
-    if kbar_cache.dtype != torch.float32 or not kbar_cache.is_cuda:
-        raise ValueError("kbar_cache must be an fp32 GPU tensor")
+    _check_kv_cache(k_cache, host, "k_cache")
+    _check_kbar_cache(kbar_cache, k_cache, host.numel() - 1, max_blocks)
     shape = _shape(hkv, hkv, d, k_cache.dtype)
     _check(_load().moba_kbar_append(_ptr(k_cache), _ptr(cdev), _ptr(host), _ptr(prev_d),
                                     _ptr(prev_h), host.numel() - 1, ctypes.byref(shape),
@@ -326,10 +399,17 @@ def moba_decode(q_new, k_cache, v_cache, cu_q, cu_k, block_size, topk, kbar_cach
     nseq = qh.numel() - 1
     if kh.numel() - 1 != nseq:
         raise ValueError("cu_q and cu_k must describe the same sequences")
+    _check_cu_total(qh, Tq, "cu_q")
+    _check_kv_cache(k_cache, kh, "k_cache")
+    _check_kv_cache(v_cache, kh, "v_cache")
+    if topk > 1:
+        _check_kbar_cache(kbar_cache, k_cache, nseq, max_blocks)
+    _check_like("out", out, q_new)
     nbytes = lib.moba_decode_workspace_bytes(_ptr(qh), _ptr(kh), nseq, ctypes.byref(shape),
                                              int(block_size), int(topk), int(max_blocks))
     if nbytes == 0 and moba_last_error():
         raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    _check_workspace(workspace, q_new, nbytes)
     if workspace is None:
         workspace = _workspace(nbytes, dev)
     if out is None:
@@ -358,6 +438,7 @@ def moba_block_pool(k, cu_seqlens, block_size):
     dev = k.device
     T, hkv, d = k.shape
     host, cu_dev = _cu(cu_seqlens, dev)
+    _check_cu_total(host, T)
     shape = _shape(hkv, hkv, d, k.dtype)
     lib = _load()
     nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
@@ -394,6 +475,9 @@ def moba_route(sel, cu_seqlens, num_kv_heads, head_dim, dtype, block_size, topk)
     dev = sel.device
     T, hq, _ = sel.shape
     host, cu_dev = _cu(cu_seqlens, dev)
+    _check_cu_total(host, T)
+    if sel.dim() != 3 or sel.shape[2] != max(int(topk) - 1, 0):
+        raise ValueError("sel must be [T, Hq, topk-1]")
     shape = _shape(hq, num_kv_heads, head_dim, dtype)
     lib = _load()
     nl, ne = moba_route_sizes(host, hq, num_kv_heads, head_dim, dtype, block_size, topk)

@@ -1023,7 +1023,7 @@ hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, con
   a.o_part = w.o_sel;
   a.lse_part = w.lse_sel;
   a.ntiles = tile_bound(p, p.sel_rows);
-  a.padded = (a.ntiles + 7) / 8 * 8;
+  a.padded = pad8(a.ntiles);
   if (p.sel_rows == kSelRowsPerTile) {             // bf16, D = 128
     hipLaunchKernelGGL(k_attn4<MODE_SELECTED>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0,
                        s, a);
@@ -1045,19 +1045,16 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
   a.lse_out = lse_out;
   if (p.dtype == MOBA_DTYPE_BF16 && p.d == 128) {
     // 4-wave tiles: hw = gcd(G, 4) heads x 4 / hw groups of 32 tokens
-    const int hw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
-    const int tt = 32 * (kSelWaves / hw);
-    a.nu = (p.block + tt - 1) / tt;
-    a.ntiles = p.nb * a.nu * (p.hq / hw);
-    a.padded = (a.ntiles + 7) / 8 * 8;
+    a.nu = tiles_per_block(p, attn4_tokens(p));
+    a.ntiles = self4_tile_count(p);
+    a.padded = pad8(a.ntiles);
     hipLaunchKernelGGL(k_attn4<MODE_SELF>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s,
                        a);
     return hipGetLastError();
   }
-  const int tt = 32 * (8 / p.hg);
-  a.nu = (p.block + tt - 1) / tt;
-  a.ntiles = p.nb * a.nu * (p.hq / p.hg);
-  a.padded = (a.ntiles + 7) / 8 * 8;
+  a.nu = tiles_per_block(p, tile_tokens8(p));
+  a.ntiles = self8_tile_count(p);
+  a.padded = pad8(a.ntiles);
   return attn_dispatch<MODE_SELF>(p, a, s);
 }
 
@@ -1067,10 +1064,9 @@ hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const 
   AttnArgs a = base_args(p, q, k, v, cu_dev);
   a.out = out;
   a.lse_out = lse_out;
-  const int tt = 32 * (8 / p.hg);
-  a.nu = (int)((p.max_len + tt - 1) / tt);
-  a.ntiles = (int64_t)p.nseq * a.nu * (p.hq / p.hg);
-  a.padded = (a.ntiles + 7) / 8 * 8;
+  a.nu = dense_tiles_per_seq(p);
+  a.ntiles = dense_tile_count(p);
+  a.padded = pad8(a.ntiles);
   return attn_dispatch<MODE_DENSE>(p, a, s);
 }
 

@@ -30,7 +30,7 @@ enum { BWD_SELF = 0, BWD_SELECTED = 1 };
 constexpr int BKC = 64;       // keys per chunk (dQ pass)
 constexpr int BRC = 32;       // rows per chunk (dK/dV pass)
 constexpr int BDQ_WAVES = 8;  // dQ pass: 8 waves x 32 rows, the forward's tiles
-constexpr int BKV_WAVES = 4;  // dK/dV pass: 4 waves x 32 keys = 128 keys per tile
+constexpr int BKV_WAVES = kBkvWaves;  // dK/dV pass: 4 waves x 32 keys = 128 keys per tile
 
 // ---------------------------------------------------------------------------
 // Delta_r = sum_d dO_r[d] O_r[d] in fp32, D/8 lanes per row.
@@ -496,7 +496,7 @@ k_bwd_dkdv(BwdArgs a) {
 // its last token down, each tile stopping below its first key. (Own rows first,
 // from each tile's first key up, would start the tiles thousands of rows apart
 // and every tile would fetch every row from HBM.)
-constexpr int DKV_WAVES = 8;
+constexpr int DKV_WAVES = kDkvWaves;
 
 __device__ __forceinline__ bf16x8 tr_frag(const bf16* rows, int r0, int dt, int vrow, int vx0,
                                           int vx1, int vbyte) {
@@ -1018,7 +1018,7 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
   BwdArgs a = base;
   if (p.ks > 0 && p.nentries > 0) {
     a.ntiles = tile_bound(p, kRowsPerTile);
-    a.padded = (a.ntiles + 7) / 8 * 8;
+    a.padded = pad8(a.ntiles);
     if constexpr (sizeof(T) == 2 && D == 128)
       hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELECTED>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
     else
@@ -1028,10 +1028,9 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
     if (e != hipSuccess) return e;
   }
   {
-    const int tt = 32 * (8 / p.hg);
-    a.nu = (p.block + tt - 1) / tt;
-    a.ntiles = p.nb * a.nu * (p.hq / p.hg);
-    a.padded = (a.ntiles + 7) / 8 * 8;
+    a.nu = tiles_per_block(p, tile_tokens8(p));
+    a.ntiles = self8_tile_count(p);
+    a.padded = pad8(a.ntiles);
     if constexpr (sizeof(T) == 2 && D == 128)
       hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELF>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
     else
@@ -1040,12 +1039,12 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
     if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2 && D == 128) {
-    a.kvt = (p.block + DKV_WAVES * 32 - 1) / (DKV_WAVES * 32);
-    const int64_t lists8 = (p.nb * p.hkv + 7) / 8 * 8;
+    a.kvt = tiles_per_block(p, DKV_WAVES * 32);
+    const int64_t lists8 = pad8(p.nb * p.hkv);
     hipLaunchKernelGGL(k_bwd_dkdv_dma, dim3((unsigned)(lists8 * a.kvt)), dim3(64 * DKV_WAVES), 0,
                        s, a);
   } else {
-    a.kvt = (p.block + BKV_WAVES * 32 - 1) / (BKV_WAVES * 32);
+    a.kvt = tiles_per_block(p, BKV_WAVES * 32);
     const int64_t tiles = p.nb * p.hkv * a.kvt;
     hipLaunchKernelGGL((k_bwd_dkdv<T, D>), dim3((unsigned)tiles), dim3(256), 0, s, a);
   }

@@ -35,6 +35,38 @@ static int gcd_int(int a, int b) {
   return a;
 }
 
+int64_t max_grid_items(const Plan& p, bool backward) {
+  int64_t m = 256;                                          // set-up
+  auto take = [&](int64_t groups, int threads) { m = std::max(m, groups * threads); };
+  if (p.block == 0) {                                       // dense causal attention
+    take(pad8(dense_tile_count(p)), kAttnThreads);
+    return m;
+  }
+  const bool w4 = p.dtype == MOBA_DTYPE_BF16 && p.d == 128;
+  take((p.nb + 255) / 256, 256);                            // block table
+  take(p.nb * p.hkv, 256);                                  // pool
+  if (p.ks > 0) {
+    take(pad8(gate_tile_count(p)), 64 * kGateWaves);        // gate passes
+    take((int64_t)p.nseq * p.hkv, 256);                     // gate bound
+    take(p.nb * p.hkv, 256);                                // route count / scatter
+    take((p.nlists + 3) / 4, 256);                          // route list scans
+    take(pad8(tile_bound(p, p.sel_rows)), w4 ? 64 * kSelWaves : kAttnThreads);
+  }
+  take(w4 ? pad8(self4_tile_count(p)) : pad8(self8_tile_count(p)),
+       w4 ? 64 * kSelWaves : kAttnThreads);
+  if (backward) {
+    const int64_t rows = p.T * p.hq;
+    take((rows + 256 / (p.d / 8) - 1) / (256 / (p.d / 8)), 256);            // Delta
+    if (p.ks > 0) take(pad8(tile_bound(p, kRowsPerTile)), kAttnThreads);    // dQ selected
+    take(pad8(self8_tile_count(p)), kAttnThreads);                          // dQ self
+    if (w4)
+      take(pad8(p.nb * p.hkv) * tiles_per_block(p, kDkvWaves * 32), 64 * kDkvWaves);
+    else
+      take(p.nb * p.hkv * tiles_per_block(p, kBkvWaves * 32), 64 * kBkvWaves);
+  }
+  return m;
+}
+
 moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* shape,
                         int32_t block, int32_t topk, bool need_block, Plan* p, char* err,
                         size_t errlen) {
@@ -101,6 +133,11 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
   }
   P.nlists = P.nb * P.hkv;
   P.sel_rows = (P.dtype == MOBA_DTYPE_BF16 && P.d == 128) ? kSelRowsPerTile : kRowsPerTile;
+  P.span = need_block ? std::min((int64_t)P.block, P.max_len) : P.max_len;
+  if (max_grid_items(P, false) > kMaxGridItems)
+    return fail(MOBA_ERR_UNSUPPORTED, "this batch needs a launch grid of %lld work-items, more "
+                "than HIP allows (many short sequences with a long one?)",
+                (long long)max_grid_items(P, false));
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -118,12 +155,8 @@ moba_status_t make_plan(const int32_t* cu, int32_t nseq, const moba_shape_t* sha
       take(P.dtype == MOBA_DTYPE_BF16 ? sizeof(bf16) * 3 * P.nb * P.hkv * P.d : 0);
   P.off_kbar_err = take(sizeof(float) * P.nb * P.hkv);
   P.off_gate_bound = take(sizeof(float) * nseq * P.hkv);
-  {
-    // the gate's tiling: 8 waves x 32 rows, HG heads of one group side by side
-    const int tt = 32 * (8 / P.hg);
-    const int64_t nu = P.block > 0 ? (P.block + tt - 1) / tt : 0;
-    P.gate_tiles = P.nb * nu * (P.hq / P.hg);
-  }
+  // the gate's tiling: 8 waves x 32 rows, HG heads of one group side by side
+  P.gate_tiles = need_block ? gate_tile_count(P) : 0;
   P.off_gate_flags = take(P.gate_tiles);
   if (P.ks > 0) {
     P.off_sel = take(sizeof(int32_t) * rows * P.ks);
@@ -310,6 +343,48 @@ static BwdLayout backward_layout(const Plan& p) {
   return l;
 }
 
+// The stages of one forward call on a validated plan and a workspace of at
+// least plan.total bytes (nothing in it needs to start at zero: every word a
+// kernel reads is written earlier in the same call).
+static moba_status_t forward_enqueue(const Plan& p, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_dev, void* out, void* workspace,
+                                     int32_t* sel_out, float* lse_out, hipStream_t s) {
+  (void)hipGetLastError();
+  Work w = carve(p, workspace);
+  int32_t* sel = sel_out ? sel_out : w.sel;
+  hipError_t e = launch_setup(p, cu_dev, w, s);
+  if (e != hipSuccess) return hip_status(e, "setup");
+  {
+    StageScope t(ST_POOL, s);
+    e = launch_pool(p, k, cu_dev, w, w.kbar, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "pool");
+  if (p.ks > 0) {
+    {
+      StageScope t(ST_GATE, s);
+      e = launch_gate(p, q, cu_dev, w, sel, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "gate");
+    {
+      StageScope t(ST_ROUTE, s);
+      e = launch_route(p, sel, cu_dev, w, p.sel_rows, w.list_offsets, w.entries, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "route");
+    {
+      StageScope t(ST_SELECTED, s);
+      e = launch_attn_selected(p, q, k, v, cu_dev, w, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "selected-block attention");
+  }
+  {
+    StageScope t(ST_SELF, s);
+    e = launch_attn_self(p, q, k, v, cu_dev, w, out, lse_out, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "self-block attention");
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
 }  // namespace moba
 
 using namespace moba;
@@ -350,41 +425,8 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
   if (workspace_bytes < p.total)
     return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 p.total);
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();
-  Work w = carve(p, workspace);
-  int32_t* sel = sel_out ? sel_out : w.sel;
-  hipError_t e = launch_setup(p, cu_seqlens_dev, w, s);
-  if (e != hipSuccess) return hip_status(e, "setup");
-  {
-    StageScope t(ST_POOL, s);
-    e = launch_pool(p, k, cu_seqlens_dev, w, w.kbar, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "pool");
-  if (p.ks > 0) {
-    {
-      StageScope t(ST_GATE, s);
-      e = launch_gate(p, q, cu_seqlens_dev, w, sel, s);
-    }
-    if (e != hipSuccess) return hip_status(e, "gate");
-    {
-      StageScope t(ST_ROUTE, s);
-      e = launch_route(p, sel, cu_seqlens_dev, w, p.sel_rows, w.list_offsets, w.entries, s);
-    }
-    if (e != hipSuccess) return hip_status(e, "route");
-    {
-      StageScope t(ST_SELECTED, s);
-      e = launch_attn_selected(p, q, k, v, cu_seqlens_dev, w, s);
-    }
-    if (e != hipSuccess) return hip_status(e, "selected-block attention");
-  }
-  {
-    StageScope t(ST_SELF, s);
-    e = launch_attn_self(p, q, k, v, cu_seqlens_dev, w, out, lse_out, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "self-block attention");
-  g_err[0] = 0;
-  return MOBA_OK;
+  return forward_enqueue(p, q, k, v, cu_seqlens_dev, out, workspace, sel_out, lse_out,
+                         (hipStream_t)stream);
 }
 
 moba_status_t moba_dense_causal_forward(const void* q, const void* k, const void* v,
@@ -571,6 +613,9 @@ moba_status_t moba_backward(const void* q, const void* k, const void* v, const v
     return fail(MOBA_ERR_INVALID_ARG, "q, k, v, out, lse, dout, dq, dk, dv and cu_seqlens_dev "
                 "must be non-NULL");
   if (p.ks > 0 && !sel) return fail(MOBA_ERR_INVALID_ARG, "sel is NULL (topk > 1)");
+  if (max_grid_items(p, true) > kMaxGridItems)
+    return fail(MOBA_ERR_UNSUPPORTED, "this batch needs a backward launch grid of %lld "
+                "work-items, more than HIP allows", (long long)max_grid_items(p, true));
   if (!workspace) return fail(MOBA_ERR_INVALID_ARG, "workspace is NULL");
   if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   const BwdLayout bl = backward_layout(p);

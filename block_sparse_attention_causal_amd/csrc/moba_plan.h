@@ -23,6 +23,9 @@ constexpr int kRowsPerTile = kRowsPerWave * kAttnWaves;   // routed rows per 8-w
 // tiles of 128 rows (heads x tokens).
 constexpr int kSelWaves = 4;
 constexpr int kSelRowsPerTile = kRowsPerWave * kSelWaves;
+// Backward dK/dV tiles: 8 waves x 32 keys for 16-bit inputs with D = 128, else 4 waves.
+constexpr int kDkvWaves = 8;
+constexpr int kBkvWaves = 4;
 constexpr int kMaxSelected = 16;           // topk - 1 limit (per-lane register lists)
 constexpr int kMaxBlocksPerSeq = 16384;    // per-sequence block counters live in LDS
 
@@ -39,6 +42,7 @@ struct Plan {
   int64_t nb = 0;           // total blocks over all sequences
   int32_t max_nb = 0;       // largest per-sequence block count
   int64_t max_len = 0;      // longest sequence
+  int64_t span = 0;         // longest block: min(block, max_len); per-block tile grids use it
   int64_t tri = 0;          // sum_n Hkv * NB_n * (NB_n - 1) / 2 (route histograms)
   int64_t nlists = 0;       // nb * hkv
   int64_t nentries = 0;     // routed (row, slot) pairs
@@ -58,6 +62,41 @@ struct Plan {
 // adds at most one partial tile. A grid sized by the bound of another tile size would
 // leave workgroups idle and, under the XCD mapping, whole XCDs without work.
 inline int64_t tile_bound(const Plan& p, int rows) { return p.nentries / rows + p.nlists + 1; }
+
+// ---- launch grids, shared by the launchers and the plan's size check -------------
+// Grids whose tile order is XCD-interleaved are padded to a multiple of the 8 XCDs.
+inline int64_t pad8(int64_t n) { return (n + 7) / 8 * 8; }
+// Tokens per tile of the 8-wave per-block tiles (gate, general attention kernels, dQ
+// passes): 8 waves of 32 rows, hg heads side by side.
+inline int tile_tokens8(const Plan& p) { return 32 * (8 / p.hg); }
+// Heads side by side in an own-block tile of the 4-wave kernels: gcd(G, 4).
+inline int attn4_heads(const Plan& p) {
+  return (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
+}
+inline int attn4_tokens(const Plan& p) { return 32 * (kSelWaves / attn4_heads(p)); }
+// Tiles along the tokens of one block: no block is longer than `span`.
+inline int tiles_per_block(const Plan& p, int tokens_per_tile) {
+  return (int)((p.span + tokens_per_tile - 1) / tokens_per_tile);
+}
+inline int64_t gate_tile_count(const Plan& p) {
+  return p.nb * tiles_per_block(p, tile_tokens8(p)) * (p.hq / p.hg);
+}
+inline int64_t self8_tile_count(const Plan& p) {
+  return p.nb * tiles_per_block(p, tile_tokens8(p)) * (p.hq / p.hg);
+}
+inline int64_t self4_tile_count(const Plan& p) {
+  return p.nb * tiles_per_block(p, attn4_tokens(p)) * (p.hq / attn4_heads(p));
+}
+inline int dense_tiles_per_seq(const Plan& p) {
+  return (int)((p.max_len + tile_tokens8(p) - 1) / tile_tokens8(p));
+}
+inline int64_t dense_tile_count(const Plan& p) {
+  return (int64_t)p.nseq * dense_tiles_per_seq(p) * (p.hq / p.hg);
+}
+// Work-items of the largest grid any launch of a forward (or, with `backward`, a
+// backward) call on this plan makes; HIP takes fewer than 2^32 per grid dimension.
+int64_t max_grid_items(const Plan& p, bool backward);
+constexpr int64_t kMaxGridItems = (int64_t(1) << 32) - 1;
 
 // Fills `plan` from validated arguments. Returns MOBA_OK or an error status and
 // writes a message into `err` (size errlen).

@@ -308,8 +308,9 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
                                               const int32_t* __restrict__ blk_seq,
                                               const int32_t* __restrict__ blk_local,
                                               const T* __restrict__ kparts, int64_t nb, int hq,
-                                              int hkv, int hg, int block, int ks, int64_t ntiles,
-                                              int64_t padded, const uint8_t* __restrict__ flags,
+                                              int hkv, int hg, int block, int nu, int ks,
+                                              int64_t ntiles, int64_t padded,
+                                              const uint8_t* __restrict__ flags,
                                               int32_t* __restrict__ sel) {
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LD = D + PAD;
@@ -320,7 +321,6 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
   if (logical >= ntiles) return;
   if (flags && flags[logical] == 0) return;   // the screened selection is already exact
   const int tt = 32 * (8 / hg);                       // tokens per workgroup tile
-  const int nu = (block + tt - 1) / tt;
   const int nhs = hq / hg;
   const int u = (int)(logical % nu);
   const int64_t rest = logical / nu;
@@ -511,8 +511,8 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
                                                    const int32_t* __restrict__ blk_local,
                                                    const bf16* __restrict__ khi,
                                                    const float* __restrict__ bound, int64_t nb,
-                                                   int hq, int hkv, int hg, int block, int ks,
-                                                   int64_t ntiles, int64_t padded,
+                                                   int hq, int hkv, int hg, int block, int nu,
+                                                   int ks, int64_t ntiles, int64_t padded,
                                                    uint8_t* __restrict__ flags,
                                                    int32_t* __restrict__ sel) {
   // Pooled hi keys stream through an LDS ring of GB buffers (32 blocks each,
@@ -528,7 +528,6 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
   const int64_t logical = xcd_logical(blockIdx.x, padded);
   if (logical >= ntiles) return;
   const int tt = 32 * (8 / hg);
-  const int nu = (block + tt - 1) / tt;
   const int nhs = hq / hg;
   const int u = (int)(logical % nu);
   const int64_t rest = logical / nu;
@@ -744,8 +743,8 @@ static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const
   dim3 grid((unsigned)padded), blk(512);
 #define MOBA_GATE(KBV)                                                                        \
   hipLaunchKernelGGL((k_gate<T, D, NP, KBV>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,  \
-                     w.blk_local, parts, p.nb, p.hq, p.hkv, p.hg, p.block, p.ks, ntiles,     \
-                     padded, flags, sel)
+                     w.blk_local, parts, p.nb, p.hq, p.hkv, p.hg, p.block,                   \
+                     tiles_per_block(p, tile_tokens8(p)), p.ks, ntiles, padded, flags, sel)
   if (p.ks <= 2) MOBA_GATE(2);
   else if (p.ks <= 4) MOBA_GATE(4);
   else if (p.ks <= 8) MOBA_GATE(8);
@@ -760,7 +759,8 @@ static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, 
 #define MOBA_GATE_FAST(KBV, CH)                                                                 \
   hipLaunchKernelGGL((k_gate_fast<D, KBV, CH>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,  \
                      w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
-                     p.ks, ntiles, padded, w.gate_flags, sel)
+                     tiles_per_block(p, tile_tokens8(p)), p.ks, ntiles, padded, w.gate_flags,   \
+                     sel)
   // branch-free list updates pay while a row has at most 16 chunks of 32 blocks
   const bool chain = p.max_nb <= 512;
   if (p.ks <= 2) {
@@ -776,10 +776,8 @@ static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, 
 hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, const Work& w,
                        int32_t* sel, hipStream_t s) {
   if (p.ks == 0 || p.nb == 0) return hipSuccess;
-  const int tt = 32 * (8 / p.hg);
-  const int64_t nu = (p.block + tt - 1) / tt;
-  const int64_t ntiles = p.nb * nu * (p.hq / p.hg);
-  const int64_t padded = (ntiles + 7) / 8 * 8;
+  const int64_t ntiles = gate_tile_count(p);
+  const int64_t padded = pad8(ntiles);
   if (p.dtype == MOBA_DTYPE_BF16) {
     // Screened single bf16 pass, then the exact three-pass gate on flagged tiles
     // only. With many kept blocks the list upkeep dominates either way and the

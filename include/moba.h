@@ -40,7 +40,12 @@
  *   message for the calling thread's last failed call.
  * Determinism: outputs are bitwise identical for identical inputs.
  * Limits: D in {64, 128}; block_size a positive multiple of 64; topk-1 <= 16;
- *   T*Hq and T*Hq*(topk-1) below 2^31; at most 16384 blocks per sequence.
+ *   T*Hq and T*Hq*(topk-1) below 2^31; at most 16384 blocks per sequence; every
+ *   launch grid below 2^32 work-items (a batch of very many short sequences
+ *   beside a long one can exceed it: MOBA_ERR_UNSUPPORTED). For bf16 inputs the
+ *   selected-block partial outputs are kept in fp16, so |v| must not exceed
+ *   65504 (fp16's largest finite value); larger values turn outputs into inf or
+ *   NaN without an error.
  */
 #ifndef MOBA_H
 #define MOBA_H

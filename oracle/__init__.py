@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moba_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOBA_ORACLE_LIB selects another build of the same source (the sanitizer test's)
+_LIB_PATH = os.environ.get("MOBA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
@@ -51,6 +52,9 @@ def _load():
     lib.moba_oracle_rows.argtypes = [p, p, p, i64, p, p, p, i32, i32, i32, i32, i32, i32,
                                      f64, p, p, p, p, i32]
     lib.moba_oracle_rows.restype = ctypes.c_int
+    lib.moba_oracle_rows_given_sel.argtypes = [p, p, p, i64, p, p, p, i32, i32, i32, i32, i32,
+                                               i32, p, f64, p, p, i32]
+    lib.moba_oracle_rows_given_sel.restype = ctypes.c_int
     lib.moba_oracle_causal_rows.argtypes = [p, p, p, i64, p, p, p, i32, i32, i32, i32, f64,
                                             p, p, i32]
     lib.moba_oracle_causal_rows.restype = ctypes.c_int
@@ -145,6 +149,34 @@ def rows(q, k, v, cu_seqlens, block: int, topk: int, tokens, heads, scale: float
     if rc != 0:
         raise ValueError("moba_oracle_rows failed with code %d" % rc)
     return {"out": out, "lse": lse, "sel": sel[:, :max(topk - 1, 0)], "margin": margin}
+
+
+def rows_given_sel(q, k, v, cu_seqlens, block: int, topk: int, tokens, heads, sel,
+                   scale: float = 0.0, k_f32=None, v_f32=None, nthreads: int = 0,
+                   num_q_heads: int | None = None) -> dict:
+    """Attention of the given rows over their own-block prefix and the past blocks
+    named in sel [n, topk-1] (sequence-local ids, -1 skipped) instead of the gated
+    ones, exact in fp64. Raises ValueError on an id that is not a distinct past
+    block of its row. Returns dict(out [n, D], lse [n])."""
+    qr, tokens, heads = _row_queries(q, tokens, heads)
+    kf = _f32(k) if k_f32 is None else k_f32
+    vf = _f32(v) if v_f32 is None else v_f32
+    cu = _i32(cu_seqlens)
+    n = len(tokens)
+    T, hkv, d = kf.shape
+    hq = q.shape[1] if q.ndim == 3 else int(num_q_heads)
+    ks = max(topk - 1, 0)
+    sl = np.ascontiguousarray(_i32(sel).reshape(n, ks) if ks > 0
+                              else np.zeros((n, 1), dtype=np.int32))
+    out = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().moba_oracle_rows_given_sel(_ptr(qr), _ptr(tokens), _ptr(heads), n, _ptr(kf),
+                                            _ptr(vf), _ptr(cu), len(cu) - 1, hq, hkv, d, block,
+                                            topk, _ptr(sl), float(scale),
+                                            _ptr(out), _ptr(lse), int(nthreads))
+    if rc != 0:
+        raise ValueError("moba_oracle_rows_given_sel failed with code %d" % rc)
+    return {"out": out, "lse": lse}
 
 
 def causal_rows(q, k, v, cu_seqlens, tokens, heads, scale: float = 0.0, k_f32=None,

@@ -164,6 +164,49 @@ static void gate_and_select(const float* q, const double* kbar_g, int64_t i, int
   }
 }
 
+/* Step 5 for one row: the attended key set A is the own block's prefix
+ * {s : i*B <= s <= t} (causal) followed by every token of each chosen past
+ * block (chosen[0..nsel), sequence-local ids, all complete blocks). Logits
+ * c * q . k_s are stored first, then a softmax with the maximum taken out, then
+ * the weighted sum of V; lse = max + log(sum of weights). `logit` has room for
+ * block * (nsel + 1) values. Token indices are packed: the row's sequence starts
+ * at token `start` and the row is token `tok`. */
+static void attend_row(const float* q, const float* k, const float* v, int32_t hkv, int32_t d,
+                       int32_t g, int64_t start, int64_t i, int64_t tok, int32_t block,
+                       const int32_t* chosen, int64_t nsel, double scale, double* logit,
+                       double* o, double* lse_row) {
+  int64_t na = 0;
+  for (int64_t s = start + i * block; s <= tok; ++s)
+    logit[na++] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
+  for (int64_t m = 0; m < nsel; ++m) {
+    int64_t s0 = start + (int64_t)chosen[m] * block;
+    for (int64_t s = s0; s < s0 + block; ++s)   /* past blocks are full */
+      logit[na++] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
+  }
+  double mx = -INFINITY;
+  for (int64_t a = 0; a < na; ++a) if (logit[a] > mx) mx = logit[a];
+  double denom = 0.0;
+  for (int32_t e = 0; e < d; ++e) o[e] = 0.0;
+  int64_t a = 0;
+  for (int64_t s = start + i * block; s <= tok; ++s, ++a) {
+    double w = exp(logit[a] - mx);
+    denom += w;
+    const float* vs = v + (s * hkv + g) * d;
+    for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
+  }
+  for (int64_t m = 0; m < nsel; ++m) {
+    int64_t s0 = start + (int64_t)chosen[m] * block;
+    for (int64_t s = s0; s < s0 + block; ++s, ++a) {
+      double w = exp(logit[a] - mx);
+      denom += w;
+      const float* vs = v + (s * hkv + g) * d;
+      for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
+    }
+  }
+  for (int32_t e = 0; e < d; ++e) o[e] /= denom;
+  *lse_row = mx + log(denom);
+}
+
 /* Steps 3-5 for a list of rows.
  *
  * q_rows:   [nrows, d] fp32, the query vector of each requested row.
@@ -256,40 +299,9 @@ int moba_oracle_rows(const float* q_rows, const int32_t* row_tok, const int32_t*
           for (; w < topk - 1; ++w) srow[w] = -1;
         }
 
-        /* Step 5: the attended key set A, own block first (causal), then the
-         * selected blocks. Logits are stored, then softmax with the max taken
-         * out, then the weighted sum of V. */
-        int64_t na = 0;
-        for (int64_t s = start + i * block; s <= tok; ++s)
-          logit[na++] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
-        for (int64_t m = 0; m < nsel; ++m) {
-          int64_t s0 = start + (int64_t)chosen[m] * block;
-          for (int64_t s = s0; s < s0 + block; ++s)   /* past blocks are full */
-            logit[na++] = scale * dot_ff(q, k + (s * hkv + g) * d, d);
-        }
-        double mx = -INFINITY;
-        for (int64_t a = 0; a < na; ++a) if (logit[a] > mx) mx = logit[a];
-        double denom = 0.0;
-        double* o = out + r * d;
-        for (int32_t e = 0; e < d; ++e) o[e] = 0.0;
-        int64_t a = 0;
-        for (int64_t s = start + i * block; s <= tok; ++s, ++a) {
-          double w = exp(logit[a] - mx);
-          denom += w;
-          const float* vs = v + (s * hkv + g) * d;
-          for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
-        }
-        for (int64_t m = 0; m < nsel; ++m) {
-          int64_t s0 = start + (int64_t)chosen[m] * block;
-          for (int64_t s = s0; s < s0 + block; ++s, ++a) {
-            double w = exp(logit[a] - mx);
-            denom += w;
-            const float* vs = v + (s * hkv + g) * d;
-            for (int32_t e = 0; e < d; ++e) o[e] += w * (double)vs[e];
-          }
-        }
-        for (int32_t e = 0; e < d; ++e) o[e] /= denom;
-        lse[r] = mx + log(denom);
+        /* Step 5 over the own-block prefix and the blocks just chosen. */
+        attend_row(q, k, v, hkv, d, g, start, i, tok, block, chosen, nsel, scale, logit,
+                   out + r * d, lse + r);
       }
     }
     free(sigma);
@@ -299,6 +311,75 @@ int moba_oracle_rows(const float* q_rows, const int32_t* row_tok, const int32_t*
   }
   free(kbar);
   free(block_base);
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Step 5 alone for a list of rows, with the kept past blocks given instead of
+ * gated: sel_in [nrows, topk-1] int32 lists sequence-local block ids (entries
+ * < 0 are skipped; every other entry must be a distinct past block of the row,
+ * 0 <= j < i, else the call fails with ORACLE_BAD_ARG). This evaluates the
+ * attention a row would get from that selection: it serves to check a GPU's
+ * output on rows whose selection is one of several valid top-(topk-1) sets
+ * (scores tied within rounding). Other arguments as moba_oracle_rows. */
+int moba_oracle_rows_given_sel(const float* q_rows, const int32_t* row_tok,
+                               const int32_t* row_head, int64_t nrows, const float* k,
+                               const float* v, const int32_t* cu_seqlens, int32_t nseq,
+                               int32_t hq, int32_t hkv, int32_t d, int32_t block, int32_t topk,
+                               const int32_t* sel_in, double scale, double* out, double* lse,
+                               int32_t nthreads) {
+  if (!q_rows || !row_tok || !row_head || !k || !v || !out || !lse || nrows < 0 ||
+      topk < 1 || !check_layout(cu_seqlens, nseq, hq, hkv, d, block))
+    return ORACLE_BAD_ARG;
+  if (topk > 1 && !sel_in) return ORACLE_BAD_ARG;
+  const int64_t T = cu_seqlens[nseq];
+  const int32_t ks = topk - 1;
+  for (int64_t r = 0; r < nrows; ++r) {
+    if (row_tok[r] < 0 || row_tok[r] >= T || row_head[r] < 0 || row_head[r] >= hq)
+      return ORACLE_BAD_ARG;
+    const int32_t n = seq_of_token(cu_seqlens, nseq, row_tok[r]);
+    const int64_t i = (row_tok[r] - (int64_t)cu_seqlens[n]) / block;
+    for (int32_t a = 0; a < ks; ++a) {
+      const int32_t j = sel_in[r * ks + a];
+      if (j < 0) continue;
+      if (j >= i) return ORACLE_BAD_ARG;
+      for (int32_t b = 0; b < a; ++b)
+        if (sel_in[r * ks + b] == j) return ORACLE_BAD_ARG;
+    }
+  }
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+  const int32_t group = hq / hkv;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* logit = (double*)malloc(sizeof(double) * (size_t)block * (size_t)topk);
+    int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)topk);
+    if (!logit || !chosen) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t tok = row_tok[r];
+        const int32_t n = seq_of_token(cu_seqlens, nseq, tok);
+        const int64_t start = cu_seqlens[n];
+        const int64_t i = (tok - start) / block;
+        int64_t nsel = 0;
+        for (int32_t a = 0; a < ks; ++a)
+          if (sel_in[r * ks + a] >= 0) chosen[nsel++] = sel_in[r * ks + a];
+        attend_row(q_rows + r * d, k, v, hkv, d, row_head[r] / group, start, i, tok, block,
+                   chosen, nsel, scale, logit, out + r * d, lse + r);
+      }
+    }
+    free(logit);
+    free(chosen);
+  }
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 

@@ -190,13 +190,15 @@ def make_config(name: str, seed=0, device="cpu", **over) -> Inputs:
                        **{k: v for k, v in over.items() if k in ("plant", "alpha", "beta")})
 
 
-def sample_tokens(seqlens, block: int, n_tokens: int, seed: int = 0) -> np.ndarray:
+def sample_tokens(seqlens, block: int, n_tokens: int, seed: int = 0,
+                  every_block: bool = False) -> np.ndarray:
     """Seeded sample of packed token indices for sampled-row checks.
 
     Always includes: the first and last token of every sequence, the first and last
     token of blocks 0, 1 and 2 of every sequence (rows with fewer than topk-1 past
-    blocks), and the first token of each sequence's last block; the rest are drawn
-    uniformly over all tokens. Sorted, unique.
+    blocks), and the first token of each sequence's last block; with every_block, also
+    one uniformly drawn token of every block of every sequence. The rest, up to
+    n_tokens, are drawn uniformly over all tokens. Sorted, unique.
     """
     rng = np.random.default_rng(seed)
     fixed, start = [], 0
@@ -208,8 +210,14 @@ def sample_tokens(seqlens, block: int, n_tokens: int, seed: int = 0) -> np.ndarr
                 if b * block < s:
                     fixed += [start + b * block, start + min((b + 1) * block, s) - 1]
             fixed.append(start + ((s - 1) // block) * block)
+            if every_block:
+                nb = (s + block - 1) // block
+                lo = np.arange(nb, dtype=np.int64) * block
+                hi = np.minimum(lo + block, s)
+                fixed += (start + lo + rng.integers(0, hi - lo)).tolist()
         start += s
-    fixed = sorted(set(fixed))
-    extra = max(0, n_tokens - len(fixed))
-    rand = rng.integers(0, T, size=extra) if T > 0 else np.zeros(0, dtype=np.int64)
-    return np.unique(np.concatenate([np.asarray(fixed, dtype=np.int64), rand])).astype(np.int32)
+    picked = np.unique(np.asarray(fixed, dtype=np.int64))
+    want = min(int(n_tokens), T)
+    while picked.size < want:          # uniform extras until n_tokens distinct tokens
+        picked = np.unique(np.concatenate([picked, rng.integers(0, T, size=want - picked.size)]))
+    return picked.astype(np.int32)

@@ -327,3 +327,37 @@ def test_profiling_copy_calibration_sums_split_launches(tmp_path):
     txt = profiling.dram(ddir, 4096)
     assert "copy_read_bytes: 4.29497e+09 (ratio 1.0000)" in txt
     assert "| attn_selected | 1 | 1.0000 | 2.0000 |" in txt
+
+
+def test_binding_argument_checks():
+    """The binding's host checks that keep a call from reading or writing past a
+    tensor: cu_seqlens must end at the tensors' token count, caller outputs must
+    mirror their inputs, caches must hold the tokens cu_k names, the pooled-key
+    cache must hold num_seqs * max_blocks blocks, and a workspace must be a byte
+    buffer on the right device of the needed size."""
+    q = torch.zeros(100, 4, 64)
+    moba._check_cu_total(torch.tensor([0, 40, 100], dtype=torch.int32), 100)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        moba._check_cu_total(torch.tensor([0, 40, 120], dtype=torch.int32), 100)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        moba._check_cu_total(torch.tensor([0, 40], dtype=torch.int32), 100)
+    moba._check_like("out", None, q)
+    moba._check_like("out", torch.empty_like(q), q)
+    for bad in (torch.zeros(99, 4, 64), torch.zeros(100, 4, 64, dtype=torch.bfloat16),
+                torch.zeros(100, 64, 4).transpose(1, 2)):
+        with pytest.raises(ValueError, match="out"):
+            moba._check_like("out", bad, q)
+    kc = torch.zeros(300, 2, 64)
+    moba._check_kv_cache(kc, torch.tensor([0, 100, 300], dtype=torch.int32), "k_cache")
+    with pytest.raises(ValueError, match="k_cache"):
+        moba._check_kv_cache(kc, torch.tensor([0, 100, 301], dtype=torch.int32), "k_cache")
+    moba._check_kbar_cache(torch.zeros(2 * 5, 2, 64), kc, 2, 5)
+    with pytest.raises(ValueError, match="kbar_cache"):
+        moba._check_kbar_cache(torch.zeros(2 * 5 - 1, 2, 64), kc, 2, 5)
+    with pytest.raises(ValueError, match="kbar_cache"):
+        moba._check_kbar_cache(torch.zeros(10, 2, 64, dtype=torch.float64), kc, 2, 5)
+    moba._check_workspace(torch.zeros(1000, dtype=torch.uint8), q, 1000)
+    with pytest.raises(ValueError, match="workspace"):
+        moba._check_workspace(torch.zeros(999, dtype=torch.uint8), q, 1000)
+    with pytest.raises(ValueError, match="workspace"):
+        moba._check_workspace(torch.zeros(1000, dtype=torch.float32), q, 1000)

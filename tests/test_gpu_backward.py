@@ -120,8 +120,10 @@ def test_backward_full_size(name):
     dout = make_grad(inp.q.shape, cfg["dtype"], seed=3, device="cuda", mean=0.25)
     sel, dq, dk, dv = _fwd_bwd(inp, dout)
     assert torch.equal(sel.cpu(), inp.targets)
-    toks = sample_tokens(inp.seqlens, inp.block, 32, seed=4)
+    # dq on 1,024 tokens x every q head, at least one token of every block
+    toks = sample_tokens(inp.seqlens, inp.block, 1024, seed=4, every_block=True)
     hq = cfg["hq"]
+    print("oracle dq rows: %d tokens x %d heads" % (len(toks), hq), flush=True)
     tt, hh = np.repeat(toks, hq), np.tile(np.arange(hq), len(toks))
     ref = oracle.dq_rows(inp.q, inp.k, inp.v, dout, inp.cu_seqlens, inp.block, inp.topk, tt, hh)
     got = dq[torch.as_tensor(tt, device="cuda"), torch.as_tensor(hh, device="cuda")]

@@ -66,11 +66,65 @@ BRUTE_CASES = [
 def test_oracle_matches_dense_mask_brute_force(oracle_mod, case):
     seqlens, hq, hkv, d, block, topk = case
     q, k, v, cu = _rand_inputs(seqlens, hq, hkv, d, seed=len(seqlens) * 7 + d)
-    ref_out, ref_lse, ref_sel = brute_force(_np(q), _np(k), _np(v), seqlens, block, topk)
+    ref_out, ref_lse, ref_sel, ref_margin = brute_force(_np(q), _np(k), _np(v), seqlens, block,
+                                                        topk, return_margin=True)
     res = oracle_mod.all_rows(q, k, v, cu, block, topk)
     np.testing.assert_array_equal(res["sel"], ref_sel)
     np.testing.assert_allclose(res["out"], ref_out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(res["lse"], ref_lse, rtol=1e-13, atol=1e-12)
+    # the margin (lowest kept score minus highest score left out) decides which
+    # rows a GPU test compares by selection; the brute force computes it from its
+    # own dense score matrix
+    fin = np.isfinite(ref_margin)
+    np.testing.assert_array_equal(np.isfinite(res["margin"]), fin)
+    np.testing.assert_allclose(res["margin"][fin], ref_margin[fin], rtol=0, atol=1e-12)
+    if topk > 1 and fin.any():
+        assert (ref_margin[fin] > 0).all()          # random scores: no exact ties
+
+
+def _random_valid_selection(seqlens, hq, block, topk, seed):
+    """For every row, a random set of min(topk-1, i) distinct past blocks (not the
+    gated ones), ascending, -1 padded."""
+    rng = np.random.default_rng(seed)
+    ks = topk - 1
+    rows = []
+    for S in seqlens:
+        for t in range(S):
+            i = t // block
+            for _ in range(hq):
+                c = np.sort(rng.choice(i, size=min(ks, i), replace=False)) if i else []
+                rows.append(list(c) + [-1] * (ks - len(c)))
+    return np.asarray(rows, dtype=np.int32).reshape(sum(seqlens), hq, ks)
+
+
+@pytest.mark.parametrize("case", [([700, 0, 333], 4, 2, 16, 64, 4), ([1024], 2, 1, 8, 128, 3)])
+def test_rows_given_sel_matches_brute_force(oracle_mod, case):
+    """Attention over a forced selection (what a GPU's near-tied choice is checked
+    against): the brute force's dense mask built from the same forced blocks."""
+    seqlens, hq, hkv, d, block, topk = case
+    q, k, v, cu = _rand_inputs(seqlens, hq, hkv, d, seed=77)
+    sel = _random_valid_selection(seqlens, hq, block, topk, seed=5)
+    ref_out, ref_lse, _ = brute_force(_np(q), _np(k), _np(v), seqlens, block, topk, sel_in=sel)
+    T = sum(seqlens)
+    tt, hh = np.repeat(np.arange(T), hq), np.tile(np.arange(hq), T)
+    res = oracle_mod.rows_given_sel(q, k, v, cu, block, topk, tt, hh, sel.reshape(T * hq, -1))
+    np.testing.assert_allclose(res["out"].reshape(T, hq, d), ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["lse"].reshape(T, hq), ref_lse, rtol=1e-13, atol=1e-12)
+    # on its own gated selection it is the full oracle (blocks summed in ascending
+    # order instead of the order taken: equal up to fp64 rounding)
+    full = oracle_mod.rows(q, k, v, cu, block, topk, tt, hh)
+    again = oracle_mod.rows_given_sel(q, k, v, cu, block, topk, tt, hh, full["sel"])
+    np.testing.assert_allclose(again["out"], full["out"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(again["lse"], full["lse"], rtol=1e-14, atol=1e-13)
+    # ids that are not distinct past blocks are refused
+    bad = sel.reshape(T * hq, -1).copy()
+    r = int(np.nonzero((tt // block) == 2)[0][0])     # a row in block 2
+    bad[r, 0] = 2                                       # its own block
+    with pytest.raises(ValueError):
+        oracle_mod.rows_given_sel(q, k, v, cu, block, topk, tt, hh, bad)
+    bad[r, :2] = [1, 1]                                 # a duplicate
+    with pytest.raises(ValueError):
+        oracle_mod.rows_given_sel(q, k, v, cu, block, topk, tt, hh, bad)
 
 
 def test_planted_tiny_matches_brute_force_and_targets(oracle_mod):
