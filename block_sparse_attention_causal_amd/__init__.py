@@ -57,6 +57,7 @@ def _load():
         "moba_last_error": ([], ctypes.c_char_p),
         "moba_workspace_bytes": ([p, i32, shp, i32, i32], sz),
         "moba_forward": ([p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p], ctypes.c_int),
+        "moba_forward_noalloc": ([p, p, p, p, p, i32, shp, i32, i32, p, p, p, p], ctypes.c_int),
         "moba_dense_causal_forward": ([p, p, p, p, p, i32, shp, p, p, p], ctypes.c_int),
         "moba_attention_forward": ([i32, p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p],
                                    ctypes.c_int),
@@ -87,7 +88,7 @@ def exported_symbols():
     """Names the binding resolves in libmoba.so (loading fails if any is missing)."""
     _load()
     return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
-            "moba_dense_causal_forward", "moba_attention_forward",
+            "moba_forward_noalloc", "moba_dense_causal_forward", "moba_attention_forward",
             "moba_block_pool", "moba_kbar_append", "moba_decode_workspace_bytes", "moba_decode_forward",
             "moba_backward_workspace_bytes", "moba_backward", "moba_route_sizes", "moba_route",
             "moba_timing_enable", "moba_timing_read", "moba_stage_name"]
@@ -240,6 +241,36 @@ def moba_forward(q, k, v, cu_seqlens, block_size, topk, *, out=None, workspace=N
                             host.numel() - 1, ctypes.byref(shape), int(block_size), int(topk),
                             _ptr(out), _ptr(workspace), workspace.numel(), _ptr(sel), _ptr(lse),
                             _stream(dev)))
+    res = [out]
+    if return_sel:
+        res.append(sel if sel is not None else torch.empty(T, hq, 0, dtype=torch.int32, device=dev))
+    if return_lse:
+        res.append(lse)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def moba_forward_noalloc(q, k, v, cu_seqlens, block_size, topk, *, out=None, return_sel=False,
+                         return_lse=False, softmax_scale=0.0, cu_seqlens_dev=None):
+    """moba_forward with the workspace in the library's static scratch (no device
+    allocation inside the call; batches whose workspace exceeds the scratch are
+    refused). Same arguments and results as moba_forward, without `workspace`."""
+    _check_qkv(q, k, v)
+    dev = q.device
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    host, cu_dev = _cu(cu_seqlens, dev, cu_seqlens_dev)
+    _check_cu_total(host, T)
+    _check_like("out", out, q)
+    shape = _shape(hq, hkv, d, q.dtype, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    sel = torch.empty(T, hq, max(topk - 1, 0), dtype=torch.int32, device=dev) \
+        if (return_sel and topk > 1) else None
+    lse = torch.empty(T, hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(_load().moba_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_dev), _ptr(host),
+                                        host.numel() - 1, ctypes.byref(shape), int(block_size),
+                                        int(topk), _ptr(out), _ptr(sel), _ptr(lse),
+                                        _stream(dev)))
     res = [out]
     if return_sel:
         res.append(sel if sel is not None else torch.empty(T, hq, 0, dtype=torch.int32, device=dev))

@@ -385,6 +385,39 @@ static moba_status_t forward_enqueue(const Plan& p, const void* q, const void* k
   return MOBA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch for moba_forward_noalloc: a device array in this code object,
+// one copy per GPU, alive until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is handed to the kernels.
+constexpr size_t kScratchBytes = MOBA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static moba_status_t scratch_pointer(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOBA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (uintptr_t)p % 256)
+      return fail(MOBA_ERR_HIP, "static scratch has an unusable address %p", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOBA_OK;
+}
+
 }  // namespace moba
 
 using namespace moba;
@@ -426,6 +459,32 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
     return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 p.total);
   return forward_enqueue(p, q, k, v, cu_seqlens_dev, out, workspace, sel_out, lse_out,
+                         (hipStream_t)stream);
+}
+
+moba_status_t moba_forward_noalloc(const void* q, const void* k, const void* v,
+                                   const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                   int32_t num_seqs, const moba_shape_t* shape,
+                                   int32_t block_size, int32_t topk, void* out,
+                                   int32_t* sel_out, float* lse_out, void* stream) {
+  Plan p;
+  moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  if (p.total > kScratchBytes)
+    return fail(MOBA_ERR_WORKSPACE, "this batch needs %zu bytes of workspace, more than the "
+                "%zu bytes of the library's static scratch; use moba_forward", p.total,
+                (size_t)kScratchBytes);
+  if (p.T == 0) {
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  if (!q || !k || !v || !out || !cu_seqlens_dev)
+    return fail(MOBA_ERR_INVALID_ARG, "q, k, v, out and cu_seqlens_dev must be non-NULL");
+  void* ws = nullptr;
+  st = scratch_pointer(&ws);
+  if (st != MOBA_OK) return st;
+  return forward_enqueue(p, q, k, v, cu_seqlens_dev, out, ws, sel_out, lse_out,
                          (hipStream_t)stream);
 }
 

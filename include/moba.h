@@ -112,6 +112,31 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
                            int32_t topk, void* out, void* workspace, size_t workspace_bytes,
                            int32_t* sel_out, float* lse_out, void* stream);
 
+/* moba_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and outputs as moba_forward, with the workspace
+ * taken from a static scratch array inside the library instead of a caller
+ * buffer. Nothing is allocated: no hipMalloc, hipFree or allocating library
+ * routine is called.
+ *   Limit: the batch's moba_workspace_bytes(...) must be at most
+ *          MOBA_NOALLOC_SCRATCH_BYTES (256 MiB; e.g. 8192 tokens x 32 q heads at
+ *          topk 3 in bf16 fit); larger batches return MOBA_ERR_WORKSPACE with
+ *          nothing enqueued.
+ *   Scratch: one array per GPU the library runs on, resident from the library's
+ *          first use of that GPU until the process ends; its device address is
+ *          looked up once per device, on the first call made with that device
+ *          current. Every call on a GPU shares that GPU's array and leaves its
+ *          contents behind; no call relies on them (each call writes every
+ *          scratch word it reads). Calls whose work overlaps on one GPU (other
+ *          streams, or other threads) race on the array: serialise them.
+ *   Arguments, layouts, outputs and errors otherwise as moba_forward. */
+#define MOBA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+moba_status_t moba_forward_noalloc(const void* q, const void* k, const void* v,
+                                   const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                   int32_t num_seqs, const moba_shape_t* shape,
+                                   int32_t block_size, int32_t topk, void* out,
+                                   int32_t* sel_out, float* lse_out, void* stream);
+
 /* Dense causal flash attention with the same kernels (one block per sequence):
  * every row attends to keys 0..t of its own sequence. The comparison point for
  * MoBA's speed-up (README, "Seamlessly Transition between Full and Sparse

@@ -329,6 +329,32 @@ def test_profiling_copy_calibration_sums_split_launches(tmp_path):
     assert "| attn_selected | 1 | 1.0000 | 2.0000 |" in txt
 
 
+def _noalloc(lib, cu, shape, block, topk, ptr=FAKE):
+    return lib.moba_forward_noalloc(ptr, ptr, ptr, ptr, ctypes.c_void_p(cu.data_ptr()),
+                                    cu.numel() - 1, ctypes.byref(shape), block, topk, ptr, None,
+                                    None, None)
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch(lib):
+    """The no-allocation forward takes its workspace from a 256 MiB static array:
+    a batch needing more is refused on the host, before any HIP call."""
+    limit = 256 << 20
+    big = _cu([1 << 20])                                   # the 1M-token workload
+    assert moba.moba_workspace_bytes(big, 32, 8, 128, torch.bfloat16, 2048, 3) > limit
+    assert _noalloc(lib, big, _shape(), 2048, 3) == moba.MOBA_ERR_WORKSPACE
+    assert "scratch" in lib.moba_last_error().decode()
+    small = _cu([4096, 1000])
+    assert moba.moba_workspace_bytes(small, 32, 8, 128, torch.bfloat16, 2048, 3) <= limit
+    # within the limit, the pointers are checked next (still no HIP call)
+    assert _noalloc(lib, small, _shape(), 2048, 3, ptr=None) == moba.MOBA_ERR_INVALID_ARG
+    # shape errors as moba_forward's
+    assert _noalloc(lib, small, _shape(d=96), 2048, 3) == moba.MOBA_ERR_UNSUPPORTED
+    assert _noalloc(lib, torch.tensor([0, 100, 50], dtype=torch.int32), _shape(), 64, 3) == \
+        moba.MOBA_ERR_INVALID_ARG
+    # an empty batch is a no-op
+    assert _noalloc(lib, _cu([0]), _shape(), 2048, 3, ptr=None) == moba.MOBA_OK
+
+
 def test_binding_argument_checks():
     """The binding's host checks that keep a call from reading or writing past a
     tensor: cu_seqlens must end at the tensors' token count, caller outputs must
