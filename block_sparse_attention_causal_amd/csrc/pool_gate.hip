@@ -571,13 +571,21 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
     const int slot = threadIdx.x;                        // 16-byte slot in a buffer
     const int srow = slot / PIECES_ROW;
     const int spiece = (slot % PIECES_ROW) ^ (swz(srow) & (PIECES_ROW - 1));
+    // the lane's piece of block srow, and the last block it may read: chunk st
+    // reads block min(32 st + srow, i - 1) (chunks past the end repeat in-range
+    // blocks, never used), one 64-bit add per chunk
+    const char* kpiece = (const char*)(khi + ((gbase + srow) * hkv + g) * D + 8 * spiece);
+    const int kmax = i - 1 - srow;                       // may be negative: then block i - 1
+    const int64_t kstride = (int64_t)hkv * D * (int64_t)sizeof(bf16);
     auto issue = [&](int st) __attribute__((always_inline)) {
-      const int jj = min(min(st, nsteps - 1) * 32 + srow, i - 1);
-      dma16(khi + ((gbase + jj) * hkv + g) * D + 8 * spiece,
+      dma16(kpiece + (int64_t)min(32 * st, kmax) * kstride,
             kb_lds + (uint32_t)(((st % GB) * KBUF + 8 * (threadIdx.x - lane)) * 2));
     };
     const int rx = swz(r32) & (PIECES_ROW - 1);
-    // S~^T of chunk st (the LDS buffer holds it), blocks >= i set to -inf
+    // blocks >= i score -inf; in the packed chain the lowest finite value instead
+    // (packing the low mantissa bits of an infinity would make a NaN)
+    constexpr float kMasked = CHAIN ? -3.4028234663852886e38f : -INFINITY;
+    // S~^T of chunk st (the LDS buffer holds it), blocks >= i masked
     auto scores = [&](int st, f32x16& acc) __attribute__((always_inline)) {
       const bf16* kr = &kb[st % GB][r32 * D];
 #pragma unroll
@@ -587,9 +595,10 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
         acc = mma_k16(load8(kr + 8 * (((2 * kk) | half) ^ rx)), qf[kk], acc);
       const int j0 = st * 32;
       if (j0 + 32 > i) {
+        const int lim = i - j0 - 4 * half;               // positions >= lim are past i
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
+          if (8 * (e >> 2) + (e & 3) >= lim) acc[e] = kMasked;
       }
     };
     auto max16 = [](const f32x16& acc) __attribute__((always_inline)) {
@@ -602,6 +611,9 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
     // Every score either enters the list (and whatever it evicts is left out)
     // or is left out at once, so out_max ends as the best score not kept.
     float ws = -INFINITY;
+    float tl[KB];                          // the packed chain's sorted values
+#pragma unroll
+    for (int p = 0; p < KB; ++p) tl[p] = -INFINITY;
     MOBA_WAIT_VM_LGKM0(0);                 // Q before any direct load
     for (int st = 0; st < GB - 1; ++st) issue(st);
     MOBA_WAIT_VM_LGKM0(GB - 2);
@@ -612,34 +624,27 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
       scores(st, acc);
       if constexpr (CHAIN) {
         // Few chunks (sequences of up to 512 blocks), where many scores still
-        // enter: every score passes through the lane's list without a branch,
-        // in ascending block order. With the scores t sorted descending,
+        // enter: every score passes through the lane's list without a branch.
+        // The score carries its place in the lane's stream in its 8 low
+        // mantissa bits (chunk st, position e: code 16 st + e, put in with one
+        // byte permute), so the list is a list of values and the block comes
+        // back from the bits at the end. With the values t sorted descending,
         // admitting s gives t'_0 = max(t_0, s) and t'_p = med3(t_{p-1}, t_p, s);
-        // an entry's block moves down one place where s beats the entry above
-        // it, and s takes the first place whose entry it beats (strictly: an
-        // equal score from a later block ranks after). The score that falls off
-        // the end, min(t_last, s), is left out; since nothing left out exceeds
-        // t_last, the best of them updates as med3(out, t_last, s). The list
-        // holds all KB >= ks entries. A block is kept as its position e in its
-        // chunk minus 16 for every chunk since (e is then an instruction
-        // constant), decoded after the loop; an entry whose score is still -inf
-        // never held a block.
-#pragma unroll
-        for (int p = 0; p < KB; ++p) bj[p] -= 16;
+        // the value that falls off the end, min(t_last, s), is left out, and
+        // since nothing left out exceeds t_last the best of them updates as
+        // med3(out, t_last, s). Clearing 8 low bits moves a score by less than
+        // 2^-15 of itself; the screen below adds that to its error bound, so
+        // the selection it accepts is still the exact-score selection. Every
+        // packed value of a lane is distinct (distinct codes).
+        const uint32_t cbase = 16u * (uint32_t)st;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float sc = acc[e];
-          bool c[KB];
+          const float sc = __uint_as_float(__builtin_amdgcn_perm(
+              cbase + (uint32_t)e, __float_as_uint(acc[e]), 0x03020104u));
+          out_max = __builtin_amdgcn_fmed3f(out_max, tl[KB - 1], sc);
 #pragma unroll
-          for (int p = 0; p < KB; ++p) c[p] = sc > bs[p];
-          out_max = __builtin_amdgcn_fmed3f(out_max, bs[KB - 1], sc);
-#pragma unroll
-          for (int p = KB - 1; p > 0; --p) {
-            bj[p] = c[p - 1] ? bj[p - 1] : (c[p] ? e : bj[p]);
-            bs[p] = __builtin_amdgcn_fmed3f(bs[p - 1], bs[p], sc);
-          }
-          bj[0] = c[0] ? e : bj[0];
-          bs[0] = vmax(bs[0], sc);
+          for (int p = KB - 1; p > 0; --p) tl[p] = __builtin_amdgcn_fmed3f(tl[p - 1], tl[p], sc);
+          tl[0] = vmax(tl[0], sc);
         }
       } else {
         // Insert the lane's scores above the cut best first, one per trip (a lane
@@ -670,19 +675,21 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
     }
     MOBA_WAIT_VM_LGKM0(0);
     if constexpr (CHAIN) {
-      // positions to blocks; entries past ks are left out too
+      // codes to blocks; entries past ks are left out too, and entries below
+      // every finite score never held a block (masked or never filled)
 #pragma unroll
       for (int p = 0; p < KB; ++p) {
-        const int cd = bj[p] + 16 * (nsteps - 1);  // 16 st + e
-        bj[p] = (bs[p] == -INFINITY)
-                    ? kNoBlock
-                    : 32 * (cd >> 4) + 8 * ((cd & 15) >> 2) + 4 * half + (cd & 3);
-        if (p >= ks) {
-          out_max = vmax(out_max, bs[p]);
-          bs[p] = -INFINITY;
-          bj[p] = kNoBlock;
+        const uint32_t cd = __float_as_uint(tl[p]) & 0xffu;
+        const bool real = tl[p] > -1e38f;
+        if (p < ks) {
+          bs[p] = real ? tl[p] : -INFINITY;
+          bj[p] = real ? 32 * (int)(cd >> 4) + 8 * (int)((cd & 15) >> 2) + 4 * half + (int)(cd & 3)
+                       : kNoBlock;
+        } else if (real) {
+          out_max = vmax(out_max, tl[p]);
         }
       }
+      if (!(out_max > -1e38f)) out_max = -INFINITY;
     }
     float os[KB];
     int oj[KB];
@@ -699,13 +706,24 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
 #pragma unroll
       for (int p = 0; p < KB; ++p)
         if (p == ks - 1) s_in = bs[p];
+      // |q|^2 from packed bf16 pairs (products exact; the screen's bound has room
+      // for the rounding of the sum)
       float qq = 0.f;
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e)
+      for (int e = 0; e < D / 16; ++e) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+        const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, qf[e]);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) qq = fmaf((float)qf[e][x], (float)qf[e][x], qq);
+        for (int x = 0; x < 4; ++x) {
+          const bf16x2_t v2 = {v8[2 * x], v8[2 * x + 1]};
+          qq = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, qq, false);
+        }
+      }
       const float qnorm = sqrtf(qq + swap_half(qq));
-      const float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
+      float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
+      // packed values sit within 2^-15 of their score (low 8 bits cleared)
+      if constexpr (CHAIN) e2 += 0x1p-14f * (fabsf(s_in) + fabsf(out_max));
       unsure = !(s_in - out_max > e2);
     }
   }
@@ -752,6 +770,10 @@ static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const
 #undef MOBA_GATE
 }
 
+// The screened pass keeps its lists branch-free (the packed chain) for sequences of
+// up to 512 blocks: 16 chunks of 32, codes of 8 bits.
+static bool gate_chain(const Plan& p) { return p.max_nb <= 512; }
+
 template <int D>
 static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, const Work& w,
                                int32_t* sel, hipStream_t s, int64_t ntiles, int64_t padded) {
@@ -761,13 +783,15 @@ static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, 
                      w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
                      tiles_per_block(p, tile_tokens8(p)), p.ks, ntiles, padded, w.gate_flags,   \
                      sel)
-  // branch-free list updates pay while a row has at most 16 chunks of 32 blocks
-  const bool chain = p.max_nb <= 512;
-  if (p.ks <= 2) {
-    if (chain) MOBA_GATE_FAST(2, true);
-    else MOBA_GATE_FAST(2, false);
+  if (gate_chain(p)) {
+    // branch-free packed-value lists while a row has at most 16 chunks of 32 blocks
+    if (p.ks <= 2) MOBA_GATE_FAST(2, true);
+    else if (p.ks <= 4) MOBA_GATE_FAST(4, true);
+    else if (p.ks <= 8) MOBA_GATE_FAST(8, true);
+    else if (p.ks <= 12) MOBA_GATE_FAST(12, true);
+    else MOBA_GATE_FAST(16, true);
   } else {
-    if (chain) MOBA_GATE_FAST(4, true);
+    if (p.ks <= 2) MOBA_GATE_FAST(2, false);
     else MOBA_GATE_FAST(4, false);
   }
 #undef MOBA_GATE_FAST
@@ -780,10 +804,9 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
   const int64_t padded = pad8(ntiles);
   if (p.dtype == MOBA_DTYPE_BF16) {
     // Screened single bf16 pass, then the exact three-pass gate on flagged tiles
-    // only. With many kept blocks the list upkeep dominates either way and the
-    // screen only adds a pass (measured: top-12 at 256K, 10.0 ms screened
-    // against 6.3 exact), so it is used for topk - 1 <= 4.
-    const bool screen = p.ks <= 4;
+    // only. The packed chain screens any topk - 1 <= 16; the best-first lists of
+    // longer sequences pay only for topk - 1 <= 4.
+    const bool screen = gate_chain(p) || p.ks <= 4;
     if (screen) {
       hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
                          w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
