@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 CONFIG_NAMES = {"tiny": "moba_fwd_tiny_2k_fp32", "llama32k": "moba_fwd_llama8b_32k",
                 "varlen131k": "moba_fwd_varlen_131k", "1m": "moba_fwd_1m",
                 "fine256k": "moba_fwd_fine_blocks_256k", "10m_shard": "moba_fwd_10m_head_shard",
-                "10m_full": "moba_fwd_10m_full_width_group_major"}
+                "10m_full": "moba_fwd_10m_full_width"}
 
 
 def work_counts(seqlens, hq, hkv, d, block, topk, elem_bytes):
@@ -332,38 +332,34 @@ def bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma, steps):
             "algorithmic_flop": flop, "achieved_tflops": tf, "mfma_frac": tf / peak_mfma}
 
 
-def bench_group_major(moba, torch, args):
-    """A full-width 10M-token layer (32 q heads, 8 kv heads) on one GPU: Q, K, V and
-    out held kv-group-major (one contiguous [T, 4, D] / [T, 1, D] slice per kv head),
-    one moba_forward per group in a step, the workspace shared by the groups. Every
-    MoBA step is independent per kv group, so this is the same computation as the
-    [T, 32, D] layout; the layout keeps the workspace at one group's size (Q, K, V
-    and out already take 205 GB)."""
-    from synth_inputs import CONFIGS, make_config
-    cfg = CONFIGS["10m_shard"]
-    groups = 8
+def bench_10m_full(moba, torch, args):
+    """A full-width 10M-token layer (32 q heads, 8 kv heads, D 128, block 2048,
+    top-3) in the packed [T, H, D] layout, one moba_forward per step. One pass over
+    all heads would need more memory than the GPU has, so the call gets the smallest
+    workspace it accepts and runs the kv groups one after another inside the
+    library (slab copies included in the timed step)."""
+    from synth_inputs import make_10m_full
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    slices = []
-    for gi in range(groups):
-        print("[bench] building inputs, kv group %d" % gi, file=sys.stderr, flush=True)
-        inp = make_config("10m_shard", seed=args.seed + gi, device=dev)
-        slices.append((inp.q, inp.k, inp.v, torch.empty_like(inp.q)))
-    T, hq, d = slices[0][0].shape
+    print("[bench] building inputs 10m_full", file=sys.stderr, flush=True)
+    inp = make_10m_full(seed=args.seed, device=dev)
+    q, k, v = inp.q, inp.k, inp.v
+    T, hq, d = q.shape
+    hkv = k.shape[1]
     cu_host = inp.cu_seqlens
     cu_dev = cu_host.to(dev)
-    nbytes = moba.moba_workspace_bytes(cu_host, hq, 1, d, slices[0][0].dtype, inp.block,
-                                       inp.topk)
+    nbytes = moba.moba_workspace_bytes_min(cu_host, hq, hkv, d, q.dtype, inp.block, inp.topk)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
 
     def step():
-        for q, k, v, out in slices:
-            moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,
-                              cu_seqlens_dev=cu_dev)
+        moba.moba_forward(q, k, v, cu_host, inp.block, inp.topk, out=out, workspace=ws,
+                          cu_seqlens_dev=cu_dev)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    moba.moba_timing_enable(True)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -372,22 +368,38 @@ def bench_group_major(moba, torch, args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    stages = moba.moba_timing_read()
+    moba.moba_timing_enable(False)
     print("[bench] %d steps: %.3f ms/step" % (args.steps, ms), file=sys.stderr, flush=True)
-    work = work_counts(inp.seqlens, hq * groups, groups, d, inp.block, inp.topk, 2)
+    work = work_counts(inp.seqlens, hq, hkv, d, inp.block, inp.topk, 2)
     attn_flop = work["attn_selected_flop"] + work["attn_self_flop"]
+    # every stage runs once per kv group in a step: rates from the per-step totals
+    per_step = {name: (tot / args.steps, 1) for name, (tot, n) in stages.items() if n}
+    rep = stage_report(per_step, work, PEAK_BF16_TFLOPS)
+    for name, (tot, n) in stages.items():
+        if n and name in rep:
+            rep[name]["launches_per_step"] = n / args.steps
+    if "slab_copy" in rep:
+        # gather q, k, v of each kv group and scatter out: 2 x (q + k + v + out) bytes
+        sb = 2.0 * T * (2 * hq + 2 * hkv) * d * 2
+        gbs = sb / (rep["slab_copy"]["avg_ms"] * 1e-3) / 1e9
+        rep["slab_copy"].update(bound="hbm", bytes_per_step=sb, achieved_gbs=gbs,
+                                frac=gbs / PEAK_HBM_GBS)
     line = {
         "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) Q/K/V with planted needle blocks",
         "config": {"workload": CONFIG_NAMES["10m_full"], "seqlens": inp.seqlens, "tokens": T,
-                   "q_heads": hq * groups, "kv_heads": groups, "head_dim": d,
+                   "q_heads": hq, "kv_heads": hkv, "head_dim": d,
                    "block_size": inp.block, "topk": inp.topk, "parallelism": "single GPU",
-                   "layout": "kv-group-major, one call per kv group"},
+                   "layout": "packed [T, H, D]; kv groups one after another inside moba_forward",
+                   "workspace_gb": nbytes / 1e9},
         "roofline": None, "cpu_baseline": None,
         "effective_attn_tflops": attn_flop / (ms * 1e-3) / 1e12,
         "attn_mfma_frac_of_step": attn_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "gpu_memory_gb": torch.cuda.max_memory_allocated(dev) / 1e9,
+        "stages": rep,
     }
     print(json.dumps(line), flush=True)
 
@@ -504,7 +516,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="1m", choices=sorted(CONFIG_NAMES),
-                    help="10m_full: a full-width 10M-token layer held kv-group-major")
+                    help="10m_full: a full-width 10M-token layer (kv groups one after "
+                         "another inside moba_forward)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
@@ -530,7 +543,7 @@ def main():
     from synth_inputs import CONFIGS, make_config
 
     if args.config == "10m_full":
-        bench_group_major(moba, torch, args)
+        bench_10m_full(moba, torch, args)
         return
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")

@@ -24,7 +24,7 @@ MOBA_OK, MOBA_ERR_INVALID_ARG, MOBA_ERR_UNSUPPORTED, MOBA_ERR_WORKSPACE, MOBA_ER
 MOBA_DTYPE_F32, MOBA_DTYPE_BF16 = 0, 1
 _DTYPE_CODE = {torch.float32: MOBA_DTYPE_F32, torch.bfloat16: MOBA_DTYPE_BF16}
 STAGES = ("pool", "gate", "route", "attn_self", "attn_selected", "merge", "attn_dense", "decode",
-          "kbar_append", "backward")
+          "kbar_append", "backward", "slab_copy")
 
 
 class MobaError(RuntimeError):
@@ -56,6 +56,7 @@ def _load():
         "moba_abi_version": ([], i32),
         "moba_last_error": ([], ctypes.c_char_p),
         "moba_workspace_bytes": ([p, i32, shp, i32, i32], sz),
+        "moba_workspace_bytes_min": ([p, i32, shp, i32, i32], sz),
         "moba_forward": ([p, p, p, p, p, i32, shp, i32, i32, p, p, sz, p, p, p], ctypes.c_int),
         "moba_forward_noalloc": ([p, p, p, p, p, i32, shp, i32, i32, p, p, p, p], ctypes.c_int),
         "moba_dense_causal_forward": ([p, p, p, p, p, i32, shp, p, p, p], ctypes.c_int),
@@ -87,7 +88,8 @@ def _load():
 def exported_symbols():
     """Names the binding resolves in libmoba.so (loading fails if any is missing)."""
     _load()
-    return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes", "moba_forward",
+    return ["moba_abi_version", "moba_last_error", "moba_workspace_bytes",
+            "moba_workspace_bytes_min", "moba_forward",
             "moba_forward_noalloc", "moba_dense_causal_forward", "moba_attention_forward",
             "moba_block_pool", "moba_kbar_append", "moba_decode_workspace_bytes", "moba_decode_forward",
             "moba_backward_workspace_bytes", "moba_backward", "moba_route_sizes", "moba_route",
@@ -204,17 +206,33 @@ def _check_workspace(ws, ref, nbytes):
         raise ValueError("workspace holds %d bytes, needs %d" % (ws.numel(), nbytes))
 
 
+def moba_workspace_bytes_min(cu_seqlens, num_q_heads, num_kv_heads, head_dim, dtype,
+                             block_size, topk) -> int:
+    """Smallest workspace moba_forward accepts (the kv-group mode's, when smaller)."""
+    host = torch.as_tensor(cu_seqlens, dtype=torch.int32).contiguous()
+    shape = _shape(num_q_heads, num_kv_heads, head_dim, dtype)
+    n = _load().moba_workspace_bytes_min(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                         int(block_size), int(topk))
+    if n == 0 and moba_last_error():
+        raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
+    return int(n)
+
+
 def _workspace(nbytes, device):
     # 256-byte aligned device buffer (the caching allocator returns 512-byte aligned blocks)
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def moba_forward(q, k, v, cu_seqlens, block_size, topk, *, out=None, workspace=None,
-                 return_sel=False, return_lse=False, softmax_scale=0.0, cu_seqlens_dev=None):
+                 return_sel=False, return_lse=False, softmax_scale=0.0, cu_seqlens_dev=None,
+                 by_kv_group=False):
     """MoBA causal prefill forward: q [T,Hq,D], k/v [T,Hkv,D] (bf16 or fp32, on the GPU).
 
     Returns out [T,Hq,D]; with return_sel / return_lse also the selected blocks
-    [T,Hq,topk-1] (int32) and the log-sum-exp [T,Hq] (fp32).
+    [T,Hq,topk-1] (int32) and the log-sum-exp [T,Hq] (fp32). A workspace smaller
+    than moba_workspace_bytes (at least moba_workspace_bytes_min) runs the kv groups
+    one after another; by_kv_group=True allocates that smaller workspace (it is also
+    used when one pass over all heads is beyond the library's limits).
     """
     _check_qkv(q, k, v)
     dev = q.device
@@ -225,13 +243,15 @@ def moba_forward(q, k, v, cu_seqlens, block_size, topk, *, out=None, workspace=N
     _check_like("out", out, q)
     shape = _shape(hq, hkv, d, q.dtype, softmax_scale)
     lib = _load()
-    nbytes = lib.moba_workspace_bytes(_ptr(host), host.numel() - 1, ctypes.byref(shape),
-                                      int(block_size), int(topk))
-    if nbytes == 0 and moba_last_error():
+    nmin = lib.moba_workspace_bytes_min(_ptr(host), host.numel() - 1, ctypes.byref(shape),
+                                        int(block_size), int(topk))
+    if nmin == 0 and moba_last_error():
         raise MobaError(MOBA_ERR_INVALID_ARG, moba_last_error())
-    _check_workspace(workspace, q, nbytes)
+    _check_workspace(workspace, q, nmin)
     if workspace is None:
-        workspace = _workspace(nbytes, dev)
+        nbytes = 0 if by_kv_group else lib.moba_workspace_bytes(
+            _ptr(host), host.numel() - 1, ctypes.byref(shape), int(block_size), int(topk))
+        workspace = _workspace(nbytes if nbytes else nmin, dev)
     if out is None:
         out = torch.empty_like(q)
     sel = torch.empty(T, hq, max(topk - 1, 0), dtype=torch.int32, device=dev) \

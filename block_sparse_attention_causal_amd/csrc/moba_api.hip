@@ -203,11 +203,11 @@ Work carve(const Plan& p, void* base) {
 // ---------------------------------------------------------------------------
 // Optional per-stage timing.
 enum { ST_POOL = 0, ST_GATE, ST_ROUTE, ST_SELF, ST_SELECTED, ST_MERGE, ST_DENSE, ST_DECODE,
-       ST_KBAR, ST_BACKWARD, ST_COUNT };
+       ST_KBAR, ST_BACKWARD, ST_SLAB, ST_COUNT };
 static const char* kStageNames[ST_COUNT] = {"pool",       "gate",   "route",
                                             "attn_self",  "attn_selected", "merge",
                                             "attn_dense", "decode", "kbar_append",
-                                            "backward"};
+                                            "backward",   "slab_copy"};
 constexpr int kMaxTimed = 4096;
 
 struct Timing {
@@ -386,6 +386,90 @@ static moba_status_t forward_enqueue(const Plan& p, const void* q, const void* k
 }
 
 // ---------------------------------------------------------------------------
+// kv-group mode of the forward: one kv group (its G q heads and its k/v head) at a
+// time. Every step of the method is independent per kv group (a row reads only
+// its own kv head), so running the groups one after another computes the same
+// rows; the group's heads are gathered into contiguous slabs, the usual stages
+// run on a [T, G, D] / [T, 1, D] batch, and the slab's outputs are scattered
+// back. The workspace then holds one group's buffers plus the slabs.
+struct SlabLayout {
+  Plan p;                       // the plan of one group's batch (G q heads, 1 kv head)
+  size_t off_q = 0, off_k = 0, off_v = 0, off_out = 0, off_sel = 0, off_lse = 0, off_ws = 0;
+  size_t total = 0;
+};
+
+static moba_status_t make_slab(const int32_t* cu, int32_t nseq, const moba_shape_t* shape,
+                               int32_t block, int32_t topk, SlabLayout* L) {
+  moba_shape_t one = *shape;
+  one.num_q_heads = shape->num_q_heads / shape->num_kv_heads;
+  one.num_kv_heads = 1;
+  moba_status_t st = make_plan(cu, nseq, &one, block, topk, true, &L->p, nullptr, 0);
+  if (st != MOBA_OK) return st;
+  const Plan& p = L->p;
+  const size_t e = p.dtype == MOBA_DTYPE_BF16 ? 2 : 4;
+  const size_t T = (size_t)p.T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L->off_q = take(T * p.hq * p.d * e);
+  L->off_k = take(T * p.d * e);
+  L->off_v = take(T * p.d * e);
+  L->off_out = take(T * p.hq * p.d * e);
+  L->off_sel = take(T * p.hq * (size_t)p.ks * 4);
+  L->off_lse = take(T * p.hq * 4);
+  L->off_ws = take(p.total);
+  L->total = off;
+  return MOBA_OK;
+}
+
+// The kv groups one after another: gather, forward, scatter (all on stream s).
+static moba_status_t forward_by_group(const SlabLayout& L, const moba_shape_t* shape,
+                                      const void* q, const void* k, const void* v,
+                                      const int32_t* cu_dev, void* out, void* workspace,
+                                      int32_t* sel_out, float* lse_out, hipStream_t s) {
+  const Plan& p = L.p;
+  const int G = p.hq, hkv = shape->num_kv_heads, hq = shape->num_q_heads;
+  const int64_t e = p.dtype == MOBA_DTYPE_BF16 ? 2 : 4;
+  const int64_t T = p.T, D = p.d;
+  char* b = (char*)workspace;
+  char *qs = b + L.off_q, *ks = b + L.off_k, *vs = b + L.off_v, *os = b + L.off_out;
+  int32_t* sels = (int32_t*)(b + L.off_sel);
+  float* lses = (float*)(b + L.off_lse);
+  for (int g = 0; g < hkv; ++g) {
+    hipError_t e1;
+    {
+      StageScope t(ST_SLAB, s);
+      e1 = launch_copy_rows((const char*)q + g * G * D * e, hq * D * e, qs, G * D * e, T, G * D * e, s);
+      if (e1 == hipSuccess)
+        e1 = launch_copy_rows((const char*)k + g * D * e, hkv * D * e, ks, D * e, T, D * e, s);
+      if (e1 == hipSuccess)
+        e1 = launch_copy_rows((const char*)v + g * D * e, hkv * D * e, vs, D * e, T, D * e, s);
+    }
+    if (e1 != hipSuccess) return hip_status(e1, "kv-group gather");
+    moba_status_t st = forward_enqueue(p, qs, ks, vs, cu_dev, os, b + L.off_ws,
+                                       (sel_out && p.ks > 0) ? sels : nullptr,
+                                       lse_out ? lses : nullptr, s);
+    if (st != MOBA_OK) return st;
+    {
+      StageScope t(ST_SLAB, s);
+      e1 = launch_copy_rows(os, G * D * e, (char*)out + g * G * D * e, hq * D * e, T, G * D * e, s);
+      if (e1 == hipSuccess && sel_out && p.ks > 0)
+        e1 = launch_copy_rows(sels, (int64_t)G * p.ks * 4, sel_out + (int64_t)g * G * p.ks,
+                              (int64_t)hq * p.ks * 4, T, (int64_t)G * p.ks * 4, s);
+      if (e1 == hipSuccess && lse_out)
+        e1 = launch_copy_rows(lses, (int64_t)G * 4, lse_out + (int64_t)g * G, (int64_t)hq * 4,
+                              T, (int64_t)G * 4, s);
+    }
+    if (e1 != hipSuccess) return hip_status(e1, "kv-group scatter");
+  }
+  g_err[0] = 0;
+  return MOBA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Static scratch for moba_forward_noalloc: a device array in this code object,
 // one copy per GPU, alive until the process ends. Host code never passes the
 // array's name to a kernel (on the host it is only a stand-in for the symbol):
@@ -438,6 +522,28 @@ size_t moba_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
   return p.total;
 }
 
+size_t moba_workspace_bytes_min(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                const moba_shape_t* shape, int32_t block_size, int32_t topk) {
+  Plan p;
+  const moba_status_t st =
+      make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
+  char msg[sizeof g_err];
+  snprintf(msg, sizeof msg, "%s", g_err);
+  size_t best = st == MOBA_OK ? p.total : 0;
+  if (shape && shape->num_kv_heads > 1 && (st == MOBA_OK || st == MOBA_ERR_UNSUPPORTED)) {
+    SlabLayout L;
+    if (make_slab(cu_seqlens_host, num_seqs, shape, block_size, topk, &L) == MOBA_OK &&
+        (best == 0 || L.total < best))
+      best = L.total;
+  }
+  if (best == 0) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return 0;
+  }
+  g_err[0] = 0;
+  return best;
+}
+
 moba_status_t moba_forward(const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                            int32_t num_seqs, const moba_shape_t* shape, int32_t block_size,
@@ -446,8 +552,11 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
   Plan p;
   moba_status_t st =
       make_plan(cu_seqlens_host, num_seqs, shape, block_size, topk, true, &p, nullptr, 0);
-  if (st != MOBA_OK) return st;
-  if (p.T == 0) {
+  // a batch over the size limits of one pass over all heads may still run by kv group
+  const bool by_group_possible =
+      (st == MOBA_OK || st == MOBA_ERR_UNSUPPORTED) && shape && shape->num_kv_heads > 1;
+  if (st != MOBA_OK && !by_group_possible) return st;
+  if (st == MOBA_OK && p.T == 0) {
     g_err[0] = 0;
     return MOBA_OK;
   }
@@ -455,11 +564,32 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
     return fail(MOBA_ERR_INVALID_ARG, "q, k, v, out and cu_seqlens_dev must be non-NULL");
   if (!workspace) return fail(MOBA_ERR_INVALID_ARG, "workspace is NULL");
   if ((uintptr_t)workspace % 256) return fail(MOBA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  if (workspace_bytes < p.total)
-    return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                p.total);
-  return forward_enqueue(p, q, k, v, cu_seqlens_dev, out, workspace, sel_out, lse_out,
-                         (hipStream_t)stream);
+  if (st == MOBA_OK && workspace_bytes >= p.total)
+    return forward_enqueue(p, q, k, v, cu_seqlens_dev, out, workspace, sel_out, lse_out,
+                           (hipStream_t)stream);
+  char msg[sizeof g_err];
+  snprintf(msg, sizeof msg, "%s", g_err);
+  const moba_status_t full_st = st;
+  const size_t full_total = st == MOBA_OK ? p.total : 0;
+  if (by_group_possible) {
+    SlabLayout L;
+    if (make_slab(cu_seqlens_host, num_seqs, shape, block_size, topk, &L) == MOBA_OK) {
+      if (workspace_bytes >= L.total)
+        return forward_by_group(L, shape, q, k, v, cu_seqlens_dev, out, workspace, sel_out,
+                                lse_out, (hipStream_t)stream);
+      if (full_st == MOBA_OK)
+        return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu (all heads at once) "
+                    "or %zu (one kv group at a time)", workspace_bytes, full_total, L.total);
+      return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu (one kv group at a "
+                  "time)", workspace_bytes, L.total);
+    }
+  }
+  if (full_st != MOBA_OK) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return full_st;
+  }
+  return fail(MOBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+              full_total);
 }
 
 moba_status_t moba_forward_noalloc(const void* q, const void* k, const void* v,

@@ -148,6 +148,10 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
 hipError_t launch_attn_dense(const Plan& p, const void* q, const void* k, const void* v,
                              const int32_t* cu_dev, void* out, float* lse_out, hipStream_t s);
 
+// Copies `rows` rows of `width` bytes (a multiple of 4) between two strided layouts.
+hipError_t launch_copy_rows(const void* src, int64_t sstride, void* dst, int64_t dstride,
+                            int64_t rows, int64_t width, hipStream_t s);
+
 // ---- backward (NEXT-1) --------------------------------------------------------
 hipError_t launch_backward(const Plan& p, const void* q, const void* k, const void* v,
                            const void* out, const float* lse, const void* dout,

@@ -94,6 +94,14 @@ const char* moba_last_error(void);
 size_t moba_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
                             const moba_shape_t* shape, int32_t block_size, int32_t topk);
 
+/* Smallest workspace moba_forward accepts for this batch. With more than one kv
+ * head this is the workspace of the kv-group mode (see moba_forward), if it is
+ * smaller than moba_workspace_bytes(); a batch beyond the int32 and grid limits of
+ * one pass over all heads (where moba_workspace_bytes() returns 0) may still run
+ * in that mode. Host-only; 0 and the last error if neither mode can run it. */
+size_t moba_workspace_bytes_min(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                const moba_shape_t* shape, int32_t block_size, int32_t topk);
+
 /* MoBA causal prefill forward (see the top of this file for what it computes).
  *   out:     [T, Hq, D] in the input dtype, written in full.
  *   topk:    >= 1; counts the row's own block, so topk-1 past blocks are kept
@@ -104,7 +112,16 @@ size_t moba_workspace_bytes(const int32_t* cu_seqlens_host, int32_t num_seqs,
  *            order, padded with -1. Ignored when topk == 1.
  *   lse_out: optional (NULL to skip), fp32 [T, Hq]: natural-log log-sum-exp of
  *            the scaled logits over each row's attended keys.
- *   workspace: at least moba_workspace_bytes(...) bytes, 256-byte aligned.
+ *   workspace: 256-byte aligned. With at least moba_workspace_bytes(...) bytes
+ *            every head runs in one pass. With less, but at least
+ *            moba_workspace_bytes_min(...) (num_kv_heads > 1), the kv groups run
+ *            one after another: each group's G = Hq/Hkv q heads and its kv head
+ *            are copied into contiguous slabs inside the workspace, the same
+ *            stages run on them, and out / sel_out / lse_out are copied back.
+ *            Every step of the method reads only a row's own kv head, so the
+ *            result is the same (bitwise); the copies cost extra HBM traffic of
+ *            about twice q, k, v and out. The int32 limits below then apply to
+ *            one group (T * G * (topk-1) < 2^31), so longer batches fit.
  */
 moba_status_t moba_forward(const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -129,7 +146,8 @@ moba_status_t moba_forward(const void* q, const void* k, const void* v,
  *          contents behind; no call relies on them (each call writes every
  *          scratch word it reads). Calls whose work overlaps on one GPU (other
  *          streams, or other threads) race on the array: serialise them.
- *   Arguments, layouts, outputs and errors otherwise as moba_forward. */
+ *   Arguments, layouts, outputs and errors otherwise as moba_forward (all heads
+ *   in one pass; the kv-group mode needs a caller workspace). */
 #define MOBA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
 moba_status_t moba_forward_noalloc(const void* q, const void* k, const void* v,
                                    const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -294,7 +312,7 @@ moba_status_t moba_route(const int32_t* sel_dev, const int32_t* cu_seqlens_dev,
  * always 0 launches; the id is kept so that the others stay fixed), 6 dense
  * causal attention, 7 decode (gate, parts and merge of moba_decode_forward),
  * 8 pooled-key append, 9 backward (Delta, dq and dk/dv passes; its routing is
- * timed as stage 2). Returns the number of stages
+ * timed as stage 2), 10 the kv-group mode's slab copies. Returns the number of stages
  * written. At most 4096 event pairs are kept; later ones are not recorded. */
 moba_status_t moba_timing_enable(int32_t enable);
 int32_t moba_timing_read(double* stage_ms, int32_t* stage_launches, int32_t max_stages);

@@ -190,6 +190,31 @@ def make_config(name: str, seed=0, device="cpu", **over) -> Inputs:
                        **{k: v for k, v in over.items() if k in ("plant", "alpha", "beta")})
 
 
+def make_10m_full(seed=0, device="cpu", groups=8) -> Inputs:
+    """A full-width 10M-token layer: the 10m_shard recipe for each of `groups` kv
+    groups (seed + g for group g; 4 q heads and 1 kv head each), laid out as one
+    [T, 4 * groups, D] / [T, groups, D] batch. Group g holds q heads 4g .. 4g+3 and
+    kv head g, exactly the g-th head share of the layer."""
+    base = CONFIGS["10m_shard"]
+    T, d, G = sum(base["seqlens"]), base["d"], base["hq"]
+    tdt = DTYPES[base["dtype"]]
+    dev = torch.device(device)
+    q = torch.empty(T, G * groups, d, dtype=tdt, device=dev)
+    k = torch.empty(T, groups, d, dtype=tdt, device=dev)
+    v = torch.empty(T, groups, d, dtype=tdt, device=dev)
+    targets = torch.empty(T, G * groups, base["topk"] - 1, dtype=torch.int32)
+    for g in range(groups):
+        part = make_config("10m_shard", seed=seed + g, device=device)
+        q[:, G * g:G * (g + 1)] = part.q
+        k[:, g] = part.k[:, 0]
+        v[:, g] = part.v[:, 0]
+        targets[:, G * g:G * (g + 1)] = part.targets
+        del part
+    meta = dict(seed=seed, groups=groups, recipe="10m_shard per kv group")
+    return Inputs(q=q, k=k, v=v, cu_seqlens=cu_seqlens_of(base["seqlens"]), block=base["block"],
+                  topk=base["topk"], targets=targets, meta=meta)
+
+
 def sample_tokens(seqlens, block: int, n_tokens: int, seed: int = 0,
                   every_block: bool = False) -> np.ndarray:
     """Seeded sample of packed token indices for sampled-row checks.

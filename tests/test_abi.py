@@ -387,3 +387,30 @@ def test_binding_argument_checks():
         moba._check_workspace(torch.zeros(999, dtype=torch.uint8), q, 1000)
     with pytest.raises(ValueError, match="workspace"):
         moba._check_workspace(torch.zeros(1000, dtype=torch.float32), q, 1000)
+
+
+def test_workspace_bytes_min_runs_by_kv_group():
+    """The smallest workspace moba_forward takes: one kv group's buffers plus the
+    slabs, when that is smaller than one pass over all heads; a batch beyond the
+    one-pass int32 limits (8M tokens x 32 heads with top-12: T Hq (topk-1) >= 2^31)
+    still has one."""
+    bf = torch.bfloat16
+    full = moba.moba_workspace_bytes([0, 32768], 32, 8, 128, bf, 2048, 3)
+    small = moba.moba_workspace_bytes_min([0, 32768], 32, 8, 128, bf, 2048, 3)
+    assert small < full / 2
+    # one kv head: nothing to split
+    assert moba.moba_workspace_bytes_min([0, 32768], 4, 1, 128, bf, 2048, 3) == \
+        moba.moba_workspace_bytes([0, 32768], 4, 1, 128, bf, 2048, 3)
+    # own block only: no selected parts, one pass is the smaller
+    assert moba.moba_workspace_bytes_min([0, 32768], 32, 8, 128, bf, 2048, 1) == \
+        moba.moba_workspace_bytes([0, 32768], 32, 8, 128, bf, 2048, 1)
+    T = 8 * 2 ** 20
+    with pytest.raises(moba.MobaError):
+        moba.moba_workspace_bytes([0, T], 32, 8, 128, bf, 512, 12)
+    assert moba.moba_workspace_bytes_min([0, T], 32, 8, 128, bf, 512, 12) > 0
+    # below the minimum: refused, both sizes named
+    lib = moba._load()
+    cu = _cu([32768])
+    st = _fwd(lib, cu, _shape(), 2048, 3, ws_bytes=small - 1)
+    assert st == moba.MOBA_ERR_WORKSPACE
+    assert "kv group" in lib.moba_last_error().decode()

@@ -17,7 +17,7 @@ import torch
 
 import block_sparse_attention_causal_amd as moba
 import oracle
-from synth_inputs import CONFIGS, make_config, make_inputs, sample_tokens
+from synth_inputs import CONFIGS, make_10m_full, make_config, make_inputs, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -421,6 +421,30 @@ def test_large_values_within_the_fp16_part_range():
     assert err <= 2.0 ** -8 * 60000.0, err
 
 
+@pytest.mark.parametrize("case", [
+    # shapes whose kv-group workspace is the smaller (many selected parts per row)
+    ("bf16-gqa2-varlen-k6", [1000, 64, 0, 2300, 129], 8, 4, 128, 128, 6, "bf16"),
+    ("f32-gqa2-d64-k5", [700, 450], 4, 2, 64, 64, 5, "f32"),
+    ("bf16-gqa3-k6", [1500, 97], 6, 2, 128, 128, 6, "bf16"),
+], ids=lambda c: c[0])
+def test_kv_group_mode_equals_one_pass(case):
+    """A workspace below moba_workspace_bytes runs the kv groups one after another
+    (slabs gathered, the same stages, outputs scattered back): the same rows, so
+    out, sel and lse are bitwise those of one pass over all heads."""
+    name, seqlens, hq, hkv, d, block, topk, dt = case
+    _say("kv-group mode %s" % name)
+    inp = _to_gpu(make_inputs(seqlens, hq, hkv, d, block, topk, dtype=dt, seed=23))
+    full = moba.moba_workspace_bytes(inp.cu_seqlens, hq, hkv, d, inp.q.dtype, block, topk)
+    small = moba.moba_workspace_bytes_min(inp.cu_seqlens, hq, hkv, d, inp.q.dtype, block, topk)
+    assert small < full
+    a = _run(inp)
+    ws = torch.empty(small, dtype=torch.uint8, device="cuda")
+    b = _run(inp, workspace=ws)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    _check_all_rows(inp, b[0], b[1], b[2], TOL[inp.q.dtype])
+
+
 # --- full-size workloads, benchmark launch configuration, sampled rows --------
 
 FULL = ["llama32k", "varlen131k", "fine256k", "1m", "10m_shard"]
@@ -463,3 +487,53 @@ def test_dense_full_32k_sampled_rows():
     got = out[torch.as_tensor(tt, device="cuda"), torch.as_tensor(hh, device="cuda")]
     err = np.abs(got.float().cpu().numpy() - ref["out"]).max()
     assert err <= 2e-2, err
+
+
+def test_full_width_10m_by_kv_group():
+    """A full-width 10M-token layer (32 q heads, 8 kv heads, 5,120 blocks) through
+    moba_forward itself: one pass over all heads would need more than the GPU's
+    memory, so the forward runs kv group by kv group inside the library. Every
+    row's selection equals the planted targets; sampled rows (one token of every
+    block and more, all 32 heads) match the oracle, evaluated per kv group on that
+    group's keys."""
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    _say("full-width 10M layer, kv-group mode")
+    inp = make_10m_full(seed=0, device="cuda")
+    T, hq, d = inp.q.shape
+    hkv = inp.k.shape[1]
+    G = hq // hkv
+    full = moba.moba_workspace_bytes_min(inp.cu_seqlens, hq, hkv, d, inp.q.dtype, inp.block,
+                                         inp.topk)
+    print("workspace (kv-group mode): %.1f GB" % (full / 1e9), flush=True)
+    out, sel, lse = moba.moba_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, inp.block, inp.topk,
+                                      return_sel=True, return_lse=True, by_kv_group=True)
+    torch.cuda.synchronize()
+    sel_h = sel.cpu()
+    assert torch.equal(sel_h, inp.targets), "selection differs from planted targets"
+    toks = sample_tokens(inp.seqlens, inp.block, 4096, seed=1, every_block=True)
+    tt_dev = torch.as_tensor(toks, dtype=torch.long, device="cuda")
+    worst = 0.0
+    for g in range(hkv):
+        kf = oracle._f32(inp.k[:, g:g + 1])
+        vf = oracle._f32(inp.v[:, g:g + 1])
+        qg = inp.q[:, G * g:G * (g + 1)]
+        tt, hh = np.repeat(toks, G), np.tile(np.arange(G), len(toks))
+        qr = oracle._f32(qg[tt_dev][:, :, :].reshape(-1, d))
+        ref = oracle.rows(qr, kf, vf, inp.cu_seqlens, inp.block, inp.topk, tt, hh,
+                          num_q_heads=G)
+        m = ref["margin"]
+        assert np.all(m[np.isfinite(m)] >= 0.5)
+        np.testing.assert_array_equal(sel_h.numpy()[tt, G * g + hh], ref["sel"])
+        got = out[tt_dev][:, G * g:G * (g + 1)].float().cpu().numpy().reshape(-1, d)
+        err = np.abs(got - ref["out"]).max()
+        worst = max(worst, err)
+        assert err <= 2e-2, (g, err)
+        lg = lse[tt_dev][:, G * g:G * (g + 1)].cpu().numpy().reshape(-1)
+        assert np.abs(lg - ref["lse"]).max() <= 1e-3
+        del kf, vf
+        print("kv group %d: %d rows, max-abs error %.3g" % (g, len(tt), err), flush=True)
+    del inp, out, sel, lse
+    gc.collect()
+    torch.cuda.empty_cache()
