@@ -471,6 +471,61 @@ def time_forward(moba, torch, inp, cu_dev, steps, warmup, timing=True):
     return {"ms": ms, "work": work, "stages": stage_report(stages, work, peak)}
 
 
+def bench_small_shapes(moba, torch, seed):
+    """Short prefills (4K and 8K tokens, the Llama-3.1-8B-shaped layer), where the
+    pages report MoBA slower than FlashAttention because of gating and routing,
+    and the README's own comparison shape (32K tokens, 1 head, block 2048,
+    top-3): MoBA forward and dense causal attention from the same library, each
+    the median of 20 timed calls after 5 warm-ups, with MoBA's per-stage times."""
+    from synth_inputs import make_inputs
+    dev = torch.device("cuda:0")
+    res = {}
+    shapes = (("prefill_4k", [4096], 32, 8), ("prefill_8k", [8192], 32, 8),
+              ("readme_32k_1head", [32768], 1, 1))
+    for name, seqlens, hq, hkv in shapes:
+        inp = make_inputs(seqlens, hq, hkv, 128, 2048, 3, dtype="bf16", seed=seed, device=dev)
+        cu_dev = inp.cu_seqlens.to(dev)
+        nbytes = moba.moba_workspace_bytes(inp.cu_seqlens, hq, hkv, 128, inp.q.dtype, 2048, 3)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        out = torch.empty_like(inp.q)
+
+        def mo():
+            moba.moba_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, 2048, 3, out=out,
+                              workspace=ws, cu_seqlens_dev=cu_dev)
+
+        def de():
+            moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, out=out,
+                                           cu_seqlens_dev=cu_dev)
+
+        def median_ms(fn, timing=False):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            if timing:
+                moba.moba_timing_enable(True)
+            times = []
+            for _ in range(20):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            st = moba.moba_timing_read() if timing else {}
+            moba.moba_timing_enable(False)
+            times.sort()
+            return times[len(times) // 2], st
+
+        mms, st = median_ms(mo, timing=True)
+        dms, _ = median_ms(de)
+        res[name] = {"tokens": sum(seqlens), "q_heads": hq, "kv_heads": hkv, "moba_ms": mms,
+                     "dense_causal_ms": dms, "speedup_vs_dense": dms / mms,
+                     "stages_ms": {k: t / n for k, (t, n) in st.items() if n}}
+        del inp, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_second_workload(moba, torch, name, steps, warmup, seed, dense_steps):
     """The metric's second point (S = 128K: the packed varlen batch of 134,144
     tokens), timed like the headline workload in the same run: tokens/s, every
@@ -631,6 +686,12 @@ def main():
         backward = bench_backward(moba, torch, inp, cu_dev, attn_flop, peak_mfma,
                                   steps=max(1, min(args.steps, 5)))
 
+    small = None
+    if not args.no_second and args.config == "1m":
+        print("[bench] short prefills and the README's comparison shape", file=sys.stderr,
+              flush=True)
+        small = bench_small_shapes(moba, torch, args.seed)
+
     second = None
     if not args.no_second and args.config == "1m":
         second = bench_second_workload(moba, torch, "varlen131k", steps=max(args.steps, 10),
@@ -670,6 +731,7 @@ def main():
         "backward": backward,
         "stages": stage_rep,
         "workload_128k": second,
+        "small_shapes": small,
     }
     print(json.dumps(line), flush=True)
 

@@ -51,6 +51,7 @@ KERNELS = {
     "route_offsets": r"k_route_offsets",
     "route_scatter": r"k_route_scatter",
     "setup": r"k_setup|k_block_info",
+    "slab_copy": r"k_copy_rows",
     "copy_calibration": r"neg_kernel",
 }
 
