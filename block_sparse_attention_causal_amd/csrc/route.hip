@@ -12,8 +12,10 @@
 //               i > j that can feed it -> each chunk's start inside the list,
 //               and the list size;
 //   3. offsets: one exclusive scan over list sizes (and over tiles of 256 rows);
-//   4. scatter: per chunk, one wave walks its entries in row order and ranks
-//               equal block ids with ballots, so rows ascend inside every list.
+//   4. scatter: per chunk, a few waves each take a slice of its entries in row
+//               order, count them per block, take their first places from a
+//               prefix over the waves, and rank equal block ids with ballots, so
+//               rows ascend inside every list.
 // The result is identical on every run.
 #include "moba_plan.h"
 
@@ -138,8 +140,13 @@ __global__ void __launch_bounds__(1024) k_route_offsets(const int32_t* __restric
   }
 }
 
-// One wave per chunk (query block i, kv-head g).
-__global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict__ sel,
+// One workgroup of W waves per chunk (query block i, kv-head g). The chunk's
+// entries (in row order) are cut into W consecutive slices, one per wave. Each
+// wave counts its slice's entries per block into LDS, a prefix over the waves
+// gives every wave its first place in each block's segment of the list, and each
+// wave then walks its slice 64 entries at a time, ranking equal block ids with
+// ballots: rows ascend within every list, as with one wave walking the chunk.
+__global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict__ sel,
                                                       const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ blk_base,
                                                       const int32_t* __restrict__ tri_base,
@@ -149,20 +156,17 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
                                                       const int32_t* __restrict__ list_offsets,
                                                       int hq, int hkv, int block, int ks,
                                                       int32_t* __restrict__ entries) {
-  extern __shared__ int32_t next[];
+  extern __shared__ int32_t next[];                // [W][i]: per wave, per block
   const int64_t c = blockIdx.x;
   const int64_t b = c / hkv;
   const int g = (int)(c % hkv);
   const int n = blk_seq[b], i = blk_local[b];
   if (i == 0) return;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int group = hq / hkv;
   const int nbn = blk_base[n + 1] - blk_base[n];
   const int64_t gb0 = blk_base[n];
   const int64_t tri0 = tri_index(tri_base, n, nbn, g, i, 0);
-  for (int j = lane; j < i; j += 64)
-    next[j] = list_offsets[(gb0 + j) * hkv + g] + chunk_off[tri0 + j];
-  __syncthreads();
   const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
   const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
   const int per_tok = group * ks;
@@ -170,24 +174,47 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
   const int nbits = (i <= 1) ? 0 : 32 - __clz(i - 1);
   const int nvalid = min(ks, i);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // entry e of the chunk: its row, slot and block id (-1 past the end)
+  // the wave's slice [e_lo, e_hi) of the chunk's entries, whole steps of 64
+  const int slice = (total + 64 * W - 1) / (64 * W) * 64;
+  const int e_lo = min(total, w * slice), e_hi = min(total, e_lo + slice);
+  // entry e of the chunk: its row, slot and block id (-1 outside the slice)
   auto fetch = [&](int e, int64_t& row, int& slot) __attribute__((always_inline)) -> int {
     row = 0;
     slot = 0;
-    if (e >= total) return -1;
+    if (e >= e_hi) return -1;
     const int t = e / per_tok;
     const int r = e % per_tok;
     slot = r % ks;
     row = (s0 + t) * hq + (int64_t)g * group + r / ks;
     return sel[row * ks + slot];
   };
+  int32_t* mine = next + w * i;
+  for (int j = threadIdx.x; j < W * i; j += blockDim.x) next[j] = 0;
+  __syncthreads();
+  for (int e = e_lo + lane; e < e_hi; e += 64) {
+    int64_t row;
+    int slot;
+    const int j = fetch(e, row, slot);
+    if (j >= 0 && j < i && slot < nvalid) atomicAdd(&mine[j], 1);
+  }
+  __syncthreads();
+  // counts -> first places: the list's segment for this chunk, then wave by wave
+  for (int j = threadIdx.x; j < i; j += blockDim.x) {
+    int32_t at = list_offsets[(gb0 + j) * hkv + g] + chunk_off[tri0 + j];
+    for (int v = 0; v < W; ++v) {
+      const int32_t cnt = next[v * i + j];
+      next[v * i + j] = at;
+      at += cnt;
+    }
+  }
+  __syncthreads();
   int64_t row_n;
   int slot_n;
-  int j_n = fetch(lane, row_n, slot_n);
-  // The workgroup is one wave: its LDS accesses take effect in program order,
-  // so the counters need no barrier between steps (only the compiler must keep
-  // the order), and the next step's ids are loaded before this step ranks.
-  for (int e0 = 0; e0 < total; e0 += 64) {
+  int j_n = fetch(e_lo + lane, row_n, slot_n);
+  // A wave's own LDS accesses take effect in program order, so its counters need
+  // no barrier between steps (only the compiler must keep the order), and the
+  // next step's ids are loaded before this step ranks.
+  for (int e0 = e_lo; e0 < e_hi; e0 += 64) {
     const int j = j_n;
     const int64_t row = row_n;
     const int slot = slot_n;
@@ -201,9 +228,9 @@ __global__ void __launch_bounds__(64) k_route_scatter(const int32_t* __restrict_
     }
     if (act) {
       const int rank = __popcll(peers & below);
-      const int32_t base = next[j];
+      const int32_t base = mine[j];
       entries[base + rank] = (int32_t)(row * ks + slot);
-      if ((peers & below) == 0) next[j] = base + __popcll(peers);
+      if ((peers & below) == 0) mine[j] = base + __popcll(peers);
     }
     asm volatile("" ::: "memory");
   }
@@ -222,9 +249,13 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
                      w.chunk_off, w.list_count);
   hipLaunchKernelGGL(k_route_offsets, dim3(1), dim3(1024), 0, s, w.list_count, p.nlists,
                      rows_per_tile, list_offsets, w.tile_offsets);
-  hipLaunchKernelGGL(k_route_scatter, dim3(nchunks), dim3(64), lds, s, sel, cu_dev, w.blk_base,
-                     w.tri_base, w.blk_seq, w.blk_local, w.chunk_off, list_offsets, p.hq, p.hkv,
-                     p.block, p.ks, entries);
+  // as many waves per chunk as the per-wave counters fit in 64 KB of LDS (8 for
+  // sequences of up to 2048 blocks)
+  int waves = 8;
+  while (waves > 1 && (size_t)waves * p.max_nb * sizeof(int32_t) > 65536) waves >>= 1;
+  hipLaunchKernelGGL(k_route_scatter, dim3(nchunks), dim3(64 * waves), lds * waves, s, sel,
+                     cu_dev, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, w.chunk_off,
+                     list_offsets, p.hq, p.hkv, p.block, p.ks, entries);
   return hipGetLastError();
 }
 
