@@ -503,25 +503,29 @@ __global__ void __launch_bounds__(256) k_gate_bound(const int32_t* __restrict__ 
   if (threadIdx.x == 0) bound[blockIdx.x] = vmax(vmax(red[0], red[1]), vmax(red[2], red[3]));
 }
 
-template <int D, int KB, bool CHAIN>
-__global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
-                                                   const int32_t* __restrict__ cu,
-                                                   const int32_t* __restrict__ blk_base,
-                                                   const int32_t* __restrict__ blk_seq,
-                                                   const int32_t* __restrict__ blk_local,
-                                                   const bf16* __restrict__ khi,
-                                                   const float* __restrict__ bound, int64_t nb,
-                                                   int hq, int hkv, int hg, int block, int nu,
-                                                   int ks, int64_t ntiles, int64_t padded,
-                                                   uint8_t* __restrict__ flags,
-                                                   int32_t* __restrict__ sel) {
-  // Pooled hi keys stream through an LDS ring of GB buffers (32 blocks each,
-  // rows of D bf16 in 16-byte pieces, piece p of row r at p ^ swz(r) as in the
-  // attention kernels) by direct loads, GB - 1 chunks in flight: each thread
-  // issues exactly one 16-byte load per chunk (clamped past the end; with
-  // D = 64 the upper half of a buffer holds unused rows), so "chunk s+1 has
-  // landed" is vmcnt(GB - 2) at the end of iteration s.
+// (four waves per SIMD: two workgroups per CU, as the LDS ring allows)
+template <int D, int KB, bool CHAIN, int R>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
+k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
+            const int32_t* __restrict__ blk_base, const int32_t* __restrict__ blk_seq,
+            const int32_t* __restrict__ blk_local, const bf16* __restrict__ khi,
+            const float* __restrict__ bound, int64_t nb, int hq, int hkv, int hg, int block,
+            int nu, int nuf, int ks, int64_t ntiles, int64_t padded,
+            uint8_t* __restrict__ flags, int32_t* __restrict__ sel) {
+  // A workgroup covers R consecutive tiles of the exact gate (same block, same
+  // heads): each wave holds R row sets of 32, one per tile, and every key
+  // fragment read from LDS feeds R matrix products. Pooled hi keys stream
+  // through an LDS ring of GB buffers (32 blocks each, rows of D bf16 in
+  // 16-byte pieces, piece p of row r at p ^ swz(r) as in the attention kernels)
+  // by direct loads. The ring turns in groups of GRP chunks with one barrier per
+  // group (the waves' list upkeep differs from chunk to chunk; within a group
+  // they drift instead of meeting at every chunk): a trip issues the group
+  // GB / GRP - 1 ahead into the buffers the previous trip used, then works on
+  // its own group. Each thread issues exactly one 16-byte load per chunk
+  // (clamped past the end; with D = 64 the upper half of a buffer holds unused
+  // rows), so "the next group has landed" is vmcnt(GB - 2 GRP) at a trip's end.
   constexpr int GB = 8;
+  constexpr int GRP = 4;
   constexpr int KBUF = 512 * 8;                       // bf16 per buffer: 512 16-byte slots
   __shared__ __attribute__((aligned(16))) bf16 kb[GB][KBUF];
 
@@ -529,17 +533,19 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
   if (logical >= ntiles) return;
   const int tt = 32 * (8 / hg);
   const int nhs = hq / hg;
-  const int u = (int)(logical % nu);
-  const int64_t rest = logical / nu;
+  const int uf = (int)(logical % nuf);
+  const int64_t rest = logical / nuf;
   const int64_t b = nb - 1 - (rest % nb);
   const int hs = (int)(rest / nb);
   const int n = blk_seq[b];
   const int i = blk_local[b];
   const int64_t seq0 = cu[n];
   const int64_t blk_end = min(seq0 + (int64_t)(i + 1) * block, (int64_t)cu[n + 1]);
-  const int64_t tok0 = seq0 + (int64_t)i * block + (int64_t)u * tt;
+  // exact-gate tile R uf + r is set r; its flag sits at (R uf + r) + nu rest
+  const int64_t tok0 = seq0 + (int64_t)i * block + (int64_t)(R * uf) * tt;
   if (tok0 >= blk_end || hs >= nhs) {
-    if (threadIdx.x == 0) flags[logical] = 0;
+    if (threadIdx.x < R && R * uf + (int)threadIdx.x < nu)
+      flags[R * uf + threadIdx.x + nu * rest] = 0;
     return;
   }
 
@@ -547,23 +553,36 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
   const int half = lane >> 5, r32 = lane & 31;
   const int h = hs * hg + (w % hg);
   const int g = h / (hq / hkv);
-  const int64_t tok = tok0 + (int64_t)(w / hg) * 32 + r32;
-  const bool row_ok = tok < blk_end;
-  const int64_t row = tok * hq + h;
-
-  // the top-ks list as in k_gate, plus the best score left out of it
-  float bs[KB];
-  int bj[KB];
+  int64_t row[R];
+  bool row_ok[R];
 #pragma unroll
-  for (int p = 0; p < KB; ++p) { bs[p] = -INFINITY; bj[p] = kNoBlock; }
-  float out_max = -INFINITY;
-  bool unsure = false;
+  for (int r = 0; r < R; ++r) {
+    // a set past the block's end (or past the last tile) has no valid rows
+    const int64_t tok = tok0 + (int64_t)r * tt + (int64_t)(w / hg) * 32 + r32;
+    row_ok[r] = tok < blk_end;
+    row[r] = tok * hq + h;
+  }
+
+  // per set: the top-ks list as in k_gate, plus the best score left out of it
+  float bs[R][KB];
+  int bj[R][KB];
+  float out_max[R];
+  bool unsure[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int p = 0; p < KB; ++p) { bs[r][p] = -INFINITY; bj[r][p] = kNoBlock; }
+    out_max[r] = -INFINITY;
+    unsure[r] = false;
+  }
 
   if (i > 0) {
-    bf16x8 qf[D / 16];
+    bf16x8 qf[R][D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = row_ok ? load8(q + row * D + 16 * kk + 8 * half) : zero8<bf16x8>();
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qf[r][kk] = row_ok[r] ? load8(q + row[r] * D + 16 * kk + 8 * half) : zero8<bf16x8>();
     const int64_t gbase = blk_base[n];
     const int nsteps = (i + 31) / 32;
     const uint32_t kb_lds = lds_addr(&kb[0][0]);
@@ -585,20 +604,27 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
     // blocks >= i score -inf; in the packed chain the lowest finite value instead
     // (packing the low mantissa bits of an infinity would make a NaN)
     constexpr float kMasked = CHAIN ? -3.4028234663852886e38f : -INFINITY;
-    // S~^T of chunk st (the LDS buffer holds it), blocks >= i masked
-    auto scores = [&](int st, f32x16& acc) __attribute__((always_inline)) {
+    // S~^T of chunk st for every set (the LDS buffer holds it), blocks >= i masked
+    auto scores = [&](int st, f32x16 (&acc)[R]) __attribute__((always_inline)) {
       const bf16* kr = &kb[st % GB][r32 * D];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        acc = mma_k16(load8(kr + 8 * (((2 * kk) | half) ^ rx)), qf[kk], acc);
+        for (int e = 0; e < 16; ++e) acc[r][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = load8(kr + 8 * (((2 * kk) | half) ^ rx));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = mma_k16(a, qf[r][kk], acc[r]);
+      }
       const int j0 = st * 32;
       if (j0 + 32 > i) {
         const int lim = i - j0 - 4 * half;               // positions >= lim are past i
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (8 * (e >> 2) + (e & 3) >= lim) acc[e] = kMasked;
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (8 * (e >> 2) + (e & 3) >= lim) acc[r][e] = kMasked;
       }
     };
     auto max16 = [](const f32x16& acc) __attribute__((always_inline)) {
@@ -610,148 +636,175 @@ __global__ void __launch_bounds__(512) k_gate_fast(const bf16* __restrict__ q,
     };
     // Every score either enters the list (and whatever it evicts is left out)
     // or is left out at once, so out_max ends as the best score not kept.
-    float ws = -INFINITY;
-    float tl[KB];                          // the packed chain's sorted values
+    float ws[R];
+    float tl[R][KB];                       // the packed chain's sorted values
 #pragma unroll
-    for (int p = 0; p < KB; ++p) tl[p] = -INFINITY;
+    for (int r = 0; r < R; ++r) {
+      ws[r] = -INFINITY;
+#pragma unroll
+      for (int p = 0; p < KB; ++p) tl[r][p] = -INFINITY;
+    }
     MOBA_WAIT_VM_LGKM0(0);                 // Q before any direct load
-    for (int st = 0; st < GB - 1; ++st) issue(st);
-    MOBA_WAIT_VM_LGKM0(GB - 2);
+    for (int st = 0; st < GB - GRP; ++st) issue(st);
+    MOBA_WAIT_VM_LGKM0(GB - 2 * GRP);
     bare_barrier();
-    for (int st = 0; st < nsteps; ++st) {
-      issue(st + GB - 1);
-      f32x16 acc;
-      scores(st, acc);
-      if constexpr (CHAIN) {
-        // Few chunks (sequences of up to 512 blocks), where many scores still
-        // enter: every score passes through the lane's list without a branch.
-        // The score carries its place in the lane's stream in its 8 low
-        // mantissa bits (chunk st, position e: code 16 st + e, put in with one
-        // byte permute), so the list is a list of values and the block comes
-        // back from the bits at the end. With the values t sorted descending,
-        // admitting s gives t'_0 = max(t_0, s) and t'_p = med3(t_{p-1}, t_p, s);
-        // the value that falls off the end, min(t_last, s), is left out, and
-        // since nothing left out exceeds t_last the best of them updates as
-        // med3(out, t_last, s). Clearing 8 low bits moves a score by less than
-        // 2^-15 of itself; the screen below adds that to its error bound, so
-        // the selection it accepts is still the exact-score selection. Every
-        // packed value of a lane is distinct (distinct codes).
-        const uint32_t cbase = 16u * (uint32_t)st;
+    for (int st0 = 0; st0 < nsteps; st0 += GRP) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float sc = __uint_as_float(__builtin_amdgcn_perm(
-              cbase + (uint32_t)e, __float_as_uint(acc[e]), 0x03020104u));
-          out_max = __builtin_amdgcn_fmed3f(out_max, tl[KB - 1], sc);
+      for (int x = 0; x < GRP; ++x) issue(st0 + GB - GRP + x);
 #pragma unroll
-          for (int p = KB - 1; p > 0; --p) tl[p] = __builtin_amdgcn_fmed3f(tl[p - 1], tl[p], sc);
-          tl[0] = vmax(tl[0], sc);
+      for (int x = 0; x < GRP; ++x) {
+        const int st = st0 + x;
+        if (GRP > 1 && st >= nsteps) break;
+        f32x16 acc[R];
+        scores(st, acc);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if constexpr (CHAIN) {
+            // Few chunks (sequences of up to 512 blocks), where many scores still
+            // enter: every score passes through the lane's list without a branch.
+            // The score carries its place in the lane's stream in its 8 low
+            // mantissa bits (chunk st, position e: code 16 st + e, put in with one
+            // byte permute), so the list is a list of values and the block comes
+            // back from the bits at the end. With the values t sorted descending,
+            // admitting s gives t'_0 = max(t_0, s) and t'_p = med3(t_{p-1}, t_p, s);
+            // the value that falls off the end, min(t_last, s), is left out, and
+            // since nothing left out exceeds t_last the best of them updates as
+            // med3(out, t_last, s). Clearing 8 low bits moves a score by less than
+            // 2^-15 of itself; the screen below adds that to its error bound, so
+            // the selection it accepts is still the exact-score selection. Every
+            // packed value of a lane is distinct (distinct codes).
+            const uint32_t cbase = 16u * (uint32_t)st;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float sc = __uint_as_float(__builtin_amdgcn_perm(
+                  cbase + (uint32_t)e, __float_as_uint(acc[r][e]), 0x03020104u));
+              out_max[r] = __builtin_amdgcn_fmed3f(out_max[r], tl[r][KB - 1], sc);
+#pragma unroll
+              for (int p = KB - 1; p > 0; --p)
+                tl[r][p] = __builtin_amdgcn_fmed3f(tl[r][p - 1], tl[r][p], sc);
+              tl[r][0] = vmax(tl[r][0], sc);
+            }
+          } else {
+            // Insert the lane's scores above the cut best first, one per trip (a
+            // lane rarely has more than one): the element equal to the maximum with
+            // the lowest block, then its score is taken out and the maximum
+            // recomputed. Scores of one chunk follow every listed block, so a score
+            // equal to the cut loses the tie and need not be tried; the list's
+            // order is total, so the order of insertion does not change what it
+            // keeps.
+            float mx = max16(acc[r]);
+            const int j0 = st * 32;
+            while (mx > ws[r]) {
+              int eb = 15;
+#pragma unroll
+              for (int e = 15; e >= 0; --e) eb = (acc[r][e] == mx) ? e : eb;
+              out_max[r] = vmax(out_max[r],
+                                list_insert<KB>(bs[r], bj[r], ks, mx,
+                                                j0 + 8 * (eb >> 2) + 4 * half + (eb & 3)));
+#pragma unroll
+              for (int p = 0; p < KB; ++p)
+                if (p == ks - 1) ws[r] = bs[r][p];
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[r][e] = (e == eb) ? -INFINITY : acc[r][e];
+              mx = max16(acc[r]);
+            }
+            out_max[r] = vmax(out_max[r], mx);   // the best of the scores left out
+          }
         }
-      } else {
-        // Insert the lane's scores above the cut best first, one per trip (a lane
-        // rarely has more than one): the element equal to the maximum with the
-        // lowest block, then its score is taken out and the maximum recomputed.
-        // Scores of one chunk follow every listed block, so a score equal to the
-        // cut loses the tie and need not be tried; the list's order is total, so
-        // the order of insertion does not change what it keeps.
-        float mx = max16(acc);
-        const int j0 = st * 32;
-        while (mx > ws) {
-          int eb = 15;
-#pragma unroll
-          for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
-          out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, mx,
-                                                  j0 + 8 * (eb >> 2) + 4 * half + (eb & 3)));
-#pragma unroll
-          for (int p = 0; p < KB; ++p)
-            if (p == ks - 1) ws = bs[p];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
-          mx = max16(acc);
-        }
-        out_max = vmax(out_max, mx);   // the best of the scores left out
       }
-      MOBA_WAIT_VM_LGKM0(GB - 2);
+      MOBA_WAIT_VM_LGKM0(GB - 2 * GRP);
       bare_barrier();
     }
     MOBA_WAIT_VM_LGKM0(0);
-    if constexpr (CHAIN) {
-      // codes to blocks; entries past ks are left out too, and entries below
-      // every finite score never held a block (masked or never filled)
 #pragma unroll
-      for (int p = 0; p < KB; ++p) {
-        const uint32_t cd = __float_as_uint(tl[p]) & 0xffu;
-        const bool real = tl[p] > -1e38f;
-        if (p < ks) {
-          bs[p] = real ? tl[p] : -INFINITY;
-          bj[p] = real ? 32 * (int)(cd >> 4) + 8 * (int)((cd & 15) >> 2) + 4 * half + (int)(cd & 3)
-                       : kNoBlock;
-        } else if (real) {
-          out_max = vmax(out_max, tl[p]);
+    for (int r = 0; r < R; ++r) {
+      if constexpr (CHAIN) {
+        // codes to blocks; entries past ks are left out too, and entries below
+        // every finite score never held a block (masked or never filled)
+#pragma unroll
+        for (int p = 0; p < KB; ++p) {
+          const uint32_t cd = __float_as_uint(tl[r][p]) & 0xffu;
+          const bool real = tl[r][p] > -1e38f;
+          if (p < ks) {
+            bs[r][p] = real ? tl[r][p] : -INFINITY;
+            bj[r][p] = real ? 32 * (int)(cd >> 4) + 8 * (int)((cd & 15) >> 2) + 4 * half +
+                                  (int)(cd & 3)
+                            : kNoBlock;
+          } else if (real) {
+            out_max[r] = vmax(out_max[r], tl[r][p]);
+          }
         }
+        if (!(out_max[r] > -1e38f)) out_max[r] = -INFINITY;
       }
-      if (!(out_max > -1e38f)) out_max = -INFINITY;
-    }
-    float os[KB];
-    int oj[KB];
+      float os[KB];
+      int oj[KB];
 #pragma unroll
-    for (int p = 0; p < KB; ++p) { os[p] = swap_half(bs[p]); oj[p] = swap_half(bj[p]); }
-    out_max = vmax(out_max, swap_half(out_max));
-#pragma unroll
-    for (int p = 0; p < KB; ++p)
-      if (p < ks && oj[p] != kNoBlock)
-        out_max = vmax(out_max, list_insert<KB>(bs, bj, ks, os[p], oj[p]));
-    // the cut: the last kept entry against the best score left out
-    if (row_ok && i > ks) {
-      float s_in = 0.f;
+      for (int p = 0; p < KB; ++p) { os[p] = swap_half(bs[r][p]); oj[p] = swap_half(bj[r][p]); }
+      out_max[r] = vmax(out_max[r], swap_half(out_max[r]));
 #pragma unroll
       for (int p = 0; p < KB; ++p)
-        if (p == ks - 1) s_in = bs[p];
-      // |q|^2 from packed bf16 pairs (products exact; the screen's bound has room
-      // for the rounding of the sum)
-      float qq = 0.f;
+        if (p < ks && oj[p] != kNoBlock)
+          out_max[r] = vmax(out_max[r], list_insert<KB>(bs[r], bj[r], ks, os[p], oj[p]));
+      // the cut: the last kept entry against the best score left out
+      if (row_ok[r] && i > ks) {
+        float s_in = 0.f;
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e) {
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-        const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, qf[e]);
+        for (int p = 0; p < KB; ++p)
+          if (p == ks - 1) s_in = bs[r][p];
+        // |q|^2 from packed bf16 pairs (products exact; the screen's bound has
+        // room for the rounding of the sum)
+        float qq = 0.f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const bf16x2_t v2 = {v8[2 * x], v8[2 * x + 1]};
-          qq = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, qq, false);
+        for (int e = 0; e < D / 16; ++e) {
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+          const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, qf[r][e]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const bf16x2_t v2 = {v8[2 * x], v8[2 * x + 1]};
+            qq = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, qq, false);
+          }
         }
-      }
-      const float qnorm = sqrtf(qq + swap_half(qq));
-      float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
-      // packed values sit within 2^-15 of their score (low 8 bits cleared)
-      if constexpr (CHAIN) e2 += 0x1p-14f * (fabsf(s_in) + fabsf(out_max));
-      unsure = !(s_in - out_max > e2);
-    }
-  }
-  const int any = __syncthreads_or(unsure ? 1 : 0);
-  if (threadIdx.x == 0) flags[logical] = any ? 1 : 0;
-  if (!row_ok || half != 0) return;
-  int sj[KB];
-#pragma unroll
-  for (int p = 0; p < KB; ++p) sj[p] = kNoBlock;
-#pragma unroll
-  for (int p = 0; p < KB; ++p) {
-    if (p < ks) {
-      int j = bj[p];
-#pragma unroll
-      for (int r = 0; r < KB; ++r) {
-        if (r < ks) {
-          const bool lt = j < sj[r];
-          const int t = sj[r];
-          sj[r] = lt ? j : t;
-          j = lt ? t : j;
-        }
+        const float qnorm = sqrtf(qq + swap_half(qq));
+        float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
+        // packed values sit within 2^-15 of their score (low 8 bits cleared)
+        if constexpr (CHAIN) e2 += 0x1p-14f * (fabsf(s_in) + fabsf(out_max[r]));
+        unsure[r] = !(s_in - out_max[r] > e2);
       }
     }
   }
-  int32_t* dst = sel + row * ks;
 #pragma unroll
-  for (int p = 0; p < KB; ++p)
-    if (p < ks) dst[p] = (sj[p] == kNoBlock) ? -1 : sj[p];
+  for (int r = 0; r < R; ++r) {
+    const int any = __syncthreads_or(unsure[r] ? 1 : 0);
+    if (threadIdx.x == 0 && R * uf + r < nu) flags[R * uf + r + nu * rest] = any ? 1 : 0;
+  }
+  if (half != 0) return;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!row_ok[r]) continue;
+    int sj[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) sj[p] = kNoBlock;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      if (p < ks) {
+        int j = bj[r][p];
+#pragma unroll
+        for (int x = 0; x < KB; ++x) {
+          if (x < ks) {
+            const bool lt = j < sj[x];
+            const int t = sj[x];
+            sj[x] = lt ? j : t;
+            j = lt ? t : j;
+          }
+        }
+      }
+    }
+    int32_t* dst = sel + row[r] * ks;
+#pragma unroll
+    for (int p = 0; p < KB; ++p)
+      if (p < ks) dst[p] = (sj[p] == kNoBlock) ? -1 : sj[p];
+  }
 }
 
 template <typename T, int D, int NP>
@@ -774,15 +827,27 @@ static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const
 // up to 512 blocks: 16 chunks of 32, codes of 8 bits.
 static bool gate_chain(const Plan& p) { return p.max_nb <= 512; }
 
+// Row sets per wave in the screened pass: two halve the LDS reads per product and
+// the tile set-up per row where the lists are short; the best-first lists with
+// D = 128 would spill in the chunk loop at four waves per SIMD, so they keep one.
+template <int D, int KB, bool CHAIN>
+constexpr int gate_sets() { return (KB <= 4 && (CHAIN || D == 64)) ? 2 : 1; }
+
 template <int D>
 static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, const Work& w,
-                               int32_t* sel, hipStream_t s, int64_t ntiles, int64_t padded) {
-  dim3 grid((unsigned)padded), blk(512);
-#define MOBA_GATE_FAST(KBV, CH)                                                                 \
-  hipLaunchKernelGGL((k_gate_fast<D, KBV, CH>), grid, blk, 0, s, q, cu, w.blk_base, w.blk_seq,  \
-                     w.blk_local, w.kbar_split, w.gate_bound, p.nb, p.hq, p.hkv, p.hg, p.block, \
-                     tiles_per_block(p, tile_tokens8(p)), p.ks, ntiles, padded, w.gate_flags,   \
-                     sel)
+                               int32_t* sel, hipStream_t s) {
+  const int nu = tiles_per_block(p, tile_tokens8(p));
+  const int64_t rest = p.nb * (p.hq / p.hg);
+#define MOBA_GATE_FAST(KBV, CH)                                                               \
+  do {                                                                                        \
+    constexpr int R = gate_sets<D, KBV, CH>();                                                \
+    const int nuf = (nu + R - 1) / R;                                                         \
+    const int64_t nt = rest * nuf, pd = pad8(nt);                                             \
+    hipLaunchKernelGGL((k_gate_fast<D, KBV, CH, R>), dim3((unsigned)pd), dim3(512), 0, s, q,  \
+                       cu, w.blk_base, w.blk_seq, w.blk_local, w.kbar_split, w.gate_bound,    \
+                       p.nb, p.hq, p.hkv, p.hg, p.block, nu, nuf, p.ks, nt, pd, w.gate_flags, \
+                       sel);                                                                  \
+  } while (0)
   if (gate_chain(p)) {
     // branch-free packed-value lists while a row has at most 16 chunks of 32 blocks
     if (p.ks <= 2) MOBA_GATE_FAST(2, true);
@@ -811,9 +876,9 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
       hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
                          w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
       if (p.d == 128)
-        gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+        gate_fast_dispatch<128>(p, (const bf16*)q, cu_dev, w, sel, s);
       else
-        gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s, ntiles, padded);
+        gate_fast_dispatch<64>(p, (const bf16*)q, cu_dev, w, sel, s);
     }
     const uint8_t* flags = screen ? w.gate_flags : nullptr;
     if (p.d == 128)
