@@ -416,9 +416,11 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
         for (int e = 0; e < 16; ++e)
           if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
       }
-      // best first, one score per trip (as in k_gate_fast): the wave runs as
-      // many trips as its busiest lane needs, rather than one insertion for
-      // every position at which any lane has a candidate
+      // Insert the lane's scores above the cut best first, one per trip (a lane
+      // rarely has more than one): the element equal to the maximum with the
+      // lowest block, then its score is taken out and the maximum recomputed.
+      // The wave runs as many trips as its busiest lane needs, rather than one
+      // insertion for every position at which any lane has a candidate.
       auto max16 = [&]() __attribute__((always_inline)) {
         float m = acc[0];
 #pragma unroll
@@ -504,7 +506,7 @@ __global__ void __launch_bounds__(256) k_gate_bound(const int32_t* __restrict__ 
 }
 
 // (four waves per SIMD: two workgroups per CU, as the LDS ring allows)
-template <int D, int KB, bool CHAIN, int R>
+template <int D, int KB, int CB, int R>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
 k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
             const int32_t* __restrict__ blk_base, const int32_t* __restrict__ blk_seq,
@@ -601,9 +603,9 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
             kb_lds + (uint32_t)(((st % GB) * KBUF + 8 * (threadIdx.x - lane)) * 2));
     };
     const int rx = swz(r32) & (PIECES_ROW - 1);
-    // blocks >= i score -inf; in the packed chain the lowest finite value instead
-    // (packing the low mantissa bits of an infinity would make a NaN)
-    constexpr float kMasked = CHAIN ? -3.4028234663852886e38f : -INFINITY;
+    // blocks >= i score the lowest finite value (packing the low mantissa bits of
+    // an infinity would make a NaN)
+    constexpr float kMasked = -3.4028234663852886e38f;
     // S~^T of chunk st for every set (the LDS buffer holds it), blocks >= i masked
     auto scores = [&](int st, f32x16 (&acc)[R]) __attribute__((always_inline)) {
       const bf16* kr = &kb[st % GB][r32 * D];
@@ -627,23 +629,13 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
             if (8 * (e >> 2) + (e & 3) >= lim) acc[r][e] = kMasked;
       }
     };
-    auto max16 = [](const f32x16& acc) __attribute__((always_inline)) {
-      float m = acc[0];
-#pragma unroll
-      for (int e = 1; e < 16; e += 2)
-        m = (e + 1 < 16) ? vmax(vmax(m, acc[e]), acc[e + 1]) : vmax(m, acc[e]);
-      return m;
-    };
     // Every score either enters the list (and whatever it evicts is left out)
     // or is left out at once, so out_max ends as the best score not kept.
-    float ws[R];
     float tl[R][KB];                       // the packed chain's sorted values
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      ws[r] = -INFINITY;
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int p = 0; p < KB; ++p) tl[r][p] = -INFINITY;
-    }
     MOBA_WAIT_VM_LGKM0(0);                 // Q before any direct load
     for (int st = 0; st < GB - GRP; ++st) issue(st);
     MOBA_WAIT_VM_LGKM0(GB - 2 * GRP);
@@ -659,56 +651,31 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
         scores(st, acc);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if constexpr (CHAIN) {
-            // Few chunks (sequences of up to 512 blocks), where many scores still
-            // enter: every score passes through the lane's list without a branch.
-            // The score carries its place in the lane's stream in its 8 low
-            // mantissa bits (chunk st, position e: code 16 st + e, put in with one
-            // byte permute), so the list is a list of values and the block comes
-            // back from the bits at the end. With the values t sorted descending,
-            // admitting s gives t'_0 = max(t_0, s) and t'_p = med3(t_{p-1}, t_p, s);
-            // the value that falls off the end, min(t_last, s), is left out, and
-            // since nothing left out exceeds t_last the best of them updates as
-            // med3(out, t_last, s). Clearing 8 low bits moves a score by less than
-            // 2^-15 of itself; the screen below adds that to its error bound, so
-            // the selection it accepts is still the exact-score selection. Every
-            // packed value of a lane is distinct (distinct codes).
-            const uint32_t cbase = 16u * (uint32_t)st;
+          // Every score passes through the lane's list without a branch. The
+          // score carries its place in the lane's stream in its CB low mantissa
+          // bits (chunk st, position e: code 16 st + e, put in with one byte
+          // permute for CB = 8, one and-or otherwise), so the list is a list of
+          // values and the block comes back from the bits at the end. With the
+          // values t sorted descending, admitting s gives t'_0 = max(t_0, s) and
+          // t'_p = med3(t_{p-1}, t_p, s); the value that falls off the end,
+          // min(t_last, s), is left out, and since nothing left out exceeds
+          // t_last the best of them updates as med3(out, t_last, s). Replacing
+          // CB low bits moves a score by less than 2^(CB-23) of itself; the
+          // screen below adds that to its error bound, so the selection it
+          // accepts is still the exact-score selection. Every packed value of a
+          // lane is distinct (distinct codes).
+          const uint32_t cbase = 16u * (uint32_t)st;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const float sc = __uint_as_float(__builtin_amdgcn_perm(
-                  cbase + (uint32_t)e, __float_as_uint(acc[r][e]), 0x03020104u));
-              out_max[r] = __builtin_amdgcn_fmed3f(out_max[r], tl[r][KB - 1], sc);
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t bits = __float_as_uint(acc[r][e]);
+            const float sc = __uint_as_float(
+                CB == 8 ? __builtin_amdgcn_perm(cbase + (uint32_t)e, bits, 0x03020104u)
+                        : (bits & ~((1u << CB) - 1u)) | (cbase + (uint32_t)e));
+            out_max[r] = __builtin_amdgcn_fmed3f(out_max[r], tl[r][KB - 1], sc);
 #pragma unroll
-              for (int p = KB - 1; p > 0; --p)
-                tl[r][p] = __builtin_amdgcn_fmed3f(tl[r][p - 1], tl[r][p], sc);
-              tl[r][0] = vmax(tl[r][0], sc);
-            }
-          } else {
-            // Insert the lane's scores above the cut best first, one per trip (a
-            // lane rarely has more than one): the element equal to the maximum with
-            // the lowest block, then its score is taken out and the maximum
-            // recomputed. Scores of one chunk follow every listed block, so a score
-            // equal to the cut loses the tie and need not be tried; the list's
-            // order is total, so the order of insertion does not change what it
-            // keeps.
-            float mx = max16(acc[r]);
-            const int j0 = st * 32;
-            while (mx > ws[r]) {
-              int eb = 15;
-#pragma unroll
-              for (int e = 15; e >= 0; --e) eb = (acc[r][e] == mx) ? e : eb;
-              out_max[r] = vmax(out_max[r],
-                                list_insert<KB>(bs[r], bj[r], ks, mx,
-                                                j0 + 8 * (eb >> 2) + 4 * half + (eb & 3)));
-#pragma unroll
-              for (int p = 0; p < KB; ++p)
-                if (p == ks - 1) ws[r] = bs[r][p];
-#pragma unroll
-              for (int e = 0; e < 16; ++e) acc[r][e] = (e == eb) ? -INFINITY : acc[r][e];
-              mx = max16(acc[r]);
-            }
-            out_max[r] = vmax(out_max[r], mx);   // the best of the scores left out
+            for (int p = KB - 1; p > 0; --p)
+              tl[r][p] = __builtin_amdgcn_fmed3f(tl[r][p - 1], tl[r][p], sc);
+            tl[r][0] = vmax(tl[r][0], sc);
           }
         }
       }
@@ -718,24 +685,22 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
     MOBA_WAIT_VM_LGKM0(0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if constexpr (CHAIN) {
-        // codes to blocks; entries past ks are left out too, and entries below
-        // every finite score never held a block (masked or never filled)
+      // codes to blocks; entries past ks are left out too, and entries below
+      // every finite score never held a block (masked or never filled)
 #pragma unroll
-        for (int p = 0; p < KB; ++p) {
-          const uint32_t cd = __float_as_uint(tl[r][p]) & 0xffu;
-          const bool real = tl[r][p] > -1e38f;
-          if (p < ks) {
-            bs[r][p] = real ? tl[r][p] : -INFINITY;
-            bj[r][p] = real ? 32 * (int)(cd >> 4) + 8 * (int)((cd & 15) >> 2) + 4 * half +
-                                  (int)(cd & 3)
-                            : kNoBlock;
-          } else if (real) {
-            out_max[r] = vmax(out_max[r], tl[r][p]);
-          }
+      for (int p = 0; p < KB; ++p) {
+        const uint32_t cd = __float_as_uint(tl[r][p]) & ((1u << CB) - 1u);
+        const bool real = tl[r][p] > -1e38f;
+        if (p < ks) {
+          bs[r][p] = real ? tl[r][p] : -INFINITY;
+          bj[r][p] = real ? 32 * (int)(cd >> 4) + 8 * (int)((cd & 15) >> 2) + 4 * half +
+                                (int)(cd & 3)
+                          : kNoBlock;
+        } else if (real) {
+          out_max[r] = vmax(out_max[r], tl[r][p]);
         }
-        if (!(out_max[r] > -1e38f)) out_max[r] = -INFINITY;
       }
+      if (!(out_max[r] > -1e38f)) out_max[r] = -INFINITY;
       float os[KB];
       int oj[KB];
 #pragma unroll
@@ -767,8 +732,8 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
         }
         const float qnorm = sqrtf(qq + swap_half(qq));
         float e2 = 2.f * qnorm * bound[(int64_t)n * hkv + g] * (1.f + 0x1p-10f);
-        // packed values sit within 2^-15 of their score (low 8 bits cleared)
-        if constexpr (CHAIN) e2 += 0x1p-14f * (fabsf(s_in) + fabsf(out_max[r]));
+        // packed values sit within 2^(CB-23) of their score (twice that here)
+        e2 += (float)(1u << CB) * 0x1p-22f * (fabsf(s_in) + fabsf(out_max[r]));
         unsure[r] = !(s_in - out_max[r] > e2);
       }
     }
@@ -823,41 +788,49 @@ static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const
 #undef MOBA_GATE
 }
 
-// The screened pass keeps its lists branch-free (the packed chain) for sequences of
-// up to 512 blocks: 16 chunks of 32, codes of 8 bits.
-static bool gate_chain(const Plan& p) { return p.max_nb <= 512; }
+// Code bits of the screened pass's packed chain: 16 codes per chunk of 32 blocks.
+// Sequences of up to 512 blocks take 8 bits (one byte permute) for any topk - 1 <=
+// 16; longer ones take 12 or 13 bits, for topk - 1 <= 4 (a longer list there goes
+// straight to the exact gate). 0: no screened pass.
+static int gate_code_bits(const Plan& p) {
+  if (p.max_nb <= 512) return 8;
+  if (p.ks > 4) return 0;
+  return p.max_nb <= 8192 ? 12 : 13;
+}
 
 // Row sets per wave in the screened pass: two halve the LDS reads per product and
-// the tile set-up per row where the lists are short; the best-first lists with
-// D = 128 would spill in the chunk loop at four waves per SIMD, so they keep one.
-template <int D, int KB, bool CHAIN>
-constexpr int gate_sets() { return (KB <= 4 && (CHAIN || D == 64)) ? 2 : 1; }
+// the tile set-up per row where the lists are short (few registers each).
+template <int KB>
+constexpr int gate_sets() { return KB <= 4 ? 2 : 1; }
 
 template <int D>
 static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, const Work& w,
                                int32_t* sel, hipStream_t s) {
   const int nu = tiles_per_block(p, tile_tokens8(p));
   const int64_t rest = p.nb * (p.hq / p.hg);
-#define MOBA_GATE_FAST(KBV, CH)                                                               \
+#define MOBA_GATE_FAST(KBV, CBV)                                                              \
   do {                                                                                        \
-    constexpr int R = gate_sets<D, KBV, CH>();                                                \
+    constexpr int R = gate_sets<KBV>();                                                       \
     const int nuf = (nu + R - 1) / R;                                                         \
     const int64_t nt = rest * nuf, pd = pad8(nt);                                             \
-    hipLaunchKernelGGL((k_gate_fast<D, KBV, CH, R>), dim3((unsigned)pd), dim3(512), 0, s, q,  \
+    hipLaunchKernelGGL((k_gate_fast<D, KBV, CBV, R>), dim3((unsigned)pd), dim3(512), 0, s, q, \
                        cu, w.blk_base, w.blk_seq, w.blk_local, w.kbar_split, w.gate_bound,    \
                        p.nb, p.hq, p.hkv, p.hg, p.block, nu, nuf, p.ks, nt, pd, w.gate_flags, \
                        sel);                                                                  \
   } while (0)
-  if (gate_chain(p)) {
-    // branch-free packed-value lists while a row has at most 16 chunks of 32 blocks
-    if (p.ks <= 2) MOBA_GATE_FAST(2, true);
-    else if (p.ks <= 4) MOBA_GATE_FAST(4, true);
-    else if (p.ks <= 8) MOBA_GATE_FAST(8, true);
-    else if (p.ks <= 12) MOBA_GATE_FAST(12, true);
-    else MOBA_GATE_FAST(16, true);
+  const int cb = gate_code_bits(p);
+  if (cb == 8) {
+    if (p.ks <= 2) MOBA_GATE_FAST(2, 8);
+    else if (p.ks <= 4) MOBA_GATE_FAST(4, 8);
+    else if (p.ks <= 8) MOBA_GATE_FAST(8, 8);
+    else if (p.ks <= 12) MOBA_GATE_FAST(12, 8);
+    else MOBA_GATE_FAST(16, 8);
+  } else if (cb == 12) {
+    if (p.ks <= 2) MOBA_GATE_FAST(2, 12);
+    else MOBA_GATE_FAST(4, 12);
   } else {
-    if (p.ks <= 2) MOBA_GATE_FAST(2, false);
-    else MOBA_GATE_FAST(4, false);
+    if (p.ks <= 2) MOBA_GATE_FAST(2, 13);
+    else MOBA_GATE_FAST(4, 13);
   }
 #undef MOBA_GATE_FAST
 }
@@ -869,9 +842,8 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
   const int64_t padded = pad8(ntiles);
   if (p.dtype == MOBA_DTYPE_BF16) {
     // Screened single bf16 pass, then the exact three-pass gate on flagged tiles
-    // only. The packed chain screens any topk - 1 <= 16; the best-first lists of
-    // longer sequences pay only for topk - 1 <= 4.
-    const bool screen = gate_chain(p) || p.ks <= 4;
+    // only (every tile where no screened pass runs).
+    const bool screen = gate_code_bits(p) != 0;
     if (screen) {
       hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,
                          w.blk_base, w.kbar_err, p.hkv, w.gate_bound);
