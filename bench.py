@@ -558,6 +558,9 @@ def bench_second_workload(moba, torch, name, steps, warmup, seed, dense_steps):
            "tokens_per_s": T / (ms * 1e-3),
            "effective_attn_tflops": attn_flop / (ms * 1e-3) / 1e12,
            "attn_selected_mfma_frac": sel.get("frac"),
+           # HBM bytes per launch of the selected-block kernel on this workload
+           # (profiles/traffic_attn_selected_<config>.txt; null when stale)
+           "attn_selected_traffic": load_traffic("attn_selected", name),
            "dense_causal_ms": dms, "speedup_vs_dense": dms / ms,
            "stages": fwd["stages"]}
     del inp, out
