@@ -62,7 +62,7 @@ SMALL = [
     ("g8-heads-bf16", [900], 16, 2, 128, 192, 3, "bf16"),
     ("g3-heads-f32", [700, 450], 6, 2, 64, 64, 3, "f32"),
     ("gqa-fp32", [1200, 300], 4, 2, 128, 128, 5, "f32"),
-    # more than 512 blocks in a sequence: the screened gate's best-first lists
+    # more than 512 blocks in a sequence: the screened gate's 12-bit codes
     ("many-blocks-k3-bf16", [40000, 900], 2, 1, 64, 64, 3, "bf16"),
     ("many-blocks-k5-bf16", [36000], 4, 2, 128, 64, 5, "bf16"),
     # three q heads per kv head with 16-bit D = 128: own-block tiles of one head,
