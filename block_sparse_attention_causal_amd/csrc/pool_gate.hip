@@ -789,12 +789,10 @@ static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const
 }
 
 // Code bits of the screened pass's packed chain: 16 codes per chunk of 32 blocks.
-// Sequences of up to 512 blocks take 8 bits (one byte permute) for any topk - 1 <=
-// 16; longer ones take 12 or 13 bits, for topk - 1 <= 4 (a longer list there goes
-// straight to the exact gate). 0: no screened pass.
+// Sequences of up to 512 blocks take 8 bits (one byte permute), longer ones 12
+// (up to 8,192 blocks) or 13 bits; any topk - 1 <= 16.
 static int gate_code_bits(const Plan& p) {
   if (p.max_nb <= 512) return 8;
-  if (p.ks > 4) return 0;
   return p.max_nb <= 8192 ? 12 : 13;
 }
 
@@ -827,10 +825,16 @@ static void gate_fast_dispatch(const Plan& p, const bf16* q, const int32_t* cu, 
     else MOBA_GATE_FAST(16, 8);
   } else if (cb == 12) {
     if (p.ks <= 2) MOBA_GATE_FAST(2, 12);
-    else MOBA_GATE_FAST(4, 12);
+    else if (p.ks <= 4) MOBA_GATE_FAST(4, 12);
+    else if (p.ks <= 8) MOBA_GATE_FAST(8, 12);
+    else if (p.ks <= 12) MOBA_GATE_FAST(12, 12);
+    else MOBA_GATE_FAST(16, 12);
   } else {
     if (p.ks <= 2) MOBA_GATE_FAST(2, 13);
-    else MOBA_GATE_FAST(4, 13);
+    else if (p.ks <= 4) MOBA_GATE_FAST(4, 13);
+    else if (p.ks <= 8) MOBA_GATE_FAST(8, 13);
+    else if (p.ks <= 12) MOBA_GATE_FAST(12, 13);
+    else MOBA_GATE_FAST(16, 13);
   }
 #undef MOBA_GATE_FAST
 }
@@ -842,7 +846,7 @@ hipError_t launch_gate(const Plan& p, const void* q, const int32_t* cu_dev, cons
   const int64_t padded = pad8(ntiles);
   if (p.dtype == MOBA_DTYPE_BF16) {
     // Screened single bf16 pass, then the exact three-pass gate on flagged tiles
-    // only (every tile where no screened pass runs).
+    // only.
     const bool screen = gate_code_bits(p) != 0;
     if (screen) {
       hipLaunchKernelGGL(k_gate_bound, dim3((unsigned)(p.nseq * p.hkv)), dim3(256), 0, s,

@@ -217,19 +217,24 @@ def test_gate_near_ties_match_oracle():
     ([600000], 2, 1, 128, 5, False),     # the same, unplanted, topk - 1 = 4
     ([70000, 40000], 2, 2, 64, 4, True),  # 1,094 and 625 blocks: 12-bit codes, D = 64
     ([40000], 4, 2, 128, 3, False),      # 625 blocks, unplanted: flagged tiles
+    ([40000], 4, 2, 128, 13, True),      # 625 blocks, twelve kept: 12-bit codes
+    ([600000], 2, 1, 128, 9, False),     # 9,375 blocks, eight kept, unplanted
 ])
 def test_many_blocks_wide_codes(seqlens, hq, hkv, d, topk, plant):
     """Sequences of more than 512 blocks (block 64): the screened pass packs wider
     codes (12 bits up to 8,192 blocks, 13 beyond) into the scores, so its screen
-    bound is looser. Planted inputs must still select the targets on every row;
-    1,024 sampled tokens x every q head (each sequence's first and last tokens and
-    its early blocks among them) against the oracle, tied rows for validity."""
+    bound is looser. Planted inputs with up to four targets must still select them
+    on every row; 1,024 sampled tokens x every q head (each sequence's first and
+    last tokens and its early blocks among them) against the oracle, tied rows
+    for validity."""
     _say("many blocks bf16 %s hq=%d hkv=%d d=%d block=64 topk=%d plant=%s"
          % (seqlens, hq, hkv, d, topk, plant))
     inp = make_inputs(seqlens, hq, hkv, d, 64, topk, dtype="bf16", seed=21, device="cuda",
                       plant=plant)
     out, sel, lse = _run(inp)
-    if plant:
+    if plant and topk <= 5:
+        # (with twelve planted blocks the weakest can score below a noise block,
+        # so there only the oracle decides)
         assert torch.equal(sel.cpu(), inp.targets), "selection differs from planted targets"
     toks = sample_tokens(seqlens, 64, 1024, seed=3, every_block=False)
     tt, hh = np.repeat(toks, hq), np.tile(np.arange(hq), len(toks))
