@@ -1,5 +1,6 @@
 """GPU parity on seeded random shapes: the HIP path against the CPU oracle on every
-row of 24 batches drawn from a fixed generator, so that combinations the hand-made
+row of 24 forward batches (and every gradient element of 10 backward batches) drawn
+from a fixed generator, so that combinations the hand-made
 cases do not name (empty and one-token sequences, ragged tails, G from 1 to 8, D 64
 and 128, block sizes from 64 to 512, one to sixteen kept blocks, bf16 and fp32,
 planted or plain N(0,1) inputs) meet the kernels' tilings together.
@@ -11,8 +12,11 @@ or 1e-4 (fp32).
 """
 import numpy as np
 import pytest
+import torch
 
-from synth_inputs import make_inputs
+import block_sparse_attention_causal_amd as moba
+import oracle
+from synth_inputs import make_grad, make_inputs
 from test_gpu_parity import (TOL, _all_rows_index, _check_all_rows, _check_rows_exact_or_valid,
                              _run, _say, _to_gpu)
 
@@ -60,3 +64,52 @@ def test_random_shape_every_row(case):
     tt, hh = _all_rows_index(inp)
     n = _check_rows_exact_or_valid(inp, out, sel, tt, hh, tol, min_equal=0.97)
     print("rows with a tied, valid selection: %d of %d" % (n, tt.size))
+
+
+def _draw_backward_cases(n=10, seed=4048):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 3, 4]))
+        d = int(rng.choice([64, 128]))
+        block = int(rng.choice([64, 128, 192, 256]))
+        topk = int(rng.integers(1, 7))
+        dt = "f32" if rng.random() < 0.3 else "bf16"
+        nseq = int(rng.integers(1, 4))
+        lens = [0 if rng.random() < 0.1 else int(rng.integers(1, 1100)) for _ in range(nseq)]
+        if sum(lens) == 0:
+            lens[0] = int(rng.integers(64, 900))
+        cases.append(("b%02d" % c, lens, hkv * G, hkv, d, block, topk, dt))
+    return cases
+
+
+BWD_CASES = _draw_backward_cases()
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_random_shape_backward_every_element(case):
+    """The backward on seeded random batches (planted inputs, so that no selection
+    ties): every element of dq, dk, dv against the oracle's backward, within the
+    bars of test_gpu_backward (1e-4 fp32, 2e-2 bf16, times max(1, max |reference|))."""
+    name, seqlens, hq, hkv, d, block, topk, dt = case
+    _say("%s seqlens=%s hq=%d hkv=%d d=%d block=%d topk=%d %s"
+         % (name, seqlens, hq, hkv, d, block, topk, dt))
+    inp = make_inputs(seqlens, hq, hkv, d, block, topk, dtype=dt, seed=71, device="cuda")
+    dout = make_grad(inp.q.shape, dt, seed=72, device="cuda")
+    out, sel, lse = moba.moba_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, block, topk,
+                                      return_sel=True, return_lse=True)
+    dq, dk, dv = moba.moba_backward(inp.q, inp.k, inp.v, out, lse, dout, sel, inp.cu_seqlens,
+                                    block, topk)
+    torch.cuda.synchronize()
+    if topk > 1:                       # the gradients below are those of this selection
+        ref_fwd = oracle.all_rows(inp.q, inp.k, inp.v, inp.cu_seqlens, block, topk)
+        np.testing.assert_array_equal(sel.cpu().numpy(), ref_fwd["sel"])
+    ref = oracle.backward(inp.q, inp.k, inp.v, dout, inp.cu_seqlens, block, topk)
+    tol = TOL[inp.q.dtype]
+    for gname, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        r = ref[gname]
+        scale = max(1.0, float(np.abs(r).max()) if r.size else 1.0)
+        err = float(np.abs(got.float().cpu().numpy() - r).max()) if r.size else 0.0
+        print("  %s: max-abs error %.3g (max |ref| %.3g)" % (gname, err, scale), flush=True)
+        assert err <= tol * scale, "%s: max-abs error %.3g > %.3g" % (gname, err, tol * scale)
