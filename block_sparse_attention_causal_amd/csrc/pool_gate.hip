@@ -594,7 +594,8 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
     const int spiece = (slot % PIECES_ROW) ^ (swz(srow) & (PIECES_ROW - 1));
     // the lane's piece of block srow, and the last block it may read: chunk st
     // reads block min(32 st + srow, i - 1) (chunks past the end repeat in-range
-    // blocks, never used), one 64-bit add per chunk
+    // blocks, never used). (A running pointer instead of this multiply measured
+    // the same and spilled registers in the loop of the four-entry lists.)
     const char* kpiece = (const char*)(khi + ((gbase + srow) * hkv + g) * D + 8 * spiece);
     const int kmax = i - 1 - srow;                       // may be negative: then block i - 1
     const int64_t kstride = (int64_t)hkv * D * (int64_t)sizeof(bf16);
