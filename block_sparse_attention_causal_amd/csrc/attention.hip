@@ -650,35 +650,43 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // ---------------------------------------------------------------------------
 // Selected-block and own-block attention for 16-bit inputs with D = 128, in
-// 4-wave workgroups. The keys stream through two 32 KB LDS buffers (K then V
-// rows of a 64-key chunk, the same swizzled layout and fragment reads as
-// k_attn's direct-load path), one chunk in flight. With 64 KB of LDS two
-// workgroups share a CU, and one's tile prologue, epilogue and barrier waits
-// overlap the other's products, which matters most when tiles are short
-// (block 512: 8 chunks per selected tile; the own-block tiles of the causal
-// triangle: 1 to B/64 chunks). Every wave issues 8 direct loads per chunk (16
-// rows of K and of V), so "chunk c+1 landed" is vmcnt(0) at the end of
-// iteration c.
-//   SELECTED: a tile is 128 routed rows (4 waves x 32) of one (block, kv head)
-//     list over the block's B keys; writes fp16 parts and their LSE.
+// 4-wave workgroups. The keys stream through two LDS buffers (K then V rows of
+// a KCH-key chunk, the same swizzled layout and fragment reads as k_attn's
+// direct-load path), one chunk in flight. Several workgroups share a CU, and
+// one's tile prologue, epilogue and barrier waits overlap the others'
+// products, which matters most when tiles are short (block 512: 16 chunks per
+// selected tile; the own-block tiles of the causal triangle: 1 to B/64
+// chunks). Every wave issues KCH/8 direct loads per chunk (KCH/4 rows of K and
+// of V), so "chunk c+1 landed" is vmcnt(0) at the end of iteration c.
+//   SELECTED (KCH = 32): a tile is 128 routed rows (4 waves x 32) of one
+//     (block, kv head) list over the block's B keys; writes fp16 parts and their
+//     LSE. Two 16 KB buffers, 34 KB with the output staging: three workgroups
+//     per CU (three waves per SIMD, within the 168 registers that allows),
+//     which measured 3 to 4 % faster than two workgroups on 64-key chunks.
 //   SELF: a tile is 4 / hw groups of 32 consecutive tokens of one block for hw
 //     q heads of one kv group (hw = gcd(G, 4), one wave per head and token
 //     group, the heads sharing the K/V chunks), over the block's keys up to the
 //     tile's last token with the causal mask; the epilogue merges the row's
-//     selected parts (or, with no selection, writes the output).
-template <int MODE>
-__global__ void __launch_bounds__(64 * kSelWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+//     selected parts (or, with no selection, writes the output). KCH = 64: two
+//     32 KB buffers (the merge stages one part per buffer), two workgroups per
+//     CU.
+template <int MODE, int KCH>
+__global__ void __launch_bounds__(64 * kSelWaves)
+__attribute__((amdgpu_waves_per_eu(KCH == 32 ? 3 : 2, KCH == 32 ? 3 : 2)))
 k_attn4(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef bf16 T;
   constexpr int D = 128;
   typedef bf16x8 frag_t;
   typedef typename PartType<T>::type PT;
-  constexpr int DBUF = 2 * KC * D;                 // K rows then V rows of one chunk
-  static_assert(kSelWaves * 32 * (D + 16 / sizeof(PT)) * sizeof(PT) <= 2 * DBUF * sizeof(T) &&
-                    kSelWaves * 32 * (D + 16 / sizeof(T)) * sizeof(T) <= 2 * DBUF * sizeof(T),
-                "output staging must fit in the LDS buffers");
-  __shared__ __attribute__((aligned(16))) T lds[2 * DBUF];
+  static_assert((MODE == MODE_SELECTED && KCH == 32) || (MODE == MODE_SELF && KCH == 64),
+                "the chunk sizes the launches use");
+  static_assert(sizeof(PT) == sizeof(T), "output staging sized for 16-bit outputs");
+  constexpr int NT = KCH / 32;                     // 32-key score tiles per chunk
+  constexpr int DBUF = 2 * KCH * D;                // K rows then V rows of one chunk
+  constexpr int STAGE = kSelWaves * 32 * (D + 8);  // output staging (elements)
+  constexpr int LDS_ELEMS = (STAGE > 2 * DBUF) ? STAGE : 2 * DBUF;
+  __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
   const int64_t logical = xcd_logical(blockIdx.x, a.padded);
   if (logical >= a.ntiles) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -774,7 +782,7 @@ k_attn4(AttnArgs a) {
   auto vfrag = [&](int buf, int dt, int qq) __attribute__((always_inline)) -> frag_t {
     // keys 32kt + 16mm + {4h .. 4h+3} and the same + 8; head dim 32dt + r32
     const int kt = qq >> 1, mm = qq & 1;
-    const T* vb = lds + buf * DBUF + KC * D + (32 * kt + 16 * mm + vrow) * D;
+    const T* vb = lds + buf * DBUF + KCH * D + (32 * kt + 16 * mm + vrow) * D;
     const T* p0 = vb + 8 * ((4 * dt) ^ vx0) + vbyte;
     const T* p1 = vb + 8 * D + 8 * ((4 * dt) ^ vx1) + vbyte;
     const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
@@ -785,34 +793,40 @@ k_attn4(AttnArgs a) {
     r[4] = x1[0]; r[5] = x1[1]; r[6] = x1[2]; r[7] = x1[3];
     return __builtin_bit_cast(frag_t, r);
   };
-  // one staged chunk (keys c0 .. c0+63) into the wave's running softmax state
-  // (as in k_attn)
+  // one staged chunk (keys c0 .. c0+KCH-1) into the wave's running softmax
+  // state (as in k_attn)
   auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
     if constexpr (MODE == MODE_SELF) {
       if (!wave_live || c0 > wtok0 + 31) return;   // every key after every row
     }
-    f32x16 s0, s1;
+    f32x16 s[NT];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s0 = mma_k16(kfrag(buf, 0, kk), qf[kk], s0);
-      s1 = mma_k16(kfrag(buf, 1, kk), qf[kk], s1);
-    }
+      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s[t] = mma_k16(kfrag(buf, t, kk), qf[kk], s[t]);
     if constexpr (MODE == MODE_SELF) {
-      if (c0 + KC - 1 > wtok0) {                    // some key after some row
+      if (c0 + KCH - 1 > wtok0) {                   // some key after some row
         const int64_t tok = wtok0 + r32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t key = c0 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (key > tok) s0[e] = -INFINITY;
-          if (key + 32 > tok) s1[e] = -INFINITY;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if (key + 32 * t > tok) s[t][e] = -INFINITY;
         }
       }
     }
-    float mx = vmax(s0[0], s1[0]);
+    float mx = s[0][0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = vmax(vmax(mx, s0[e]), s1[e]);
+    for (int t = 1; t < NT; ++t) mx = vmax(mx, s[t][0]);
+#pragma unroll
+    for (int e = 1; e < 16; ++e)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) mx = vmax(mx, s[t][e]);
     mx = vmax(mx, swap_half_valu(mx, lane));
     const float m_cand = vmax(m_run, mx * a.scale_log2);
     if (__ballot(m_cand > m_run + 8.f)) {
@@ -825,51 +839,58 @@ k_attn4(AttnArgs a) {
       m_run = m_cand;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float p0[16], p1[16];
+    float pr[NT][16];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      p0[e] = fast_exp2(fmaf(s0[e], a.scale_log2, -m_use));
-      p1[e] = fast_exp2(fmaf(s1[e], a.scale_log2, -m_use));
-      psum += p0[e] + p1[e];
+      float pe = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        pr[t][e] = fast_exp2(fmaf(s[t][e], a.scale_log2, -m_use));
+        pe = (t == 0) ? pr[t][e] : pe + pr[t][e];
+      }
+      psum += pe;
     }
     l_run += psum;
-    frag_t pf[4];
-    pf[0] = pack8<T>(&p0[0]);
-    pf[1] = pack8<T>(&p0[8]);
-    pf[2] = pack8<T>(&p1[0]);
-    pf[3] = pack8<T>(&p1[8]);
+    frag_t pf[2 * NT];
 #pragma unroll
-    for (int f = 0; f < (D / 32) * 4; ++f)
-      o[f >> 2] = mma_k16(vfrag(buf, f >> 2, f & 3), pf[f & 3], o[f >> 2]);
+    for (int t = 0; t < NT; ++t) {
+      pf[2 * t] = pack8<T>(&pr[t][0]);
+      pf[2 * t + 1] = pack8<T>(&pr[t][8]);
+    }
+#pragma unroll
+    for (int f = 0; f < (D / 32) * 2 * NT; ++f)
+      o[f / (2 * NT)] =
+          mma_k16(vfrag(buf, f / (2 * NT), f % (2 * NT)), pf[f % (2 * NT)], o[f / (2 * NT)]);
   };
 
-  const int nch = (int)((kend - kbeg + KC - 1) / KC);
+  const int nch = (int)((kend - kbeg + KCH - 1) / KCH);
   const int row_stride = a.hkv * D;
   const uint32_t lds0 = lds_addr(lds);
   // chunk c into LDS buffer `buf` (the loop passes both as known constants
   // parities, so every LDS address of a chunk is a loop-invariant register plus
   // an immediate offset)
   auto issue = [&](int c, int buf) __attribute__((always_inline)) {
-    const int64_t c0 = kbeg + (int64_t)min(c, nch - 1) * KC;
+    const int64_t c0 = kbeg + (int64_t)min(c, nch - 1) * KCH;
     const T* kb = k + (c0 * a.hkv + g) * D;
     const T* vb = v + (c0 * a.hkv + g) * D;
     // SELF: keys past the tile's range (the last chunk of a causal tile) read
     // the range's last key: in bounds, and masked. (A selected block is whole
     // chunks: the block size is a multiple of 64.)
-    const int last = (MODE == MODE_SELF) ? (int)min((int64_t)(KC - 1), kend - 1 - c0) : KC - 1;
-    const uint32_t dst = lds0 + (uint32_t)(buf * DBUF * 2 + 16 * w * 256);
+    const int last = (MODE == MODE_SELF) ? (int)min((int64_t)(KCH - 1), kend - 1 - c0) : KCH - 1;
+    constexpr int WR = KCH / 4;                    // chunk rows per wave
+    const uint32_t dst = lds0 + (uint32_t)(buf * DBUF * 2 + WR * w * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * i + (lane >> 4);  // rows 16w .. 16w+15 of the chunk
+    for (int i = 0; i < WR / 4; ++i) {
+      const int r = WR * w + 4 * i + (lane >> 4);  // rows WR w .. WR w + WR - 1 of the chunk
       const int off = ((MODE == MODE_SELF) ? min(r, last) : r) * row_stride +
                       8 * ((lane & 15) ^ swz(r));
       if (i == 0) {                                // first loads from the chunk's bases
         dma16s<true>(kb, (uint32_t)off * 2u, dst);
-        dma16s<true>(vb, (uint32_t)off * 2u, dst + (uint32_t)(KC * D * 2));
+        dma16s<true>(vb, (uint32_t)off * 2u, dst + (uint32_t)(KCH * D * 2));
       } else {
         dma16s<false>(kb, (uint32_t)off * 2u, dst + (uint32_t)(1024 * i));
-        dma16s<false>(vb, (uint32_t)off * 2u, dst + (uint32_t)(KC * D * 2 + 1024 * i));
+        dma16s<false>(vb, (uint32_t)off * 2u, dst + (uint32_t)(KCH * D * 2 + 1024 * i));
       }
     }
   };
@@ -902,19 +923,19 @@ k_attn4(AttnArgs a) {
   int c = 0;
   for (; c + 1 < nch; c += 2) {
     issue(c + 1, 1);
-    compute(0, kbeg + (int64_t)c * KC);
+    compute(0, kbeg + (int64_t)c * KCH);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
     if (pref && c + 2 >= nch) issue_part(0, 0);    // the last chunk: part 0
     else issue(c + 2, 0);                          // (clamped past the end)
-    compute(1, kbeg + (int64_t)(c + 1) * KC);
+    compute(1, kbeg + (int64_t)(c + 1) * KCH);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }
   if (c < nch) {
     if (pref) issue_part(0, 1);
     else issue(c + 1, 1);                          // clamped: the last chunk again
-    compute(0, kbeg + (int64_t)c * KC);
+    compute(0, kbeg + (int64_t)c * KCH);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }
@@ -1025,7 +1046,7 @@ hipError_t launch_attn_selected(const Plan& p, const void* q, const void* k, con
   a.ntiles = tile_bound(p, p.sel_rows);
   a.padded = pad8(a.ntiles);
   if (p.sel_rows == kSelRowsPerTile) {             // bf16, D = 128
-    hipLaunchKernelGGL(k_attn4<MODE_SELECTED>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0,
+    hipLaunchKernelGGL((k_attn4<MODE_SELECTED, 32>), dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0,
                        s, a);
     return hipGetLastError();
   }
@@ -1048,7 +1069,7 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
     a.nu = tiles_per_block(p, attn4_tokens(p));
     a.ntiles = self4_tile_count(p);
     a.padded = pad8(a.ntiles);
-    hipLaunchKernelGGL(k_attn4<MODE_SELF>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s,
+    hipLaunchKernelGGL((k_attn4<MODE_SELF, 64>), dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s,
                        a);
     return hipGetLastError();
   }
