@@ -725,18 +725,27 @@ k_bwd_dkdv_dma(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ for 16-bit inputs with D = 128: k_bwd_dq's products and tiles, with the
-// forward's key pipeline (64-key chunks of K and V by direct loads into four
-// swizzled LDS buffers, three in flight, vmcnt(8) per iteration). K and V rows
-// are the A operands of S^T and dP^T; K^T fragments for dQ^T come from the same
-// K rows through ds_read_b64_tr_b16 in the key order of the dS^T registers.
+// dQ for 16-bit inputs with D = 128: k_bwd_dq's products, with the forward's
+// 4-wave tiles and key pipeline (64-key chunks of K and V by direct loads into
+// two swizzled 32 KB LDS buffers, one chunk in flight, vmcnt(0) and a barrier
+// per chunk; two workgroups per CU, so one's tile prologue, epilogue and
+// barrier waits overlap the other's products). K and V rows are the A operands
+// of S^T and dP^T; K^T fragments for dQ^T come from the same K rows through
+// ds_read_b64_tr_b16 in the key order of the dS^T registers.
+//   SELECTED: a tile is 128 routed rows (4 waves x 32) of one (block, kv head)
+//     list; writes one bf16 part per (row, slot).
+//   SELF: a tile is 4 / hw groups of 32 consecutive tokens of one block for hw
+//     q heads of one kv group (hw = gcd(G, 4)), with the causal mask; adds the
+//     row's parts and writes dQ.
 template <int MODE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(64 * kSelWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_bwd_dq_dma(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int D = 128;
+  constexpr int NW = kSelWaves;                  // waves per workgroup
   constexpr int DBUF = 2 * BKC * D;              // K rows then V rows
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * DBUF];
+  static_assert(NW * 32 * (D + 8) <= 2 * DBUF, "part staging must fit in the LDS buffers");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * DBUF];
   const int64_t logical = xcd_logical(blockIdx.x, a.padded);
   if (logical >= a.ntiles) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -762,7 +771,7 @@ k_bwd_dq_dma(BwdArgs a) {
     const int n = a.blk_seq[b], j = a.blk_local[b];
     kbeg = (int64_t)a.cu[n] + (int64_t)j * a.block;
     kend = kbeg + a.block;
-    const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * kRowsPerTile +
+    const int64_t e0 = (int64_t)a.list_offsets[L] + (tile - toffs[L]) * (kRowsPerWave * NW) +
                        (int64_t)w * kRowsPerWave;
     const int64_t e1 = a.list_offsets[L + 1];
     wave_live = e0 < e1;
@@ -772,8 +781,9 @@ k_bwd_dq_dma(BwdArgs a) {
       row = fdiv((uint32_t)ev, a.div_ks);
     }
   } else {
-    const int tt = 32 * (8 / a.hg);
-    const int nhs = a.hq / a.hg;
+    const int hw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+    const int tt = 32 * (NW / hw);
+    const int nhs = a.hq / hw;
     const int u = a.nu - 1 - (int)(logical % a.nu);
     const int64_t rest = logical / a.nu;
     const int hs = (int)(rest % nhs);
@@ -784,9 +794,9 @@ k_bwd_dq_dma(BwdArgs a) {
     const int64_t blk_end = min(blk_start + a.block, (int64_t)a.cu[n + 1]);
     const int64_t tok0 = blk_start + (int64_t)u * tt;
     if (tok0 >= blk_end) return;
-    const int h = hs * a.hg + (w % a.hg);
+    const int h = hs * hw + (w % hw);
     g = h / group;
-    wtok0 = tok0 + (int64_t)(w / a.hg) * 32;
+    wtok0 = tok0 + (int64_t)(w / hw) * 32;
     wave_live = wtok0 < blk_end;
     kbeg = blk_start;
     kend = min(tok0 + tt, blk_end);
@@ -878,37 +888,51 @@ k_bwd_dq_dma(BwdArgs a) {
   const int nch = (int)((kend - kbeg + BKC - 1) / BKC);
   const int row_stride = a.hkv * D;
   const uint32_t smem_lds = lds_addr(smem);
-  const int rowA = 8 * w + (lane >> 4), rowB = rowA + 4;
-  const int pieceA = (lane & 15) ^ swz(rowA), pieceB = (lane & 15) ^ swz(rowB);
-  auto issue = [&](int c) __attribute__((always_inline)) {
+  // chunk c (clamped to the last) into LDS buffer `buf`: each wave loads 16 rows
+  // of K and of V. Keys past the tile's range (the last chunk of a causal tile)
+  // read the range's last key: in bounds, and masked.
+  constexpr int WR = BKC / NW;                   // chunk rows per wave
+  auto issue = [&](int c, int buf) __attribute__((always_inline)) {
     const int cc = min(c, nch - 1);
     const int64_t c0 = kbeg + (int64_t)cc * BKC;
     const int last = (int)min((int64_t)(BKC - 1), kend - 1 - c0);
     const bf16* kp = k + (c0 * a.hkv + g) * D;
     const bf16* vp2 = v + (c0 * a.hkv + g) * D;
-    const uint32_t dst = smem_lds + (uint32_t)((c & 3) * DBUF * 2 + 128 * w * 16);
-    // byte offsets from the chunk's (wave-uniform) first key
-    const uint32_t offA = (uint32_t)(min(rowA, last) * row_stride + 8 * pieceA) * 2u;
-    const uint32_t offB = (uint32_t)(min(rowB, last) * row_stride + 8 * pieceB) * 2u;
-    dma16s<true>(kp, offA, dst);                  // first loads from the chunk's bases
-    dma16s<false>(kp, offB, dst + 1024u);
-    dma16s<true>(vp2, offA, dst + (uint32_t)(BKC * D * 2));
-    dma16s<false>(vp2, offB, dst + (uint32_t)(BKC * D * 2) + 1024u);
+    const uint32_t dst = smem_lds + (uint32_t)(buf * DBUF * 2 + WR * w * 256);
+#pragma unroll
+    for (int i = 0; i < WR / 4; ++i) {
+      const int r = WR * w + 4 * i + (lane >> 4);
+      // byte offset from the chunk's (wave-uniform) first key
+      const uint32_t off = (uint32_t)(min(r, last) * row_stride + 8 * ((lane & 15) ^ swz(r))) * 2u;
+      if (i == 0) {                                // first loads from the chunk's bases
+        dma16s<true>(kp, off, dst);
+        dma16s<true>(vp2, off, dst + (uint32_t)(BKC * D * 2));
+      } else {
+        dma16s<false>(kp, off, dst + (uint32_t)(1024 * i));
+        dma16s<false>(vp2, off, dst + (uint32_t)(BKC * D * 2 + 1024 * i));
+      }
+    }
   };
   // the Q and dO fragments (compiler-visible loads) land before any direct load
   MOBA_WAIT_VM_LGKM0(0);
-  issue(0);
-  issue(1);
-  issue(2);
-  MOBA_WAIT_VM_LGKM0(8);
+  issue(0, 0);
+  MOBA_WAIT_VM_LGKM0(0);
   bare_barrier();
-  for (int c = 0; c < nch; ++c) {
-    issue(c + 3);
-    compute(c & 3, kbeg + (int64_t)c * BKC);
-    MOBA_WAIT_VM_LGKM0(8);
+  // two chunks per trip, buffers 0 then 1, and an odd last chunk after the loop
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    issue(c + 1, 1);
+    compute(0, kbeg + (int64_t)c * BKC);
+    MOBA_WAIT_VM_LGKM0(0);
+    bare_barrier();
+    issue(c + 2, 0);                               // (clamped past the end)
+    compute(1, kbeg + (int64_t)(c + 1) * BKC);
+    MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }
-  MOBA_WAIT_VM_LGKM0(0);
+  if (c < nch) {
+    compute(0, kbeg + (int64_t)c * BKC);
+  }
 
   // epilogue: lane holds dQ^T[32dt + 8(i/4) + 4half + i%4][row r32]
   if (MODE == BWD_SELECTED) {
@@ -1017,24 +1041,30 @@ static hipError_t bwd_launch(const BwdArgs& base, const Plan& p, const void* out
   }
   BwdArgs a = base;
   if (p.ks > 0 && p.nentries > 0) {
-    a.ntiles = tile_bound(p, kRowsPerTile);
+    a.ntiles = tile_bound(p, p.sel_rows);            // the lists were routed in these tiles
     a.padded = pad8(a.ntiles);
     if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELECTED>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
+      hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELECTED>, dim3((unsigned)a.padded),
+                         dim3(64 * kSelWaves), 0, s, a);
     else
       hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELECTED>), dim3((unsigned)a.padded), dim3(512), 0,
                          s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    a.nu = tiles_per_block(p, attn4_tokens(p));
+    a.ntiles = self4_tile_count(p);
+    a.padded = pad8(a.ntiles);
+    hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELF>, dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
     a.nu = tiles_per_block(p, tile_tokens8(p));
     a.ntiles = self8_tile_count(p);
     a.padded = pad8(a.ntiles);
-    if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL(k_bwd_dq_dma<BWD_SELF>, dim3((unsigned)a.padded), dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELF>), dim3((unsigned)a.padded), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_dq<T, D, BWD_SELF>), dim3((unsigned)a.padded), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

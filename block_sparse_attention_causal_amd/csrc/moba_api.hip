@@ -57,8 +57,10 @@ int64_t max_grid_items(const Plan& p, bool backward) {
   if (backward) {
     const int64_t rows = p.T * p.hq;
     take((rows + 256 / (p.d / 8) - 1) / (256 / (p.d / 8)), 256);            // Delta
-    if (p.ks > 0) take(pad8(tile_bound(p, kRowsPerTile)), kAttnThreads);    // dQ selected
-    take(pad8(self8_tile_count(p)), kAttnThreads);                          // dQ self
+    if (p.ks > 0)                                                           // dQ selected
+      take(pad8(tile_bound(p, p.sel_rows)), w4 ? 64 * kSelWaves : kAttnThreads);
+    take(w4 ? pad8(self4_tile_count(p)) : pad8(self8_tile_count(p)),        // dQ self
+         w4 ? 64 * kSelWaves : kAttnThreads);
     if (w4)
       take(pad8(p.nb * p.hkv) * tiles_per_block(p, kDkvWaves * 32), 64 * kDkvWaves);
     else
@@ -822,7 +824,7 @@ moba_status_t moba_backward(const void* q, const void* k, const void* v, const v
   if (e != hipSuccess) return hip_status(e, "setup");
   if (p.ks > 0) {
     StageScope t(ST_ROUTE, s);
-    e = launch_route(p, sel, cu_seqlens_dev, w, kRowsPerTile, w.list_offsets, w.entries, s);
+    e = launch_route(p, sel, cu_seqlens_dev, w, p.sel_rows, w.list_offsets, w.entries, s);
   }
   if (e != hipSuccess) return hip_status(e, "route");
   {

@@ -46,7 +46,7 @@ struct Plan {
   int64_t tri = 0;          // sum_n Hkv * NB_n * (NB_n - 1) / 2 (route histograms)
   int64_t nlists = 0;       // nb * hkv
   int64_t nentries = 0;     // routed (row, slot) pairs
-  int32_t sel_rows = 0;     // routed rows per selected-block tile of the forward
+  int32_t sel_rows = 0;     // routed rows per selected-block tile (forward and dQ)
   // workspace offsets (bytes); -1 when not used
   size_t off_blk_base = 0, off_tri_base = 0, off_blk_seq = 0, off_blk_local = 0;
   size_t off_kbar = 0, off_kbar_split = 0, off_kbar_err = 0, off_gate_bound = 0;
