@@ -667,9 +667,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 //     q heads of one kv group (hw = gcd(G, 4), one wave per head and token
 //     group, the heads sharing the K/V chunks), over the block's keys up to the
 //     tile's last token with the causal mask; the epilogue merges the row's
-//     selected parts (or, with no selection, writes the output). KCH = 64: two
-//     32 KB buffers (the merge stages one part per buffer), two workgroups per
-//     CU.
+//     selected parts (or, with no selection, writes the output). KCH = 32
+//     (three workgroups per CU) stages one part at a time in the 32 KB the two
+//     buffers span, each wave in its own 8 KB, with a memory latency per part;
+//     KCH = 64 (two 32 KB buffers, two workgroups per CU) stages two parts at
+//     a time and loads the first during the last chunk. The launch takes 32
+//     while the parts are few for the block (k-1 <= B/128): at 1M tokens,
+//     block 2048, top-3, the own-block kernel measured 23.4 -> 21.6 ms; with
+//     block 512 the 64-key form is ahead from about six parts on.
 template <int MODE, int KCH>
 __global__ void __launch_bounds__(64 * kSelWaves)
 __attribute__((amdgpu_waves_per_eu(KCH == 32 ? 3 : 2, KCH == 32 ? 3 : 2)))
@@ -679,8 +684,8 @@ k_attn4(AttnArgs a) {
   constexpr int D = 128;
   typedef bf16x8 frag_t;
   typedef typename PartType<T>::type PT;
-  static_assert((MODE == MODE_SELECTED && KCH == 32) || (MODE == MODE_SELF && KCH == 64),
-                "the chunk sizes the launches use");
+  static_assert((MODE == MODE_SELECTED || MODE == MODE_SELF) && (KCH == 32 || KCH == 64),
+                "chunks of 32 or 64 keys");
   static_assert(sizeof(PT) == sizeof(T), "output staging sized for 16-bit outputs");
   constexpr int NT = KCH / 32;                     // 32-key score tiles per chunk
   constexpr int DBUF = 2 * KCH * D;                // K rows then V rows of one chunk
@@ -926,14 +931,14 @@ k_attn4(AttnArgs a) {
     compute(0, kbeg + (int64_t)c * KCH);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
-    if (pref && c + 2 >= nch) issue_part(0, 0);    // the last chunk: part 0
+    if (KCH == 64 && pref && c + 2 >= nch) issue_part(0, 0);   // the last chunk: part 0
     else issue(c + 2, 0);                          // (clamped past the end)
     compute(1, kbeg + (int64_t)(c + 1) * KCH);
     MOBA_WAIT_VM_LGKM0(0);
     bare_barrier();
   }
   if (c < nch) {
-    if (pref) issue_part(0, 1);
+    if (KCH == 64 && pref) issue_part(0, 1);
     else issue(c + 1, 1);                          // clamped: the last chunk again
     compute(0, kbeg + (int64_t)c * KCH);
     MOBA_WAIT_VM_LGKM0(0);
@@ -958,7 +963,33 @@ k_attn4(AttnArgs a) {
       typedef PT pvec4_t __attribute__((ext_vector_type(4)));
       const char* rp = (const char*)lds + w * 8192 + r32 * 256 + 8 * half;
       float m = lse, den = 1.f, sc = inv;
-      for (int sl = 0; sl < nsel; sl += 2) {
+      // 32-key chunks: the wave's 8 KB region of the 32 KB that the two
+      // buffers span holds one part at a time
+      for (int sl = 0; KCH == 32 && sl < nsel; ++sl) {
+        MOBA_WAIT_VM_LGKM0(0);                     // the wave's reads of the region are done
+        issue_part(sl, 0);
+        const float la = (sl == 0) ? lsel0 : (sl == 1) ? lsel1
+                         : (row >= 0) ? a.sel_lse[dst_index * a.ks + sl] : -INFINITY;
+        MOBA_WAIT_VM_LGKM0(0);
+        const float mn = fmaxf(m, la);
+        const float alpha = fast_exp2((m - mn) * kLog2e);
+        const float wa = fast_exp2((la - mn) * kLog2e);
+        den = den * alpha + wa;
+        const float so = sc * alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa) {
+            const int pos = 16 * ((4 * dt + aa) ^ swz(r32));
+            const pvec4_t xa = *(const pvec4_t*)(rp + pos);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[dt][4 * aa + e] = o[dt][4 * aa + e] * so + to_f32(xa[e]) * wa;
+          }
+        m = mn;
+        sc = 1.f;
+      }
+      for (int sl = 0; KCH == 64 && sl < nsel; sl += 2) {
         const bool two = sl + 1 < nsel;
         float la = lsel0, lb = lsel1;
         if (sl > 0) {
@@ -1069,8 +1100,14 @@ hipError_t launch_attn_self(const Plan& p, const void* q, const void* k, const v
     a.nu = tiles_per_block(p, attn4_tokens(p));
     a.ntiles = self4_tile_count(p);
     a.padded = pad8(a.ntiles);
-    hipLaunchKernelGGL((k_attn4<MODE_SELF, 64>), dim3((unsigned)a.padded), dim3(64 * kSelWaves), 0, s,
-                       a);
+    // 32-key chunks (three workgroups per CU) unless the merge has many parts
+    // for a short block: that form stages one part at a time
+    if (p.ks * 128 <= p.block)
+      hipLaunchKernelGGL((k_attn4<MODE_SELF, 32>), dim3((unsigned)a.padded), dim3(64 * kSelWaves),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn4<MODE_SELF, 64>), dim3((unsigned)a.padded), dim3(64 * kSelWaves),
+                         0, s, a);
     return hipGetLastError();
   }
   a.nu = tiles_per_block(p, tile_tokens8(p));
