@@ -34,6 +34,7 @@ __global__ void __launch_bounds__(256) k_route_count(const int32_t* __restrict__
                                                      const int32_t* __restrict__ blk_seq,
                                                      const int32_t* __restrict__ blk_local,
                                                      int hq, int hkv, int block, int ks,
+                                                     FastDiv div_pt, FastDiv div_ks,
                                                      int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];
   const int64_t c = blockIdx.x;
@@ -51,11 +52,12 @@ __global__ void __launch_bounds__(256) k_route_count(const int32_t* __restrict__
   const int nvalid = min(ks, i);
   const int32_t* base = sel + (s0 * hq + (int64_t)g * group) * ks;
   for (int e = threadIdx.x; e < total; e += 256) {
-    const int t = e / per_tok;
-    const int r = e % per_tok;
+    const int t = (int)fdiv((uint32_t)e, div_pt);
+    const int r = e - t * per_tok;
     const int j = base[t * hq * ks + r];
     // only ids a row can hold: at most min(ks, i) valid slots, each in [0, i)
-    if (j >= 0 && j < i && (r % ks) < nvalid) atomicAdd(&cnt[j], 1);
+    if (j >= 0 && j < i && (r - (int)fdiv((uint32_t)r, div_ks) * ks) < nvalid)
+      atomicAdd(&cnt[j], 1);
   }
   __syncthreads();
   const int nbn = blk_base[n + 1] - blk_base[n];
@@ -155,6 +157,7 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
                                                       const int32_t* __restrict__ chunk_off,
                                                       const int32_t* __restrict__ list_offsets,
                                                       int hq, int hkv, int block, int ks,
+                                                      FastDiv div_pt, FastDiv div_ks,
                                                       int32_t* __restrict__ entries) {
   extern __shared__ int32_t next[];                // [W][i]: per wave, per block
   const int64_t c = blockIdx.x;
@@ -182,10 +185,11 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
     row = 0;
     slot = 0;
     if (e >= e_hi) return -1;
-    const int t = e / per_tok;
-    const int r = e % per_tok;
-    slot = r % ks;
-    row = (s0 + t) * hq + (int64_t)g * group + r / ks;
+    const int t = (int)fdiv((uint32_t)e, div_pt);
+    const int r = e - t * per_tok;
+    const int h = (int)fdiv((uint32_t)r, div_ks);
+    slot = r - h * ks;
+    row = (s0 + t) * hq + (int64_t)g * group + h;
     return sel[row * ks + slot];
   };
   int32_t* mine = next + w * i;
@@ -242,8 +246,12 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
   if (p.ks == 0 || p.nb == 0) return hipSuccess;
   const unsigned nchunks = (unsigned)(p.nb * p.hkv);
   const size_t lds = (size_t)p.max_nb * sizeof(int32_t);
+  // entry e of a chunk: token e / (G ks), head and slot from e mod (G ks)
+  const FastDiv div_pt = make_fastdiv((uint32_t)((p.hq / p.hkv) * p.ks));
+  const FastDiv div_ks = make_fastdiv((uint32_t)p.ks);
   hipLaunchKernelGGL(k_route_count, dim3(nchunks), dim3(256), lds, s, sel, cu_dev, w.blk_base,
-                     w.tri_base, w.blk_seq, w.blk_local, p.hq, p.hkv, p.block, p.ks, w.hist);
+                     w.tri_base, w.blk_seq, w.blk_local, p.hq, p.hkv, p.block, p.ks, div_pt,
+                     div_ks, w.hist);
   hipLaunchKernelGGL(k_route_lists, dim3((unsigned)((p.nlists + 3) / 4)), dim3(256), 0, s,
                      w.hist, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, p.hkv, p.nlists,
                      w.chunk_off, w.list_count);
@@ -255,7 +263,7 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
   while (waves > 1 && (size_t)waves * p.max_nb * sizeof(int32_t) > 65536) waves >>= 1;
   hipLaunchKernelGGL(k_route_scatter, dim3(nchunks), dim3(64 * waves), lds * waves, s, sel,
                      cu_dev, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, w.chunk_off,
-                     list_offsets, p.hq, p.hkv, p.block, p.ks, entries);
+                     list_offsets, p.hq, p.hkv, p.block, p.ks, div_pt, div_ks, entries);
   return hipGetLastError();
 }
 
