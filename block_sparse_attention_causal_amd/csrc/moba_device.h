@@ -271,8 +271,9 @@ inline FastDiv make_fastdiv(uint32_t d) {
   f.m = (uint32_t)((((1ull << sh) - d) << 32) / d + 1);
   return f;
 }
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (__umulhi(n, f.m) + n) >> f.s;
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)n * f.m) >> 32);   // v_mul_hi_u32 on the GPU
+  return (hi + n) >> f.s;
 }
 
 // A bare s_barrier (the host pass of the compiler sees only an empty body).

@@ -13,14 +13,14 @@ namespace moba {
 constexpr int kRowsPerWave = 32;           // one 32-row MFMA tile per wave
 constexpr int kGateWaves = 8;              // gate workgroups: 512 threads
 // Attention workgroups of the general kernels (fp32, or D = 64): 8 waves (512
-// threads), one per CU; all eight share each staged K/V chunk. The backward uses
-// 8-wave tiles too.
+// threads), one per CU; all eight share each staged K/V chunk. Their backward
+// uses 8-wave tiles too.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kRowsPerTile = kRowsPerWave * kAttnWaves;   // routed rows per 8-wave tile
-// The forward attention kernels for 16-bit inputs with D = 128 run 4-wave
-// workgroups, two per CU: selected-block tiles of 128 routed rows, own-block
-// tiles of 128 rows (heads x tokens).
+// The attention kernels for 16-bit inputs with D = 128 (forward, and the
+// backward's dQ) run 4-wave workgroups, two or three per CU: selected-block
+// tiles of 128 routed rows, own-block tiles of 128 rows (heads x tokens).
 constexpr int kSelWaves = 4;
 constexpr int kSelRowsPerTile = kRowsPerWave * kSelWaves;
 // Backward dK/dV tiles: 8 waves x 32 keys for 16-bit inputs with D = 128, else 4 waves.
