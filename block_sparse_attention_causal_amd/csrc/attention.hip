@@ -694,7 +694,10 @@ k_attn4(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T lds[LDS_ELEMS];
   const int64_t logical = xcd_logical(blockIdx.x, a.padded);
   if (logical >= a.ntiles) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // the wave index in a scalar register: everything derived from it (heads,
+  // token groups, row bases) stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, r32 = lane & 31;
   const T* __restrict__ q = (const T*)a.q;
   const T* __restrict__ k = (const T*)a.k;
@@ -763,7 +766,7 @@ k_attn4(AttnArgs a) {
   const int nsel = (MODE == MODE_SELF) ? min(a.ks, blk_i) : 0;
   const bool pref = MODE == MODE_SELF && nsel > 0;
   float lsel0 = -INFINITY, lsel1 = -INFINITY;
-  if (pref && row >= 0) {
+  if (KCH == 64 && pref && row >= 0) {
     lsel0 = a.sel_lse[dst_index * a.ks];
     if (nsel > 1) lsel1 = a.sel_lse[dst_index * a.ks + 1];
   }
@@ -968,8 +971,7 @@ k_attn4(AttnArgs a) {
       for (int sl = 0; KCH == 32 && sl < nsel; ++sl) {
         MOBA_WAIT_VM_LGKM0(0);                     // the wave's reads of the region are done
         issue_part(sl, 0);
-        const float la = (sl == 0) ? lsel0 : (sl == 1) ? lsel1
-                         : (row >= 0) ? a.sel_lse[dst_index * a.ks + sl] : -INFINITY;
+        const float la = (row >= 0) ? a.sel_lse[dst_index * a.ks + sl] : -INFINITY;
         MOBA_WAIT_VM_LGKM0(0);
         const float mn = fmaxf(m, la);
         const float alpha = fast_exp2((m - mn) * kLog2e);
