@@ -523,7 +523,8 @@ k_bwd_dkdv_dma(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float meta_lds[4][DKV_WAVES][64];
   __shared__ __attribute__((aligned(16))) int32_t ent_lds[8][DKV_WAVES][64];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[DKV_WAVES * 32 * D];   // the tile's V rows
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar wave index
   const int half = lane >> 5, r32 = lane & 31;
   const int G = a.hq / a.hkv;
   // dispatch id -> (list, key tile): list 8 (j / kvt) + xcd, key tile j % kvt
@@ -748,7 +749,8 @@ k_bwd_dq_dma(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * DBUF];
   const int64_t logical = xcd_logical(blockIdx.x, a.padded);
   if (logical >= a.ntiles) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar wave index
   const int half = lane >> 5, r32 = lane & 31;
   const int group = a.hq / a.hkv;
   const bf16* __restrict__ q = (const bf16*)a.q;

@@ -551,7 +551,8 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
     return;
   }
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar wave index
   const int half = lane >> 5, r32 = lane & 31;
   const int h = hs * hg + (w % hg);
   const int g = h / (hq / hkv);

@@ -31,8 +31,8 @@ from collections import defaultdict
 
 # kernel key -> pattern on the (demangled or mangled) kernel name
 KERNELS = {
-    "attn_selected": r"k_attn<[^,]+, \d+, 1>|k_attnI\w+Li1EEEv|k_attn4<1>|k_attn4ILi1E",
-    "attn_self": r"k_attn<[^,]+, \d+, 0>|k_attnI\w+Li0EEEv|k_attn4<0>|k_attn4ILi0E",
+    "attn_selected": r"k_attn<[^,]+, \d+, 1>|k_attnI\w+Li1EEEv|k_attn4<1[,>]|k_attn4ILi1E",
+    "attn_self": r"k_attn<[^,]+, \d+, 0>|k_attnI\w+Li0EEEv|k_attn4<0[,>]|k_attn4ILi0E",
     "attn_dense": r"k_attn<[^,]+, \d+, 2>|k_attnI\w+Li2EEEv",
     "gate_fast": r"k_gate_fast",
     "gate_bound": r"k_gate_bound",

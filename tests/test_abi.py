@@ -255,6 +255,11 @@ def test_profiling_kernel_keys():
         "_ZN4moba7k_attn4ILi0EEEvNS_8AttnArgsE": "attn_self",
         "void moba::k_attn4<1>(moba::AttnArgs)": "attn_selected",
         "void moba::k_attn4<0>(moba::AttnArgs)": "attn_self",
+        "_ZN4moba7k_attn4ILi1ELi32EEEvNS_8AttnArgsE": "attn_selected",
+        "_ZN4moba7k_attn4ILi0ELi64EEEvNS_8AttnArgsE": "attn_self",
+        "void moba::k_attn4<1, 32>(moba::AttnArgs)": "attn_selected",
+        "void moba::k_attn4<0, 32>(moba::AttnArgs)": "attn_self",
+        "void moba::k_attn4<0, 64>(moba::AttnArgs)": "attn_self",
         "_ZN4moba10k_dec_partIDF16bLi128EEEvNS_10DecodeArgsE": "decode_part",
         "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel": "copy_calibration",
     }
