@@ -48,7 +48,7 @@ int64_t max_grid_items(const Plan& p, bool backward) {
   if (p.ks > 0) {
     take(pad8(gate_tile_count(p)), 64 * kGateWaves);        // gate passes
     take((int64_t)p.nseq * p.hkv, 256);                     // gate bound
-    take(p.nb * p.hkv, 512);                                // route count / scatter
+    take(pad8(p.nb) * p.hkv, 512);                          // route count / scatter
     take((p.nlists + 3) / 4, 256);                          // route list scans
     take(pad8(tile_bound(p, p.sel_rows)), w4 ? 64 * kSelWaves : kAttnThreads);
   }

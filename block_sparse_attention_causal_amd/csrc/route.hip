@@ -21,6 +21,18 @@
 
 namespace moba {
 
+// Chunk (query block b, kv head g) of workgroup id x, for the count and scatter
+// grids of 8 * ceil(nb / 8) * hkv workgroups: ids go round-robin over the 8
+// XCDs, so block b goes to XCD b mod 8 and its hkv chunks run there one after
+// another. Those chunks read the same 256-byte rows of sel (32 bytes each) and
+// share them in that XCD's L2, while consecutive blocks still spread over the
+// XCDs. (With b * hkv + g the kv heads of a block went to eight XCDs, each
+// fetching whole rows: four times sel's bytes from DRAM at 1M tokens.)
+__device__ __forceinline__ int64_t chunk_block(int64_t x, int hkv) {
+  return ((x >> 3) / hkv) * 8 + (x & 7);
+}
+__device__ __forceinline__ int chunk_head(int64_t x, int hkv) { return (int)((x >> 3) % hkv); }
+
 __device__ __forceinline__ int64_t tri_index(const int32_t* tri_base, int n, int nbn, int g,
                                              int i, int j) {
   return (int64_t)tri_base[n] + (int64_t)g * ((int64_t)nbn * (nbn - 1) / 2) +
@@ -33,13 +45,13 @@ __global__ void __launch_bounds__(256) k_route_count(const int32_t* __restrict__
                                                      const int32_t* __restrict__ tri_base,
                                                      const int32_t* __restrict__ blk_seq,
                                                      const int32_t* __restrict__ blk_local,
-                                                     int hq, int hkv, int block, int ks,
-                                                     FastDiv div_pt, FastDiv div_ks,
+                                                     int64_t nb, int hq, int hkv, int block,
+                                                     int ks, FastDiv div_pt, FastDiv div_ks,
                                                      int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];
-  const int64_t c = blockIdx.x;
-  const int64_t b = c / hkv;
-  const int g = (int)(c % hkv);
+  const int64_t b = chunk_block(blockIdx.x, hkv);
+  if (b >= nb) return;
+  const int g = chunk_head(blockIdx.x, hkv);
   const int n = blk_seq[b], i = blk_local[b];
   if (i == 0) return;
   const int group = hq / hkv;
@@ -51,14 +63,40 @@ __global__ void __launch_bounds__(256) k_route_count(const int32_t* __restrict__
   const int total = (int)len * per_tok;            // below T * hq * ks < 2^31
   const int nvalid = min(ks, i);
   const int32_t* base = sel + (s0 * hq + (int64_t)g * group) * ks;
-  for (int e = threadIdx.x; e < total; e += 256) {
-    const int t = (int)fdiv((uint32_t)e, div_pt);
-    const int r = e - t * per_tok;
-    const int j = base[t * hq * ks + r];
-    // only ids a row can hold: at most min(ks, i) valid slots, each in [0, i)
-    if (j >= 0 && j < i && (r - (int)fdiv((uint32_t)r, div_ks) * ks) < nvalid)
-      atomicAdd(&cnt[j], 1);
+  // eight loads in flight before their counts go to LDS: the loads take a
+  // clamped index (entry total-1 stands in past the end) so that none sits
+  // under a branch, which would make the compiler wait for each. A lane counts
+  // a run of equal ids in a register and adds the run to LDS when the id
+  // changes: with a stride that G (k-1) divides, a lane keeps one head and slot,
+  // whose rows often choose the same block, and the lanes of a wave that add to
+  // one LDS word at once would otherwise be serialised.
+  constexpr int NL = 8;
+  int run_j = -1, run_n = 0;
+  for (int e0 = threadIdx.x; e0 < total; e0 += 256 * NL) {
+    int jv[NL];
+    bool ok[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int e = e0 + 256 * u;
+      const int ec = min(e, total - 1);
+      const int t = (int)fdiv((uint32_t)ec, div_pt);
+      const int r = ec - t * per_tok;
+      jv[u] = base[t * hq * ks + r];
+      // only ids a row can hold: at most min(ks, i) valid slots, each in [0, i)
+      ok[u] = e < total && (r - (int)fdiv((uint32_t)r, div_ks) * ks) < nvalid;
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int j = (ok[u] && jv[u] >= 0 && jv[u] < i) ? jv[u] : -1;
+      if (j != run_j) {
+        if (run_j >= 0) atomicAdd(&cnt[run_j], run_n);
+        run_j = j;
+        run_n = 0;
+      }
+      ++run_n;
+    }
   }
+  if (run_j >= 0) atomicAdd(&cnt[run_j], run_n);
   __syncthreads();
   const int nbn = blk_base[n + 1] - blk_base[n];
   const int64_t dst = tri_index(tri_base, n, nbn, g, i, 0);
@@ -156,13 +194,13 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
                                                       const int32_t* __restrict__ blk_local,
                                                       const int32_t* __restrict__ chunk_off,
                                                       const int32_t* __restrict__ list_offsets,
-                                                      int hq, int hkv, int block, int ks,
-                                                      FastDiv div_pt, FastDiv div_ks,
+                                                      int64_t nb, int hq, int hkv, int block,
+                                                      int ks, FastDiv div_pt, FastDiv div_ks,
                                                       int32_t* __restrict__ entries) {
   extern __shared__ int32_t next[];                // [W][i]: per wave, per block
-  const int64_t c = blockIdx.x;
-  const int64_t b = c / hkv;
-  const int g = (int)(c % hkv);
+  const int64_t b = chunk_block(blockIdx.x, hkv);
+  if (b >= nb) return;
+  const int g = chunk_head(blockIdx.x, hkv);
   const int n = blk_seq[b], i = blk_local[b];
   if (i == 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
@@ -180,27 +218,48 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
   // the wave's slice [e_lo, e_hi) of the chunk's entries, whole steps of 64
   const int slice = (total + 64 * W - 1) / (64 * W) * 64;
   const int e_lo = min(total, w * slice), e_hi = min(total, e_lo + slice);
-  // entry e of the chunk: its row, slot and block id (-1 outside the slice)
+  // entry e of the chunk: its row, slot and block id (-1 outside the slice).
+  // The load takes a clamped index (e_hi - 1 >= 0: every chunk has entries),
+  // so it never sits under a branch and several stay in flight.
   auto fetch = [&](int e, int64_t& row, int& slot) __attribute__((always_inline)) -> int {
-    row = 0;
-    slot = 0;
-    if (e >= e_hi) return -1;
-    const int t = (int)fdiv((uint32_t)e, div_pt);
-    const int r = e - t * per_tok;
+    const int ec = min(e, e_hi - 1);
+    const int t = (int)fdiv((uint32_t)ec, div_pt);
+    const int r = ec - t * per_tok;
     const int h = (int)fdiv((uint32_t)r, div_ks);
     slot = r - h * ks;
     row = (s0 + t) * hq + (int64_t)g * group + h;
-    return sel[row * ks + slot];
+    // -1 past the slice by an or, not a select: a select lets the compiler move
+    // the load under a branch again
+    return sel[row * ks + slot] | -(int)(e >= e_hi);
   };
   int32_t* mine = next + w * i;
   for (int j = threadIdx.x; j < W * i; j += blockDim.x) next[j] = 0;
   __syncthreads();
-  for (int e = e_lo + lane; e < e_hi; e += 64) {
-    int64_t row;
-    int slot;
-    const int j = fetch(e, row, slot);
-    if (j >= 0 && j < i && slot < nvalid) atomicAdd(&mine[j], 1);
+  // (loads in flight and runs counted in registers as in k_route_count)
+  constexpr int NL = 8;
+  int run_j = -1, run_n = 0;
+  for (int e0 = e_lo + lane; e0 < e_hi; e0 += 64 * NL) {
+    int jv[NL];
+    bool ok[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      int64_t row;
+      int slot;
+      jv[u] = fetch(e0 + 64 * u, row, slot);
+      ok[u] = slot < nvalid;
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int j = (ok[u] && jv[u] >= 0 && jv[u] < i) ? jv[u] : -1;
+      if (j != run_j) {
+        if (run_j >= 0) atomicAdd(&mine[run_j], run_n);
+        run_j = j;
+        run_n = 0;
+      }
+      ++run_n;
+    }
   }
+  if (run_j >= 0) atomicAdd(&mine[run_j], run_n);
   __syncthreads();
   // counts -> first places: the list's segment for this chunk, then wave by wave
   for (int j = threadIdx.x; j < i; j += blockDim.x) {
@@ -212,31 +271,56 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
     }
   }
   __syncthreads();
-  int64_t row_n;
-  int slot_n;
-  int j_n = fetch(e_lo + lane, row_n, slot_n);
-  // A wave's own LDS accesses take effect in program order, so its counters need
-  // no barrier between steps (only the compiler must keep the order), and the
-  // next step's ids are loaded before this step ranks.
-  for (int e0 = e_lo; e0 < e_hi; e0 += 64) {
-    const int j = j_n;
-    const int64_t row = row_n;
-    const int slot = slot_n;
-    j_n = fetch(e0 + 64 + lane, row_n, slot_n);
-    const bool act = j >= 0 && j < i && slot < nvalid;
-    uint64_t peers = __ballot(act);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool on = act && ((j >> bit) & 1);
-      const uint64_t m = __ballot(on);
-      peers &= on ? m : ~m;
+  // Rank pass, in batches of RB steps of 64 entries: the next batch's ids are
+  // loaded while this batch ranks, the ranking touches only LDS (per-wave
+  // counters) and ballots, and the batch's entry stores go out together at its
+  // end, so a wave pays about one memory round trip per batch rather than one
+  // per step (a store between a step's load and its use makes the compiler
+  // wait for both). A wave's own LDS accesses take effect in program order, so
+  // its counters need no barrier between steps. An id is -1 for entries past
+  // the slice and for slots a row cannot hold.
+  constexpr int RB = 8;
+  auto fetch_id = [&](int e, int& val) __attribute__((always_inline)) -> int {
+    int64_t row;
+    int slot;
+    const int jv = fetch(e, row, slot);
+    val = (int)(row * ks + slot);
+    return jv | -(int)(slot >= nvalid);
+  };
+  int jq[RB], vq[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) jq[u] = fetch_id(e_lo + 64 * u + lane, vq[u]);
+  for (int e00 = e_lo; e00 < e_hi; e00 += 64 * RB) {
+    int jc[RB], vc[RB], at[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      jc[u] = jq[u];
+      vc[u] = vq[u];
     }
-    if (act) {
-      const int rank = __popcll(peers & below);
-      const int32_t base = mine[j];
-      entries[base + rank] = (int32_t)(row * ks + slot);
-      if ((peers & below) == 0) mine[j] = base + __popcll(peers);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) jq[u] = fetch_id(e00 + 64 * (RB + u) + lane, vq[u]);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      at[u] = -1;
+      if (e00 + 64 * u >= e_hi) continue;          // wave-uniform
+      const int j = jc[u];
+      const bool act = j >= 0 && j < i;
+      uint64_t peers = __ballot(act);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = act && ((j >> bit) & 1);
+        const uint64_t m = __ballot(on);
+        peers &= on ? m : ~m;
+      }
+      if (act) {
+        const int32_t base = mine[j];
+        at[u] = base + __popcll(peers & below);
+        if ((peers & below) == 0) mine[j] = base + __popcll(peers);
+      }
+      asm volatile("" ::: "memory");
     }
-    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (at[u] >= 0) entries[at[u]] = vc[u];
   }
 }
 
@@ -244,14 +328,14 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
                         int rows_per_tile,
                         int32_t* list_offsets, int32_t* entries, hipStream_t s) {
   if (p.ks == 0 || p.nb == 0) return hipSuccess;
-  const unsigned nchunks = (unsigned)(p.nb * p.hkv);
+  const unsigned nchunks = (unsigned)(pad8(p.nb) * p.hkv);
   const size_t lds = (size_t)p.max_nb * sizeof(int32_t);
   // entry e of a chunk: token e / (G ks), head and slot from e mod (G ks)
   const FastDiv div_pt = make_fastdiv((uint32_t)((p.hq / p.hkv) * p.ks));
   const FastDiv div_ks = make_fastdiv((uint32_t)p.ks);
   hipLaunchKernelGGL(k_route_count, dim3(nchunks), dim3(256), lds, s, sel, cu_dev, w.blk_base,
-                     w.tri_base, w.blk_seq, w.blk_local, p.hq, p.hkv, p.block, p.ks, div_pt,
-                     div_ks, w.hist);
+                     w.tri_base, w.blk_seq, w.blk_local, p.nb, p.hq, p.hkv, p.block, p.ks,
+                     div_pt, div_ks, w.hist);
   hipLaunchKernelGGL(k_route_lists, dim3((unsigned)((p.nlists + 3) / 4)), dim3(256), 0, s,
                      w.hist, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, p.hkv, p.nlists,
                      w.chunk_off, w.list_count);
@@ -263,7 +347,7 @@ hipError_t launch_route(const Plan& p, const int32_t* sel, const int32_t* cu_dev
   while (waves > 1 && (size_t)waves * p.max_nb * sizeof(int32_t) > 65536) waves >>= 1;
   hipLaunchKernelGGL(k_route_scatter, dim3(nchunks), dim3(64 * waves), lds * waves, s, sel,
                      cu_dev, w.blk_base, w.tri_base, w.blk_seq, w.blk_local, w.chunk_off,
-                     list_offsets, p.hq, p.hkv, p.block, p.ks, div_pt, div_ks, entries);
+                     list_offsets, p.nb, p.hq, p.hkv, p.block, p.ks, div_pt, div_ks, entries);
   return hipGetLastError();
 }
 
