@@ -290,6 +290,11 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
   int jq[RB], vq[RB];
 #pragma unroll
   for (int u = 0; u < RB; ++u) jq[u] = fetch_id(e_lo + 64 * u + lane, vq[u]);
+  // the previous step's ids and peer masks: when no lane's id changed (a lane
+  // keeps one head and slot from step to step when G (k-1) divides 64, and a
+  // head's rows often choose the same blocks), the peers are the same too
+  int j_prev = -2;
+  uint64_t peers_prev = 0;
   for (int e00 = e_lo; e00 < e_hi; e00 += 64 * RB) {
     int jc[RB], vc[RB], at[RB];
 #pragma unroll
@@ -303,14 +308,22 @@ __global__ void __launch_bounds__(512) k_route_scatter(const int32_t* __restrict
     for (int u = 0; u < RB; ++u) {
       at[u] = -1;
       if (e00 + 64 * u >= e_hi) continue;          // wave-uniform
-      const int j = jc[u];
-      const bool act = j >= 0 && j < i;
-      uint64_t peers = __ballot(act);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const bool on = act && ((j >> bit) & 1);
-        const uint64_t m = __ballot(on);
-        peers &= on ? m : ~m;
+      const int j0 = jc[u];
+      const bool act = j0 >= 0 && j0 < i;
+      const int j = act ? j0 : -1;
+      uint64_t peers;
+      if (__ballot(j != j_prev) == 0) {
+        peers = peers_prev;
+      } else {
+        peers = __ballot(act);
+        for (int bit = 0; bit < nbits; ++bit) {
+          const bool on = act && ((j >> bit) & 1);
+          const uint64_t m = __ballot(on);
+          peers &= on ? m : ~m;
+        }
       }
+      j_prev = j;
+      peers_prev = peers;
       if (act) {
         const int32_t base = mine[j];
         at[u] = base + __popcll(peers & below);
