@@ -338,8 +338,34 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
   const int h = hs * hg + (w % hg);
   const int g = h / (hq / hkv);
   const int64_t tok = tok0 + (int64_t)(w / hg) * 32 + r32;
-  const bool row_ok = tok < blk_end;
-  const int64_t row = tok * hq + h;
+  bool row_ok = tok < blk_end;
+  int64_t row = tok * hq + h;
+  bool wave_has = true;                               // the wave has rows to score
+  if (flags) {
+    // After the screened pass only the rows it left unsettled (their first
+    // slot holds -2) are scored again, packed into the leading waves of the
+    // tile; every row of a tile has the same candidates and kv head, so any
+    // wave can take any of them. The waves left without rows still stage keys.
+    __shared__ int64_t crow[256];
+    __shared__ int ccount[8];
+    const bool fl = row_ok && sel[row * ks] == -2;
+    const uint64_t bal = __ballot(fl) & 0xffffffffull;   // one bit per row (half 0)
+    if (lane == 0) ccount[w] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int cv = ccount[v];
+      before += (v < w) ? cv : 0;
+      total += cv;
+    }
+    if (fl && half == 0) crow[before + __popcll(bal & ((1ull << r32) - 1))] = row;
+    __syncthreads();
+    const int ci = 32 * w + r32;
+    row_ok = ci < total;
+    row = row_ok ? crow[ci] : 0;
+    wave_has = 32 * w < total;
+  }
 
   float bs[KB];
   int bj[KB];
@@ -396,50 +422,52 @@ __global__ void __launch_bounds__(512) k_gate(const T* __restrict__ q,
     int buf = 0;
     for (int j0 = 0; j0 < i; j0 += 32) {
       if (j0 + 32 < i) fetch(j0 + 32);
-      f32x16 acc;
+      if (wave_has) {
+        f32x16 acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int part = 0; part < NP; ++part) {
+        for (int part = 0; part < NP; ++part) {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          frag_t a = load8(&kb[buf][part][r32][16 * kk + 8 * half]);
-          acc = mma_k16(a, qf[kk], acc);
+          for (int kk = 0; kk < D / 16; ++kk) {
+            frag_t a = load8(&kb[buf][part][r32][16 * kk + 8 * half]);
+            acc = mma_k16(a, qf[kk], acc);
+          }
         }
-      }
-      // Candidates of this lane arrive in increasing block order, and every
-      // block already in the list is lower, so a candidate enters only with a
-      // strictly larger score than the list's worst (a tie keeps the lower
-      // block). Blocks >= i (last chunk only) are not candidates.
-      if (j0 + 32 > i) {
+        // Candidates of this lane arrive in increasing block order, and every
+        // block already in the list is lower, so a candidate enters only with a
+        // strictly larger score than the list's worst (a tie keeps the lower
+        // block). Blocks >= i (last chunk only) are not candidates.
+        if (j0 + 32 > i) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
-      }
-      // Insert the lane's scores above the cut best first, one per trip (a lane
-      // rarely has more than one): the element equal to the maximum with the
-      // lowest block, then its score is taken out and the maximum recomputed.
-      // The wave runs as many trips as its busiest lane needs, rather than one
-      // insertion for every position at which any lane has a candidate.
-      auto max16 = [&]() __attribute__((always_inline)) {
-        float m = acc[0];
+          for (int e = 0; e < 16; ++e)
+            if (j0 + 8 * (e >> 2) + 4 * half + (e & 3) >= i) acc[e] = -INFINITY;
+        }
+        // Insert the lane's scores above the cut best first, one per trip (a lane
+        // rarely has more than one): the element equal to the maximum with the
+        // lowest block, then its score is taken out and the maximum recomputed.
+        // The wave runs as many trips as its busiest lane needs, rather than one
+        // insertion for every position at which any lane has a candidate.
+        auto max16 = [&]() __attribute__((always_inline)) {
+          float m = acc[0];
 #pragma unroll
-        for (int e = 1; e < 16; e += 2)
-          m = (e + 1 < 16) ? vmax(vmax(m, acc[e]), acc[e + 1]) : vmax(m, acc[e]);
-        return m;
-      };
-      float mx = max16();
-      while (mx > ws) {
-        int eb = 15;
+          for (int e = 1; e < 16; e += 2)
+            m = (e + 1 < 16) ? vmax(vmax(m, acc[e]), acc[e + 1]) : vmax(m, acc[e]);
+          return m;
+        };
+        float mx = max16();
+        while (mx > ws) {
+          int eb = 15;
 #pragma unroll
-        for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
-        list_insert<KB>(bs, bj, ks, mx, j0 + 8 * (eb >> 2) + 4 * half + (eb & 3));
+          for (int e = 15; e >= 0; --e) eb = (acc[e] == mx) ? e : eb;
+          list_insert<KB>(bs, bj, ks, mx, j0 + 8 * (eb >> 2) + 4 * half + (eb & 3));
 #pragma unroll
-        for (int p = 0; p < KB; ++p)
-          if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
+          for (int p = 0; p < KB; ++p)
+            if (p == ks - 1) { ws = bs[p]; wj = bj[p]; }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
-        mx = max16();
+          for (int e = 0; e < 16; ++e) acc[e] = (e == eb) ? -INFINITY : acc[e];
+          mx = max16();
+        }
       }
       if (j0 + 32 < i) stash(buf ^ 1);
       __syncthreads();
@@ -768,9 +796,11 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
       }
     }
     int32_t* dst = sel + row[r] * ks;
+    // a row the screen cannot settle is marked -2 in its first slot: the exact
+    // gate scores those rows only (its tile is flagged too)
 #pragma unroll
     for (int p = 0; p < KB; ++p)
-      if (p < ks) dst[p] = (sj[p] == kNoBlock) ? -1 : sj[p];
+      if (p < ks) dst[p] = (p == 0 && unsure[r]) ? -2 : (sj[p] == kNoBlock) ? -1 : sj[p];
   }
 }
 
