@@ -1,5 +1,5 @@
 """GPU parity on seeded random shapes: the HIP path against the CPU oracle on every
-row of 24 forward batches (and every gradient element of 10 backward batches) drawn
+row of 64 forward batches (and every gradient element of 20 backward batches) drawn
 from a fixed generator, so that combinations the hand-made
 cases do not name (empty and one-token sequences, ragged tails, G from 1 to 8, D 64
 and 128, block sizes from 64 to 512, one to sixteen kept blocks, bf16 and fp32,
@@ -23,7 +23,7 @@ from test_gpu_parity import (TOL, _all_rows_index, _check_all_rows, _check_rows_
 pytestmark = pytest.mark.gpu
 
 
-def _draw_cases(n=24, seed=2024):
+def _draw_cases(n=64, seed=2024):
     rng = np.random.default_rng(seed)
     cases = []
     for c in range(n):
@@ -66,7 +66,7 @@ def test_random_shape_every_row(case):
     print("rows with a tied, valid selection: %d of %d" % (n, tt.size))
 
 
-def _draw_backward_cases(n=10, seed=4048):
+def _draw_backward_cases(n=20, seed=4048):
     rng = np.random.default_rng(seed)
     cases = []
     for c in range(n):
