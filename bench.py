@@ -152,7 +152,7 @@ def cpu_baseline(inp, hq, budget_s, seed):
     import oracle
     from synth_inputs import sample_tokens
     # every core this process may run on, unless OMP_NUM_THREADS sets the CPU share
-    # (a GPU machine gives each GPU a share of its cores through it)
+    # (a machine shared by several GPUs may give each one a share of its cores so)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or nproc()
     kf = oracle._f32(inp.k)
     vf = oracle._f32(inp.v)
