@@ -471,6 +471,36 @@ def time_forward(moba, torch, inp, cu_dev, steps, warmup, timing=True):
     return {"ms": ms, "work": work, "stages": stage_report(stages, work, peak)}
 
 
+def bench_merge(moba, torch, inp, cu_dev, steps, warmup, self_ms, work):
+    """The merge of the parts runs inside the self-block kernel's epilogue, so it
+    has no launch of its own to time. Its cost is measured as an increment: the
+    same inputs through moba_forward with top-k 1 (own block only: the same
+    self-block tiles and chunk form, no parts to merge) against the workload's
+    own self-block time. The increment's algorithmic bytes are the parts it reads
+    (D values at 2 or 4 bytes and one fp32 LSE per (row, selected slot)); the
+    output store is common to both runs."""
+    if inp.topk <= 1 or self_ms is None:
+        return None
+    own_only = type("OwnOnly", (), {})()
+    for name in ("q", "k", "v", "cu_seqlens", "block", "seqlens"):
+        setattr(own_only, name, getattr(inp, name))
+    own_only.topk = 1
+    fwd = time_forward(moba, torch, own_only, cu_dev, steps, warmup, True)
+    st = fwd["stages"].get("attn_self")
+    if st is None:
+        return None
+    inc = self_ms - st["avg_ms"]
+    part_bytes = work["merge_bytes"] - inp.q.element_size() * inp.q.numel()
+    res = {"self_ms_with_merge": self_ms, "self_ms_own_block_only": st["avg_ms"],
+           "incremental_ms": inc, "parts_bytes": part_bytes,
+           "method": "self-block kernel time at the workload's top-k minus at top-k 1 "
+                     "(same inputs, HIP events on the launch stream)"}
+    if inc > 0:
+        gbs = part_bytes / (inc * 1e-3) / 1e9
+        res.update(bound="hbm", achieved_gbs=gbs, frac=gbs / PEAK_HBM_GBS)
+    return res
+
+
 def bench_small_shapes(moba, torch, seed):
     """Short prefills (4K and 8K tokens, the Llama-3.1-8B-shaped layer), where the
     pages report MoBA slower than FlashAttention because of gating and routing,
@@ -683,6 +713,12 @@ def main():
         print("[bench] gated decode against a KV cache", file=sys.stderr, flush=True)
         decode = bench_decode(moba, torch, q, k, v, inp.block, inp.topk, steps=20)
 
+    merge = None
+    if not args.no_timing and "attn_self" in stage_rep:
+        print("[bench] merge increment (own block only, top-k 1)", file=sys.stderr, flush=True)
+        merge = bench_merge(moba, torch, inp, cu_dev, args.steps, args.warmup,
+                            stage_rep["attn_self"]["avg_ms"], work)
+
     backward = None
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
@@ -733,6 +769,7 @@ def main():
         "decode": decode,
         "backward": backward,
         "stages": stage_rep,
+        "merge": merge,
         "workload_128k": second,
         "small_shapes": small,
     }
