@@ -612,6 +612,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the gated-decode measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="skip the merge increment (an own-block-only forward at top-k 1)")
     ap.add_argument("--no-second", action="store_true",
                     help="skip the metric's 128K point (varlen 131K) timed after the 1M one")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
@@ -714,7 +716,7 @@ def main():
         decode = bench_decode(moba, torch, q, k, v, inp.block, inp.topk, steps=20)
 
     merge = None
-    if not args.no_timing and "attn_self" in stage_rep:
+    if not args.no_merge and not args.no_timing and "attn_self" in stage_rep:
         print("[bench] merge increment (own block only, top-k 1)", file=sys.stderr, flush=True)
         merge = bench_merge(moba, torch, inp, cu_dev, args.steps, args.warmup,
                             stage_rep["attn_self"]["avg_ms"], work)
