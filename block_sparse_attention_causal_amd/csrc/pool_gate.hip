@@ -533,6 +533,26 @@ __global__ void __launch_bounds__(256) k_gate_bound(const int32_t* __restrict__ 
   if (threadIdx.x == 0) bound[blockIdx.x] = vmax(vmax(red[0], red[1]), vmax(red[2], red[3]));
 }
 
+// The low code bits of a packed score: (bits & ~m) | (code & m) in one
+// bitfield insert (v_bfi_b32), the mask in a VGPR and the wave-uniform code in an
+// SGPR (an and plus an or3, or a byte permute, otherwise).
+__device__ __forceinline__ uint32_t insert_code(uint32_t m, uint32_t code, uint32_t bits) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "s"(code), "v"(bits));
+  return r;
+}
+
+// max(a, b) of two values that are never NaN, in one full-rate v_max_f32 (the
+// compiler's two-operand maximum is a half-rate v_maximum3_f32, and fmaxf would
+// first canonicalise a value built from bits). The packed scores are finite (a
+// score's exponent is never changed; masked places hold the lowest finite value)
+// and the list starts at -inf.
+__device__ __forceinline__ float max_not_nan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // (four waves per SIMD: two workgroups per CU, as the LDS ring allows)
 template <int D, int KB, int CB, int R>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -683,9 +703,9 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
         for (int r = 0; r < R; ++r) {
           // Every score passes through the lane's list without a branch. The
           // score carries its place in the lane's stream in its CB low mantissa
-          // bits (chunk st, position e: code 16 st + e, put in with one byte
-          // permute for CB = 8, one and-or otherwise), so the list is a list of
-          // values and the block comes back from the bits at the end. With the
+          // bits (chunk st, position e: code 16 st + e, put in with one bitfield
+          // insert), so the list is a list of values and the block comes back
+          // from the bits at the end. With the
           // values t sorted descending, admitting s gives t'_0 = max(t_0, s) and
           // t'_p = med3(t_{p-1}, t_p, s); the value that falls off the end,
           // min(t_last, s), is left out, and since nothing left out exceeds
@@ -695,17 +715,16 @@ k_gate_fast(const bf16* __restrict__ q, const int32_t* __restrict__ cu,
           // accepts is still the exact-score selection. Every packed value of a
           // lane is distinct (distinct codes).
           const uint32_t cbase = 16u * (uint32_t)st;
+          const uint32_t cmask = (1u << CB) - 1u;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const uint32_t bits = __float_as_uint(acc[r][e]);
             const float sc = __uint_as_float(
-                CB == 8 ? __builtin_amdgcn_perm(cbase + (uint32_t)e, bits, 0x03020104u)
-                        : (bits & ~((1u << CB) - 1u)) | (cbase + (uint32_t)e));
+                insert_code(cmask, cbase + (uint32_t)e, __float_as_uint(acc[r][e])));
             out_max[r] = __builtin_amdgcn_fmed3f(out_max[r], tl[r][KB - 1], sc);
 #pragma unroll
             for (int p = KB - 1; p > 0; --p)
               tl[r][p] = __builtin_amdgcn_fmed3f(tl[r][p - 1], tl[r][p], sc);
-            tl[r][0] = vmax(tl[r][0], sc);
+            tl[r][0] = max_not_nan(tl[r][0], sc);
           }
         }
       }
@@ -821,8 +840,8 @@ static void gate_dispatch_kb(const Plan& p, const T* q, const int32_t* cu, const
 }
 
 // Code bits of the screened pass's packed chain: 16 codes per chunk of 32 blocks.
-// Sequences of up to 512 blocks take 8 bits (one byte permute), longer ones 12
-// (up to 8,192 blocks) or 13 bits; any topk - 1 <= 16.
+// Sequences of up to 512 blocks take 8 bits, longer ones 12 (up to 8,192 blocks)
+// or 13 bits; any topk - 1 <= 16.
 static int gate_code_bits(const Plan& p) {
   if (p.max_nb <= 512) return 8;
   return p.max_nb <= 8192 ? 12 : 13;
