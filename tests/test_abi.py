@@ -289,6 +289,44 @@ def test_bench_work_counts_closed_forms():
     assert abs(w["route_bytes"] / 1e9 - 0.803) < 0.001
 
 
+def test_bench_merge_increment_bytes():
+    """The merge increment's algorithmic bytes are the selected parts alone (D fp16
+    values and one fp32 LSE per (row, selected slot)), closed form for one
+    sequence of nb full blocks: hq B (ks nb - ks(ks+1)/2) (2 D + 4); 17.4 GB at
+    1M. The own-block-only run is asked for at top-k 1 on the same inputs, and
+    the rate is those bytes over the time difference."""
+    import types
+    import bench
+    B, nb, ks, hq, hkv, d = 2048, 512, 2, 32, 8, 128
+    T = nb * B
+    w = bench.work_counts([T], hq, hkv, d, B, ks + 1, 2)
+    # q: the workload's element count, as an expanded view of one element
+    q = torch.zeros(1, dtype=torch.bfloat16).expand(T * hq * d)
+    inp = types.SimpleNamespace(q=q, k=None, v=None, cu_seqlens=None, block=B, seqlens=[T],
+                                topk=ks + 1)
+    seen = {}
+
+    def fake_time_forward(moba, torch_, own, cu_dev, steps, warmup, timing):
+        seen["topk"], seen["block"], seen["seqlens"] = own.topk, own.block, own.seqlens
+        return {"stages": {"attn_self": {"avg_ms": 18.0}}}
+
+    real = bench.time_forward
+    bench.time_forward = fake_time_forward
+    try:
+        m = bench.bench_merge(None, torch, inp, None, 2, 1, 20.0, w)
+    finally:
+        bench.time_forward = real
+    assert seen == {"topk": 1, "block": B, "seqlens": [T]}
+    parts = hq * B * (ks * nb - ks * (ks + 1) // 2) * (2 * d + 4)
+    assert m["parts_bytes"] == parts
+    assert abs(parts / 1e9 - 17.40) < 0.01
+    assert abs(m["incremental_ms"] - 2.0) < 1e-12
+    assert abs(m["achieved_gbs"] - parts / 2e-3 / 1e9) < 1e-6
+    # no increment to measure at top-k 1
+    inp.topk = 1
+    assert bench.bench_merge(None, torch, inp, None, 2, 1, 20.0, w) is None
+
+
 def test_bench_refuses_several_gpus():
     import subprocess
     import sys as _sys
