@@ -14,6 +14,10 @@
 
 namespace moba {
 
+// The selection when every row keeps all of its past blocks (pool_gate.hip).
+hipError_t launch_forced_sel(const Plan& p, const int32_t* cu_dev, const Work& w, int32_t* sel,
+                             hipStream_t s);
+
 static thread_local char g_err[512] = "";
 
 static moba_status_t fail(moba_status_t st, const char* fmt, ...) {
@@ -354,7 +358,31 @@ static moba_status_t forward_enqueue(const Plan& p, const void* q, const void* k
   (void)hipGetLastError();
   Work w = carve(p, workspace);
   int32_t* sel = sel_out ? sel_out : w.sel;
-  hipError_t e = launch_setup(p, cu_dev, w, s);
+  hipError_t e = hipSuccess;
+  if (p.max_nb <= p.topk && pad8(dense_tile_count(p)) * kAttnThreads <= kMaxGridItems) {
+    // No sequence has more than topk blocks, so no row has more than topk - 1 past
+    // blocks and every row keeps all of them: the attended set is the own block up
+    // to the row plus every earlier key, which is causal attention over the whole
+    // sequence. That runs as the dense causal kernel, and the selection is the
+    // forced one (MoBA README, FAQ of issue #27: moba_topk - 1 capped by the number
+    // of complete past blocks). Pool, gate and route have nothing to decide; the
+    // block table is built only to write the selection when it is asked for.
+    if (sel_out && p.ks > 0) {
+      e = launch_setup(p, cu_dev, w, s);
+      if (e != hipSuccess) return hip_status(e, "setup");
+      StageScope t(ST_GATE, s);
+      e = launch_forced_sel(p, cu_dev, w, sel_out, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "forced selection");
+    {
+      StageScope t(ST_DENSE, s);
+      e = launch_attn_dense(p, q, k, v, cu_dev, out, lse_out, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "causal attention");
+    g_err[0] = 0;
+    return MOBA_OK;
+  }
+  e = launch_setup(p, cu_dev, w, s);
   if (e != hipSuccess) return hip_status(e, "setup");
   {
     StageScope t(ST_POOL, s);

@@ -72,6 +72,34 @@ __global__ void __launch_bounds__(256) k_block_info(const int32_t* __restrict__ 
   blk_local[b] = (int32_t)(b - blk_base[n]);
 }
 
+// The selection when no block has more than topk - 1 past blocks: a row of block i
+// keeps every past block, so its list is 0 .. i - 1 (ascending) padded with -1.
+// One workgroup per global block; the block's rows are contiguous in sel.
+__global__ void __launch_bounds__(256) k_forced_sel(const int32_t* __restrict__ cu,
+                                                    const int32_t* __restrict__ blk_seq,
+                                                    const int32_t* __restrict__ blk_local,
+                                                    int block, int hq, int ks,
+                                                    int32_t* __restrict__ sel) {
+  const int64_t b = blockIdx.x;
+  const int n = blk_seq[b], i = blk_local[b];
+  const int64_t s0 = (int64_t)cu[n] + (int64_t)i * block;
+  const int64_t len = min((int64_t)block, (int64_t)cu[n + 1] - s0);
+  const int64_t total = len * hq * ks;               // below T * hq * ks < 2^31
+  int32_t* dst = sel + s0 * hq * ks;
+  for (int64_t e = threadIdx.x; e < total; e += 256) {
+    const int slot = (int)(e % ks);
+    dst[e] = (slot < i) ? slot : -1;
+  }
+}
+
+hipError_t launch_forced_sel(const Plan& p, const int32_t* cu_dev, const Work& w, int32_t* sel,
+                             hipStream_t s) {
+  if (p.ks == 0 || p.nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_forced_sel, dim3((unsigned)p.nb), dim3(256), 0, s, cu_dev, w.blk_seq,
+                     w.blk_local, p.block, p.hq, p.ks, sel);
+  return hipGetLastError();
+}
+
 hipError_t launch_setup(const Plan& p, const int32_t* cu_dev, const Work& w, hipStream_t s) {
   hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, s, cu_dev, p.nseq, p.block, p.hkv,
                      w.blk_base, w.tri_base);

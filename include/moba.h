@@ -122,6 +122,12 @@ size_t moba_workspace_bytes_min(const int32_t* cu_seqlens_host, int32_t num_seqs
  *            result is the same (bitwise); the copies cost extra HBM traffic of
  *            about twice q, k, v and out. The int32 limits below then apply to
  *            one group (T * G * (topk-1) < 2^31), so longer batches fit.
+ *   When no sequence of the batch has more than topk blocks, every row keeps all
+ *   of its past blocks, which makes the attended set the whole causal prefix:
+ *   the call then runs the dense causal kernel (moba_dense_causal_forward's) and
+ *   writes the forced selection (0 .. i-1 for a row of block i), with no pool,
+ *   gate or routing; results are within rounding of the MoBA kernels' (the same
+ *   attended keys, without fp16 partial outputs).
  */
 moba_status_t moba_forward(const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,

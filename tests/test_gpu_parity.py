@@ -58,7 +58,9 @@ SMALL = [
     ("gqa-d64-bf16", [1536, 700], 4, 1, 64, 128, 4, "bf16"),
     ("fine-blocks-bf16", [3000], 4, 2, 128, 64, 12, "bf16"),
     ("own-block-only-bf16", [1000, 333], 8, 8, 128, 128, 1, "bf16"),
-    ("topk-covers-all-bf16", [1100], 4, 4, 64, 128, 16, "bf16"),
+    # every past block kept in the first sequence and in the second's first 16
+    # blocks; the second's 18 blocks keep the batch on the MoBA kernels
+    ("topk-covers-all-bf16", [1100, 2200], 4, 4, 64, 128, 16, "bf16"),
     ("g8-heads-bf16", [900], 16, 2, 128, 192, 3, "bf16"),
     ("g3-heads-f32", [700, 450], 6, 2, 64, 64, 3, "f32"),
     ("gqa-fp32", [1200, 300], 4, 2, 128, 128, 5, "f32"),
@@ -359,6 +361,34 @@ def test_block_longer_than_sequence_equals_dense():
     dense = moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens)
     torch.cuda.synchronize()
     assert (out.float() - dense.float()).abs().max().item() <= 2e-2
+
+
+FORCED = [
+    # name, seqlens, hq, hkv, d, block, topk, dtype: no sequence longer than topk blocks
+    ("gqa-varlen-bf16", [1000, 0, 517, 64], 8, 2, 128, 256, 4, "bf16"),
+    ("one-block-each-f32", [200, 64, 131], 4, 2, 64, 256, 2, "f32"),
+    ("topk-equals-blocks-bf16", [2048, 1500], 4, 1, 128, 512, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FORCED, ids=[c[0] for c in FORCED])
+def test_forced_selection_runs_dense_kernel(case):
+    """When no sequence has more than topk blocks every row keeps all of its past
+    blocks, and the forward runs the dense causal kernel with the forced
+    selection: every row against the oracle, and the stage timers show the dense
+    launch and no pool, gate or selected-block launch."""
+    name, seqlens, hq, hkv, d, block, topk, dt = case
+    _say("forced selection %s seqlens=%s hq=%d hkv=%d d=%d block=%d topk=%d %s"
+         % (name, seqlens, hq, hkv, d, block, topk, dt))
+    inp = _to_gpu(make_inputs(seqlens, hq, hkv, d, block, topk, dtype=dt, seed=31))
+    moba.moba_timing_enable(True)
+    moba.moba_timing_read()
+    out, sel, lse = _run(inp)
+    st = moba.moba_timing_read()
+    moba.moba_timing_enable(False)
+    assert st["attn_dense"][1] == 1
+    assert st["pool"][1] == 0 and st["attn_selected"][1] == 0 and st["attn_self"][1] == 0
+    _check_all_rows(inp, out, sel, lse, TOL[inp.q.dtype])
 
 
 def test_hybrid_switch_runs_each_path():
