@@ -379,7 +379,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t tile = logical;
     const int32_t* toffs = a.tile_offsets;
     if (tile >= toffs[a.nlists]) return;
-    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int L = upper_index_wave(toffs, (int)a.nlists, tile, lane);
     const int64_t b = L / a.hkv;
     g = L % a.hkv;
     const int n = a.blk_seq[b], j = a.blk_local[b];
@@ -714,7 +714,7 @@ k_attn4(AttnArgs a) {
     const int64_t tile = logical;
     const int32_t* toffs = a.tile_offsets;
     if (tile >= toffs[a.nlists]) return;
-    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int L = upper_index_wave(toffs, (int)a.nlists, tile, lane);
     const int64_t b = L / a.hkv;
     g = L % a.hkv;
     const int n = a.blk_seq[b], j = a.blk_local[b];

@@ -173,7 +173,7 @@ k_bwd_dq(BwdArgs a) {
     const int64_t tile = logical;
     const int32_t* toffs = a.tile_offsets;
     if (tile >= toffs[a.nlists]) return;
-    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int L = upper_index_wave(toffs, (int)a.nlists, tile, lane);
     const int64_t b = L / a.hkv;
     g = L % a.hkv;
     const int n = a.blk_seq[b], j = a.blk_local[b];
@@ -767,7 +767,7 @@ k_bwd_dq_dma(BwdArgs a) {
     const int64_t tile = logical;
     const int32_t* toffs = a.tile_offsets;
     if (tile >= toffs[a.nlists]) return;
-    const int L = upper_index(toffs, (int)a.nlists, tile);
+    const int L = upper_index_wave(toffs, (int)a.nlists, tile, lane);
     const int64_t b = L / a.hkv;
     g = L % a.hkv;
     const int n = a.blk_seq[b], j = a.blk_local[b];

@@ -147,6 +147,26 @@ __device__ __forceinline__ int upper_index(const int32_t* offs, int n, int64_t x
   return lo;
 }
 
+// upper_index by the whole wave (x wave-uniform, every lane calls it): each round
+// reads 64 evenly spaced entries of the range that holds the answer in one vector
+// load, and the highest lane whose entry is <= x narrows the range to one stride,
+// so n <= 4096 takes two dependent loads where the binary search takes twelve.
+// Needs offs[0] <= x. Same result as upper_index.
+__device__ __forceinline__ int upper_index_wave(const int32_t* offs, int n, int64_t x,
+                                                int lane) {
+  int lo = 0, len = n;                       // the answer lies in [lo, lo + len)
+  while (len > 1) {
+    const int step = (len + 63) / 64;
+    const bool in = lane * step < len;
+    const bool ok = in && (int64_t)offs[min(lo + lane * step, n - 1)] <= x;
+    const uint64_t m = __ballot(ok);         // a prefix of the lanes; bit 0 is set
+    const int hl = 63 - __clzll((unsigned long long)m);
+    lo += hl * step;
+    len = min(step, len - hl * step);
+  }
+  return lo;
+}
+
 // Eight fp32 values as one MFMA operand fragment of the input type.
 template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
 template <> __device__ __forceinline__ bf16x8 pack8<bf16>(const float* x) {
