@@ -557,9 +557,11 @@ def bench_small_shapes(moba, torch, seed):
 
 
 def bench_second_workload(moba, torch, name, steps, warmup, seed, dense_steps):
-    """The metric's second point (S = 128K: the packed varlen batch of 134,144
-    tokens), timed like the headline workload in the same run: tokens/s, every
-    stage's rate and the dense causal comparison from the same library."""
+    """Another workload timed like the headline one in the same run: tokens/s and
+    every stage's rate, plus the dense causal comparison from the same library
+    when dense_steps > 0. Used for the metric's second point (S = 128K: the packed
+    varlen batch of 134,144 tokens) and for the 10M-token head share (no dense
+    run there: it would take minutes)."""
     from synth_inputs import make_config
     dev = torch.device("cuda:0")
     print("[bench] second workload %s" % name, file=sys.stderr, flush=True)
@@ -569,18 +571,20 @@ def bench_second_workload(moba, torch, name, steps, warmup, seed, dense_steps):
     ms, work = fwd["ms"], fwd["work"]
     T = inp.q.shape[0]
     out = torch.empty_like(inp.q)
-    moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, out=out,
-                                   cu_seqlens_dev=cu_dev)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(dense_steps):
+    dms = None
+    if dense_steps > 0:
         moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, out=out,
                                        cu_seqlens_dev=cu_dev)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dms = e0.elapsed_time(e1) / dense_steps
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(dense_steps):
+            moba.moba_dense_causal_forward(inp.q, inp.k, inp.v, inp.cu_seqlens, out=out,
+                                           cu_seqlens_dev=cu_dev)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / dense_steps
     attn_flop = work["attn_selected_flop"] + work["attn_self_flop"]
     sel = fwd["stages"].get("attn_selected", {})
     res = {"workload": CONFIG_NAMES[name], "seqlens": inp.seqlens, "tokens": T,
@@ -591,7 +595,7 @@ def bench_second_workload(moba, torch, name, steps, warmup, seed, dense_steps):
            # HBM bytes per launch of the selected-block kernel on this workload
            # (profiles/traffic_attn_selected_<config>.txt; null when stale)
            "attn_selected_traffic": load_traffic("attn_selected", name),
-           "dense_causal_ms": dms, "speedup_vs_dense": dms / ms,
+           "dense_causal_ms": dms, "speedup_vs_dense": (dms / ms) if dms else None,
            "stages": fwd["stages"]}
     del inp, out
     torch.cuda.empty_cache()
@@ -616,6 +620,8 @@ def main():
                     help="skip the merge increment (an own-block-only forward at top-k 1)")
     ap.add_argument("--no-second", action="store_true",
                     help="skip the metric's 128K point (varlen 131K) timed after the 1M one")
+    ap.add_argument("--no-10m", action="store_true",
+                    help="skip the 10M-token head share timed after the 1M one")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-timing", action="store_true", help="no per-stage HIP events")
     ap.add_argument("--no-achievable", action="store_true",
@@ -739,6 +745,11 @@ def main():
                                        warmup=max(args.warmup, 3), seed=args.seed,
                                        dense_steps=max(args.dense_steps, 3))
 
+    ten_m = None
+    if not args.no_10m and not args.no_second and args.config == "1m":
+        ten_m = bench_second_workload(moba, torch, "10m_shard", steps=3, warmup=1,
+                                      seed=args.seed, dense_steps=0)
+
     if achievable is not None:
         if decode is not None:
             decode["hbm_frac_of_achievable"] = decode["achieved_gbs"] / achievable["hbm_gbs"]
@@ -773,6 +784,7 @@ def main():
         "stages": stage_rep,
         "merge": merge,
         "workload_128k": second,
+        "workload_10m_head_share": ten_m,
         "small_shapes": small,
     }
     print(json.dumps(line), flush=True)
