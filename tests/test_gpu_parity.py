@@ -486,6 +486,9 @@ def test_large_values_within_the_fp16_part_range():
     ("bf16-gqa2-varlen-k6", [1000, 64, 0, 2300, 129], 8, 4, 128, 128, 6, "bf16"),
     ("f32-gqa2-d64-k5", [700, 450], 4, 2, 64, 64, 5, "f32"),
     ("bf16-gqa3-k6", [1500, 97], 6, 2, 128, 128, 6, "bf16"),
+    # no sequence longer than topk blocks: each group takes the dense kernel and
+    # the forced selection
+    ("bf16-gqa2-forced-k6", [640, 64, 0, 300], 8, 4, 128, 128, 6, "bf16"),
 ], ids=lambda c: c[0])
 def test_kv_group_mode_equals_one_pass(case):
     """A workspace below moba_workspace_bytes runs the kv groups one after another
