@@ -39,6 +39,8 @@ CASES = [
     # runs on scratch that still holds the first call's lists and parts
     ("bf16-gqa-varlen", [4096, 3000, 129], 8, 2, 128, 256, 4, "bf16"),
     ("fp32-small", [700, 0, 333], 4, 2, 64, 128, 3, "f32"),
+    # no sequence longer than topk blocks: the dense kernel and the forced selection
+    ("bf16-forced", [600, 900], 4, 2, 128, 256, 4, "bf16"),
 ]
 
 
